@@ -1,0 +1,289 @@
+"""Python binding of libssd_replay.so over torch tensors.
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+size (the C ABI cannot see extents), then their data pointers and the
+current HIP stream are handed to the library. Every step of the scan runs in
+the library's kernels; torch only owns memory and streams. Outputs that the
+caller does not pass are allocated with torch.empty.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+_CODE = {"bf16": _lib.SSD_BF16, "f32": _lib.SSD_F32}
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Problem shape: heads H, B/C groups G, head dim P, state size N, chunk
+    size Q; storage dtypes of x/B/C/y (io) and of raw dt."""
+    H: int
+    G: int
+    P: int
+    N: int
+    chunk_size: int
+    io_dtype: str = "bf16"
+    dt_dtype: str = "bf16"
+    dt_softplus: bool = True
+    state_dtype: str = "f32"
+
+    def c(self) -> _lib.ssd_shape:
+        return _lib.ssd_shape(self.H, self.G, self.P, self.N, self.chunk_size,
+                              _CODE[self.io_dtype], _CODE[self.dt_dtype],
+                              _CODE.get(self.state_dtype, 99), int(bool(self.dt_softplus)))
+
+    @property
+    def io(self) -> torch.dtype:
+        return _DT[self.io_dtype]
+
+    @property
+    def dtt(self) -> torch.dtype:
+        return _DT[self.dt_dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtype, device):
+    return None if t is None else _need(t, name, shape, dtype, device)
+
+
+def _cu_pair(cu_seqlens, cu_seqlens_host, device):
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens
+    host = np.ascontiguousarray(
+        cu_seqlens_host.cpu().numpy() if isinstance(cu_seqlens_host, torch.Tensor)
+        else np.asarray(cu_seqlens_host), dtype=np.int32)
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device == device:
+        dev = _need(cu_seqlens, "cu_seqlens", (host.size,), torch.int32, device)
+    else:
+        dev = torch.from_numpy(host).to(device)
+    return host, dev
+
+
+class ReplayCache:
+    """Exact-replay cache for num_slots sequences: fp32 boundary state plus
+    the partial-chunk token buffers (all zeros = every slot fresh)."""
+
+    def __init__(self, shape: Shape, num_slots: int, device="cuda", with_C: bool = False,
+                 state_dtype: torch.dtype = torch.float32, _empty: bool = False):
+        H, G, P, N, Q = shape.H, shape.G, shape.P, shape.N, shape.chunk_size
+        self.shape = shape
+        self.num_slots = num_slots
+        self.device = torch.device(device)
+        mk = torch.empty if _empty else torch.zeros
+        self.state = mk((num_slots, H, P, N), dtype=state_dtype, device=self.device)
+        self.buf_x = mk((num_slots, Q, H, P), dtype=shape.io, device=self.device)
+        self.buf_dt = mk((num_slots, Q, H), dtype=shape.dtt, device=self.device)
+        self.buf_B = mk((num_slots, Q, G, N), dtype=shape.io, device=self.device)
+        self.buf_C = (mk((num_slots, Q, G, N), dtype=shape.io, device=self.device)
+                      if with_C else None)
+        self.buf_len = mk((num_slots,), dtype=torch.int32, device=self.device)
+        self.boundary_pos = mk((num_slots,), dtype=torch.int64, device=self.device)
+
+    def struct(self) -> _lib.ssd_replay_cache:
+        sd = _lib.SSD_F32 if self.state.dtype == torch.float32 else _lib.SSD_BF16
+        return _lib.ssd_replay_cache(
+            self.state.data_ptr(), self.buf_x.data_ptr(), self.buf_dt.data_ptr(),
+            self.buf_B.data_ptr(), None if self.buf_C is None else self.buf_C.data_ptr(),
+            self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.num_slots,
+            self.shape.chunk_size, sd)
+
+    def tensors(self):
+        return [t for t in (self.state, self.buf_x, self.buf_dt, self.buf_B, self.buf_C,
+                            self.buf_len, self.boundary_pos) if t is not None]
+
+    def clone(self) -> "ReplayCache":
+        c = ReplayCache(self.shape, self.num_slots, self.device, self.buf_C is not None,
+                        self.state.dtype, _empty=True)
+        for dst, src in zip(c.tensors(), self.tensors()):
+            dst.copy_(src)
+        return c
+
+    def copy_from(self, other: "ReplayCache") -> None:
+        for dst, src in zip(self.tensors(), other.tensors()):
+            dst.copy_(src)
+
+
+def ssd_replay_cache_bytes(shape: Shape, num_slots: int, with_C: bool = True) -> int:
+    c = shape.c()
+    return int(_lib.load().ssd_replay_cache_bytes(ctypes.byref(c), num_slots, int(with_C)))
+
+
+def _slots(slot_idx, n, device):
+    if slot_idx is None:
+        return None
+    return _need(slot_idx, "slot_idx", (n,), torch.int32, device)
+
+
+def ssd_prefill_varlen(shape: Shape, cu_seqlens, x, dt, A, B, C, D=None, dt_bias=None,
+                       init_state=None, y=None, final_state=None, boundary_state=None,
+                       cu_seqlens_host=None, want_final=True, want_boundary=True, stream=None):
+    """Chunked scan of a varlen pack from init_state (None = zeros).
+    Returns (y, final_state, boundary_state)."""
+    dev = x.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _opt(init_state, "init_state", (S, H, P, N), torch.float32, dev)
+    y = torch.empty((T, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (T, H, P), shape.io, dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    if boundary_state is None and want_boundary:
+        boundary_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    _opt(final_state, "final_state", (S, H, P, N), torch.float32, dev)
+    _opt(boundary_state, "boundary_state", (S, H, P, N), torch.float32, dev)
+    sh = shape.c()
+    rc = _lib.load().ssd_prefill_varlen(
+        ctypes.byref(sh), S, T, host.ctypes.data_as(ctypes.c_void_p), _ptr(cu), _ptr(x),
+        _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(init_state), _ptr(y),
+        _ptr(final_state), _ptr(boundary_state), None, 0, _stream(stream))
+    _lib.check(rc, "ssd_prefill_varlen")
+    return y, final_state, boundary_state
+
+
+def ssd_commit_boundary(shape: Shape, cache: ReplayCache, cu_seqlens, x, dt, B, C,
+                        boundary_state, slot_idx=None, cu_seqlens_host=None, stream=None):
+    """Store a fresh prefill's boundary state and trailing partial chunk in
+    the cache slots."""
+    dev = cache.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(boundary_state, "boundary_state", (S, H, P, N), torch.float32, dev)
+    sl = _slots(slot_idx, S, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_commit_boundary(
+        ctypes.byref(sh), S, T, host.ctypes.data_as(ctypes.c_void_p), _ptr(cu), _ptr(sl),
+        _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(boundary_state), ctypes.byref(cs),
+        _stream(stream))
+    _lib.check(rc, "ssd_commit_boundary")
+
+
+def ssd_replay_prefill(shape: Shape, cache: ReplayCache, cu_seqlens, x, dt, B, C, A, D=None,
+                       dt_bias=None, slot_idx=None, y=None, cu_seqlens_host=None, stream=None):
+    """Exact-replay (chunked) prefill: resume every sequence at its slot's
+    boundary. Returns y for the new tokens."""
+    dev = cache.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, S, dev)
+    y = torch.empty((T, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (T, H, P), shape.io, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_replay_prefill(
+        ctypes.byref(sh), ctypes.byref(cs), S, T, host.ctypes.data_as(ctypes.c_void_p),
+        _ptr(cu), _ptr(sl), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+        _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssd_replay_prefill")
+    return y
+
+
+def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, dt_bias=None,
+                      slot_idx=None, y=None, stream=None):
+    """One exact-replay decode step for x.shape[0] sequences."""
+    dev = cache.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    nb = int(x.shape[0])
+    _need(x, "x", (nb, H, P), shape.io, dev)
+    _need(dt, "dt", (nb, H), shape.dtt, dev)
+    _need(B, "B", (nb, G, N), shape.io, dev)
+    _need(C, "C", (nb, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, nb, dev)
+    y = torch.empty((nb, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (nb, H, P), shape.io, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_replay_decode(
+        ctypes.byref(sh), ctypes.byref(cs), nb, _ptr(sl), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+        _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssd_replay_decode")
+    return y
+
+
+def ssm_state_update(shape: Shape, state, x, dt, B, C, A, D=None, dt_bias=None, slot_idx=None,
+                     y=None, stream=None):
+    """One recurrent selective-state update for x.shape[0] sequences; state
+    [num_slots,H,P,N] fp32 is updated in place."""
+    dev = state.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    nb = int(x.shape[0])
+    ns = int(state.shape[0])
+    _need(state, "state", (ns, H, P, N), torch.float32, dev)
+    _need(x, "x", (nb, H, P), shape.io, dev)
+    _need(dt, "dt", (nb, H), shape.dtt, dev)
+    _need(B, "B", (nb, G, N), shape.io, dev)
+    _need(C, "C", (nb, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, nb, dev)
+    y = torch.empty((nb, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (nb, H, P), shape.io, dev)
+    sh = shape.c()
+    rc = _lib.load().ssm_state_update(
+        ctypes.byref(sh), nb, ns, _ptr(sl), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+        _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssm_state_update")
+    return y
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Storage array from synth (uint16 bf16 bits or float32) -> torch tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a bf16 / fp32 tensor."""
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,301 @@
+// ssd_api.cpp -- the extern "C" entry points declared in include/ssd_replay.h:
+// host-side argument checks (all of them before any HIP call, so a rejected
+// call launches nothing) and the translation into kernel argument blocks.
+#include "ssd_replay.h"
+
+#include <limits>
+
+#include "ssd_internal.hpp"
+
+namespace {
+
+using ssd::Dims;
+
+bool pow2_in(int v, int lo, int hi) {
+    if (v < lo || v > hi)
+        return false;
+    return (v & (v - 1)) == 0;
+}
+
+int check_shape(const ssd_shape *sh, Dims *d) {
+    if (!sh)
+        return SSD_ERR_NULL;
+    if (sh->state_dtype != SSD_F32)
+        return SSD_ERR_STATE_NOT_FP32;
+    if ((sh->io_dtype != SSD_F32 && sh->io_dtype != SSD_BF16) ||
+        (sh->dt_dtype != SSD_F32 && sh->dt_dtype != SSD_BF16))
+        return SSD_ERR_DTYPE;
+    if (sh->H <= 0 || sh->G <= 0 || sh->H % sh->G != 0)
+        return SSD_ERR_SHAPE;
+    if (!pow2_in(sh->chunk_size, 16, 256) || !pow2_in(sh->P, 16, 128) ||
+        !pow2_in(sh->N, 16, 128) || sh->H > 65535)
+        return SSD_ERR_UNSUPPORTED;
+    d->H = sh->H;
+    d->G = sh->G;
+    d->P = sh->P;
+    d->N = sh->N;
+    d->Q = sh->chunk_size;
+    d->io_bf16 = sh->io_dtype == SSD_BF16;
+    d->dt_bf16 = sh->dt_dtype == SSD_BF16;
+    d->softplus = sh->dt_softplus != 0;
+    return SSD_OK;
+}
+
+// cu_seqlens_host: cu[0] == 0, non-decreasing, cu[S] == T, and the grid
+// (S * H workgroups) fits a 1D launch.
+int check_seqs(const Dims &d, int32_t S, int64_t T, const int32_t *cu_host, const int32_t *cu) {
+    if (S < 0 || T < 0 || T > std::numeric_limits<int32_t>::max())
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return T == 0 ? SSD_OK : SSD_ERR_SHAPE;
+    if (!cu_host || !cu)
+        return SSD_ERR_NULL;
+    if (cu_host[0] != 0 || cu_host[S] != T)
+        return SSD_ERR_SHAPE;
+    for (int32_t s = 0; s < S; ++s)
+        if (cu_host[s + 1] < cu_host[s])
+            return SSD_ERR_SHAPE;
+    if ((int64_t)S * d.H > std::numeric_limits<int32_t>::max())
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
+    if (!c)
+        return SSD_ERR_NULL;
+    if (c->state_dtype != SSD_F32)
+        return SSD_ERR_STATE_NOT_FP32;
+    if (c->chunk_size != sh->chunk_size)
+        return SSD_ERR_CHUNK_MISMATCH;
+    if (!c->state || !c->buf_x || !c->buf_dt || !c->buf_B || !c->buf_len || !c->boundary_pos)
+        return SSD_ERR_NULL;
+    if (c->num_slots <= 0)
+        return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+size_t dtype_bytes(int dt) { return dt == SSD_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(int status) {
+    switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: inconsistent sizes";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype";
+    case SSD_ERR_STATE_NOT_FP32: return "SSD_ERR_STATE_NOT_FP32: the SSM state must be fp32";
+    case SSD_ERR_CHUNK_MISMATCH: return "SSD_ERR_CHUNK_MISMATCH: cache and call chunk sizes differ";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape outside the built set";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown ssd_status";
+    }
+}
+
+size_t ssd_replay_cache_bytes(const ssd_shape *sh, int32_t num_slots, int32_t with_C) {
+    Dims d;
+    if (check_shape(sh, &d) != SSD_OK || num_slots < 0)
+        return 0;
+    const size_t io = dtype_bytes(sh->io_dtype), dtb = dtype_bytes(sh->dt_dtype);
+    const size_t state = (size_t)d.H * d.P * d.N * sizeof(float);
+    const size_t per_tok = (size_t)d.H * d.P * io + (size_t)d.H * dtb +
+                           (with_C ? 2 : 1) * (size_t)d.G * d.N * io;
+    const size_t per_slot = state + (size_t)d.Q * per_tok + sizeof(int32_t) + sizeof(int64_t);
+    return per_slot * (size_t)num_slots;
+}
+
+size_t ssd_prefill_workspace_bytes(const ssd_shape *sh, int32_t num_seqs, int64_t total_tokens) {
+    (void)sh;
+    (void)num_seqs;
+    (void)total_tokens;
+    return 0;
+}
+
+int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t *cu_host,
+                       const int32_t *cu, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *dt_bias,
+                       const float *init_state, void *y, float *final_state,
+                       float *boundary_state, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (workspace_bytes < ssd_prefill_workspace_bytes(sh, S, T) ||
+        (ssd_prefill_workspace_bytes(sh, S, T) > 0 && !workspace))
+        return SSD_ERR_WORKSPACE;
+    if (S == 0)
+        return SSD_OK;
+    if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
+        return SSD_ERR_NULL;
+    ssd::ScanArgs a = {};
+    a.d = d;
+    a.S = S;
+    a.cu = cu;
+    a.slot_idx = nullptr;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = y;
+    a.init_state = init_state;
+    a.final_state = final_state;
+    a.boundary_state = boundary_state;
+    a.replay = 0;
+    return hip_status(ssd::launch_scan(a, (hipStream_t)stream));
+}
+
+int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t *cu_host,
+                        const int32_t *cu, const int32_t *slot_idx, const void *x,
+                        const void *dt, const void *B, const void *C,
+                        const float *boundary_state, const ssd_replay_cache *cache,
+                        hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_cache(sh, cache)) != SSD_OK)
+        return st;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (!slot_idx && S > cache->num_slots)
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return SSD_OK;
+    if (!boundary_state || (T > 0 && (!x || !dt || !B || (cache->buf_C && !C))))
+        return SSD_ERR_NULL;
+    ssd::CommitArgs a = {};
+    a.d = d;
+    a.S = S;
+    a.cu = cu;
+    a.slot_idx = slot_idx;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.fresh = 1;
+    a.num_slots = cache->num_slots;
+    a.state_src = boundary_state;
+    a.cache_state = cache->state;
+    a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt;
+    a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
+    a.buf_len = cache->buf_len;
+    a.boundary_pos = cache->boundary_pos;
+    return hip_status(ssd::launch_commit(a, (hipStream_t)stream));
+}
+
+int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, int64_t T,
+                       const int32_t *cu_host, const int32_t *cu, const int32_t *slot_idx,
+                       const void *x, const void *dt, const void *B, const void *C,
+                       const float *A, const float *D, const float *dt_bias, void *y,
+                       hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_cache(sh, cache)) != SSD_OK)
+        return st;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (!slot_idx && S > cache->num_slots)
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return SSD_OK;
+    if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
+        return SSD_ERR_NULL;
+    ssd::ScanArgs a = {};
+    a.d = d;
+    a.S = S;
+    a.cu = cu;
+    a.slot_idx = slot_idx;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = y;
+    a.replay = 1;
+    a.num_slots = cache->num_slots;
+    a.cache_state = cache->state;
+    a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
+    a.buf_len = cache->buf_len;
+    hipError_t e = ssd::launch_scan(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return SSD_ERR_HIP;
+    ssd::CommitArgs c = {};
+    c.d = d;
+    c.S = S;
+    c.cu = cu;
+    c.slot_idx = slot_idx;
+    c.x = x; c.dt = dt; c.B = B; c.C = C;
+    c.fresh = 0;
+    c.num_slots = cache->num_slots;
+    c.state_src = nullptr;
+    c.cache_state = cache->state;
+    c.buf_x = cache->buf_x; c.buf_dt = cache->buf_dt;
+    c.buf_B = cache->buf_B; c.buf_C = cache->buf_C;
+    c.buf_len = cache->buf_len;
+    c.boundary_pos = cache->boundary_pos;
+    return hip_status(ssd::launch_commit(c, (hipStream_t)stream));
+}
+
+int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
+                      const int32_t *slot_idx, const void *x, const void *dt, const void *B,
+                      const void *C, const float *A, const float *D, const float *dt_bias,
+                      void *y, hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_cache(sh, cache)) != SSD_OK)
+        return st;
+    if (batch < 0 || (!slot_idx && batch > cache->num_slots) ||
+        (int64_t)batch * d.H > std::numeric_limits<int32_t>::max())
+        return SSD_ERR_SHAPE;
+    if (batch == 0)
+        return SSD_OK;
+    if (!x || !dt || !B || !C || !A || !y)
+        return SSD_ERR_NULL;
+    ssd::DecodeArgs a = {};
+    a.d = d;
+    a.batch = batch;
+    a.slot_idx = slot_idx;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = y;
+    a.num_slots = cache->num_slots;
+    a.cache_state = cache->state;
+    a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt;
+    a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
+    a.buf_len = cache->buf_len;
+    a.boundary_pos = cache->boundary_pos;
+    return hip_status(ssd::launch_decode(a, (hipStream_t)stream));
+}
+
+int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,
+                     const int32_t *slot_idx, float *state, const void *x, const void *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *dt_bias, void *y, hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if (batch < 0 || num_slots < 0 || (!slot_idx && batch > num_slots) ||
+        (int64_t)batch * d.H > std::numeric_limits<int32_t>::max())
+        return SSD_ERR_SHAPE;
+    if (batch == 0)
+        return SSD_OK;
+    if (!state || !x || !dt || !A || !B || !C || !y)
+        return SSD_ERR_NULL;
+    ssd::SsuArgs a = {};
+    a.d = d;
+    a.batch = batch;
+    a.slot_idx = slot_idx;
+    a.num_slots = num_slots;
+    a.state = state;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = y;
+    return hip_status(ssd::launch_ssu(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

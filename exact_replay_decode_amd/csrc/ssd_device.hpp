@@ -1,0 +1,98 @@
+// ssd_device.hpp -- device helpers shared by every scan kernel.
+//
+// Everything that decides a rounding lives here, so the prefill kernel and
+// the replay-decode kernel round identically: softplus, the decay exponent,
+// the dtype conversions, and the prefix-consistent in-chunk scan.
+// The library is built with -ffp-contract=off; every fused multiply-add is
+// written as fmaf on purpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kBlock = 256;       // threads per workgroup of the scan kernels
+constexpr int kMaxQ = 256;        // largest chunk size
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- storage types --------------------------------------------------------
+
+struct IoF32 {
+    using T = float;
+    __device__ static __forceinline__ float ld(const T *p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ T cvt(float v) { return v; }
+};
+
+struct IoBF16 {
+    using T = uint16_t;
+    __device__ static __forceinline__ float ld(const T *p, int64_t i) {
+        return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+    }
+    // round to nearest even; NaN stays NaN
+    __device__ static __forceinline__ T cvt(float v) {
+        uint32_t u = __float_as_uint(v);
+        if ((u & 0x7fffffffu) > 0x7f800000u)
+            return static_cast<T>((u >> 16) | 0x40u);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return static_cast<T>(u >> 16);
+    }
+};
+
+// ---- scalar functions that fix the rounding ------------------------------
+
+// delta = softplus(dt + bias) computed as log1p(exp(u)) for u <= 0 and
+// u + log1p(exp(-u)) otherwise; or dt + bias when softplus is off.
+__device__ __forceinline__ float delta_of(float dt_raw, float bias, int softplus) {
+    const float u = dt_raw + bias;
+    if (!softplus)
+        return u;
+    return u <= 0.0f ? log1pf(expf(u)) : u + log1pf(expf(-u));
+}
+
+// exp(v) for the decay factors, v <= 0 up to rounding: one v_exp_f32 (2^x)
+// of v * log2(e).
+__device__ __forceinline__ float decay_exp(float v) {
+    return __builtin_amdgcn_exp2f(v * kLog2e);
+}
+
+// weight of token j in row i of the intra-chunk product:
+// (C_i . B_j) * exp(lam_i - lam_j) * delta_j
+__device__ __forceinline__ float intra_weight(float cb, float lam_i, float lam_j, float dlt_j) {
+    return (cb * decay_exp(lam_i - lam_j)) * dlt_j;
+}
+
+// weight of token j in the chunk-end state: exp(lam_last - lam_j) * delta_j
+__device__ __forceinline__ float state_weight(float lam_last, float lam_j, float dlt_j) {
+    return decay_exp(lam_last - lam_j) * dlt_j;
+}
+
+// ---- prefix-consistent inclusive scan over one 256-thread workgroup -------
+// Lane t's result depends only on the values of lanes 0..t and on a fixed
+// combination tree: a Hillis-Steele scan inside each 64-lane wave, then the
+// totals of the earlier waves added in ascending order. `tot` is 4 floats of
+// LDS. Every thread of the block must call it.
+__device__ __forceinline__ float block_scan_inclusive(float v, float *tot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(v, off, 64);
+        if (lane >= off)
+            v = v + o;
+    }
+    if (lane == 63)
+        tot[wave] = v;
+    __syncthreads();
+    float r = v;
+    if (wave > 0) {
+        float pre = tot[0];
+        for (int w = 1; w < wave; ++w)
+            pre = pre + tot[w];
+        r = pre + v;
+    }
+    __syncthreads();
+    return r;
+}
+
+}  // namespace ssd

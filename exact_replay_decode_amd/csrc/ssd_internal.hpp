@@ -1,0 +1,86 @@
+// ssd_internal.hpp -- argument blocks passed from the C ABI layer to the
+// kernel launchers. Host-side only types; every pointer is a device pointer.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ssd {
+
+struct Dims {
+    int32_t H, G, P, N, Q;
+    int32_t io_bf16;   // 1: x/B/C/y are bf16, 0: fp32
+    int32_t dt_bf16;   // 1: dt is bf16, 0: fp32
+    int32_t softplus;
+};
+
+// One chunked-scan launch over S sequences, plain or replay.
+struct ScanArgs {
+    Dims d;
+    int32_t S;
+    const int32_t *cu;        // [S+1]
+    const int32_t *slot_idx;  // [S] or null (replay mode)
+    const void *x, *dt, *B, *C;
+    const float *A, *D, *dt_bias;
+    void *y;
+    // plain mode
+    const float *init_state;  // [S,H,P,N] or null
+    float *final_state;       // [S,H,P,N] or null
+    float *boundary_state;    // [S,H,P,N] or null
+    // replay mode (replay != 0): resume from the slot's boundary + buffer
+    int32_t replay;
+    int32_t num_slots;
+    float *cache_state;       // [slots,H,P,N]
+    const void *buf_x, *buf_dt, *buf_B;
+    const int32_t *buf_len;   // [slots]
+};
+
+// Write the trailing partial chunk of each sequence into the slot buffers
+// and advance buf_len / boundary_pos; optionally copy a boundary state in.
+struct CommitArgs {
+    Dims d;
+    int32_t S;
+    const int32_t *cu;
+    const int32_t *slot_idx;  // or null
+    const void *x, *dt, *B, *C;
+    int32_t fresh;            // 1: slot starts empty (after a plain prefill)
+    int32_t num_slots;
+    const float *state_src;   // [S,H,P,N] copied to the slot state, or null
+    float *cache_state;
+    void *buf_x, *buf_dt, *buf_B, *buf_C;  // buf_C may be null
+    int32_t *buf_len;
+    int64_t *boundary_pos;
+};
+
+struct DecodeArgs {
+    Dims d;
+    int32_t batch;
+    const int32_t *slot_idx;  // or null
+    const void *x, *dt, *B, *C;  // new token [batch,...]
+    const float *A, *D, *dt_bias;
+    void *y;
+    int32_t num_slots;
+    float *cache_state;
+    void *buf_x, *buf_dt, *buf_B, *buf_C;
+    int32_t *buf_len;
+    int64_t *boundary_pos;
+};
+
+struct SsuArgs {
+    Dims d;
+    int32_t batch;
+    const int32_t *slot_idx;
+    int32_t num_slots;
+    float *state;
+    const void *x, *dt, *B, *C;
+    const float *A, *D, *dt_bias;
+    void *y;
+};
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,584 @@
+// ssd_scalar.hip -- chunked scan, exact-replay decode, boundary commit and
+// the recurrent state update, computed with fp32 FMAs in fixed orders.
+//
+// The chunk arithmetic is the per-chunk closed form of the ReplaySSM
+// reproduction page ("Core equations"), per head h and chunk of Q tokens
+// starting from state S0 (lam = in-chunk inclusive cumulative sum of
+// delta*A):
+//   y_i   = exp(lam_i) (C_i . S0) + sum_{j<=i} (C_i . B_j) exp(lam_i - lam_j)
+//           delta_j x_j + D x_i
+//   S_end = exp(lam_last) S0 + sum_j exp(lam_last - lam_j) delta_j x_j B_j^T
+// The vLLM RFC "Mamba2: exact-replay decode ..." (section 3) replays a
+// partial chunk from the fp32 boundary state through this same arithmetic
+// to decode. Bit identity between the two follows from three facts that the
+// code below keeps:
+//  * every output entry (row i, column p) and every state entry (p, n) is a
+//    sequential fmaf chain over a fixed index order (n ascending, j
+//    ascending) that reads only tokens 0..i of the chunk;
+//  * the in-chunk scan is prefix-consistent (ssd_device.hpp);
+//  * the decode kernel calls the very same device functions (emit_rows,
+//    chunk_state_update) with a chunk view whose first k positions read the
+//    slot buffer.
+#include "ssd_device.hpp"
+#include "ssd_internal.hpp"
+
+namespace ssd {
+namespace {
+
+constexpr int kRows = 16;  // output rows per tile
+constexpr int kJB = 32;    // tokens per staged block
+constexpr int kMaxE = kRows * 128 / kBlock;  // output entries per thread
+constexpr int kMaxS = 128 * 128 / kBlock;    // state entries per thread
+
+// Offsets (in floats) of the scan kernels' LDS regions.
+struct LdsLayout {
+    int S, Ct, Bb, xb, Mb, lam, dlt, wb, tot, total;
+    __host__ __device__ LdsLayout(int P, int N) {
+        int o = 0;
+        S = o;   o += P * (N + 1);
+        Ct = o;  o += kRows * (N + 1);
+        Bb = o;  o += kJB * (N + 1);
+        xb = o;  o += kJB * P;
+        Mb = o;  o += kRows * kJB;
+        lam = o; o += kMaxQ;
+        dlt = o; o += kMaxQ;
+        wb = o;  o += kJB;
+        tot = o; o += 8;
+        total = o;
+    }
+};
+
+// Where chunk position j of the current chunk lives: positions [0, nb) in
+// the slot buffer, positions [nb, n_valid) in the packed input starting at
+// token tok_base. Positions >= n_valid do not exist.
+template <class IO, class DT>
+struct ChunkView {
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const T *x, *B, *C;
+    const TD *dt;
+    const T *bx, *bB;
+    const TD *bdt;
+    int64_t tok_base;
+    int nb, n_valid;
+    int h, g, H, G, P, N;
+
+    __device__ const T *xrow(int j) const {
+        return j < nb ? bx + ((int64_t)j * H + h) * P
+                      : x + ((tok_base + (j - nb)) * H + h) * P;
+    }
+    __device__ float dtv(int j) const {
+        return j < nb ? DT::ld(bdt, (int64_t)j * H + h)
+                      : DT::ld(dt, (tok_base + (j - nb)) * H + h);
+    }
+    __device__ const T *brow(int j) const {
+        return j < nb ? bB + ((int64_t)j * G + g) * N
+                      : B + ((tok_base + (j - nb)) * G + g) * N;
+    }
+    // C is only read for rows whose output is produced (never buffered rows)
+    __device__ const T *crow(int j) const { return C + ((tok_base + (j - nb)) * G + g) * N; }
+    __device__ int64_t token(int j) const { return tok_base + (j - nb); }
+};
+
+// delta and lam for the chunk; lanes past n_valid contribute zero.
+template <class IO, class DT>
+__device__ void prepare_chunk(const ChunkView<IO, DT> &v, float A_h, float bias,
+                              int softplus, float *lds, const LdsLayout &L) {
+    const int j = threadIdx.x;
+    float d = 0.0f, a = 0.0f;
+    if (j < v.n_valid) {
+        d = delta_of(v.dtv(j), bias, softplus);
+        a = d * A_h;
+    }
+    const float l = block_scan_inclusive(a, lds + L.tot);
+    lds[L.lam + j] = l;
+    lds[L.dlt + j] = d;
+    __syncthreads();
+}
+
+// Outputs of chunk rows [r0, r1) (r1 - r0 <= kRows) from the state S held in
+// LDS. y row i goes to packed token v.token(i).
+template <class IO, class DT>
+__device__ void emit_rows(const ChunkView<IO, DT> &v, int r0, int r1, float D_h,
+                          typename IO::T *y, float *lds, const LdsLayout &L) {
+    const int tid = threadIdx.x;
+    const int P = v.P, N = v.N, N1 = N + 1;
+    const int nr = r1 - r0;
+    float *S = lds + L.S, *Ct = lds + L.Ct, *Bb = lds + L.Bb, *xb = lds + L.xb;
+    float *Mb = lds + L.Mb;
+    const float *lam = lds + L.lam, *dlt = lds + L.dlt;
+
+    for (int e = tid; e < nr * N; e += kBlock) {
+        const int r = e / N, n = e % N;
+        Ct[r * N1 + n] = IO::ld(v.crow(r0 + r), n);
+    }
+    float acc_in[kMaxE];
+#pragma unroll
+    for (int k = 0; k < kMaxE; ++k)
+        acc_in[k] = 0.0f;
+    __syncthreads();
+
+    for (int jb = 0; jb < r1; jb += kJB) {
+        const int nj = min(kJB, r1 - jb);
+        for (int e = tid; e < nj * N; e += kBlock) {
+            const int jj = e / N, n = e % N;
+            Bb[jj * N1 + n] = IO::ld(v.brow(jb + jj), n);
+        }
+        for (int e = tid; e < nj * P; e += kBlock) {
+            const int jj = e / P, p = e % P;
+            xb[jj * P + p] = IO::ld(v.xrow(jb + jj), p);
+        }
+        __syncthreads();
+        for (int e = tid; e < nr * kJB; e += kBlock) {
+            const int r = e / kJB, jj = e % kJB;
+            const int i = r0 + r, j = jb + jj;
+            float m = 0.0f;
+            if (jj < nj && j <= i) {
+                float cb = 0.0f;
+                for (int n = 0; n < N; ++n)
+                    cb = fmaf(Ct[r * N1 + n], Bb[jj * N1 + n], cb);
+                m = intra_weight(cb, lam[i], lam[j], dlt[j]);
+            }
+            Mb[r * kJB + jj] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMaxE; ++k) {
+            const int e = tid + kBlock * k;
+            if (e < nr * P) {
+                const int r = e / P, p = e % P;
+                const int jmax = min(nj, r0 + r - jb + 1);
+                float acc = acc_in[k];
+                for (int jj = 0; jj < jmax; ++jj)
+                    acc = fmaf(Mb[r * kJB + jj], xb[jj * P + p], acc);
+                acc_in[k] = acc;
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int k = 0; k < kMaxE; ++k) {
+        const int e = tid + kBlock * k;
+        if (e < nr * P) {
+            const int r = e / P, p = e % P, i = r0 + r;
+            float acc_off = 0.0f;
+            for (int n = 0; n < N; ++n)
+                acc_off = fmaf(Ct[r * N1 + n], S[p * N1 + n], acc_off);
+            const float xv = IO::ld(v.xrow(i), p);
+            float yv = fmaf(decay_exp(lam[i]), acc_off, acc_in[k]);
+            yv = fmaf(D_h, xv, yv);
+            yv = yv + 0.0f;  // -0 -> +0
+            y[(v.token(i) * v.H + v.h) * P + p] = IO::cvt(yv);
+        }
+    }
+    __syncthreads();
+}
+
+// S <- exp(lam_last) S + sum_{j < n_valid} exp(lam_last - lam_j) delta_j x_j B_j^T
+// with lam_last = lam[n_valid - 1]; S in LDS.
+template <class IO, class DT>
+__device__ void chunk_state_update(const ChunkView<IO, DT> &v, float *lds, const LdsLayout &L) {
+    const int tid = threadIdx.x;
+    const int P = v.P, N = v.N, N1 = N + 1;
+    const int ne = P * N / kBlock;
+    float *S = lds + L.S, *Bb = lds + L.Bb, *xb = lds + L.xb, *wb = lds + L.wb;
+    const float *lam = lds + L.lam, *dlt = lds + L.dlt;
+    const float lam_last = lam[v.n_valid - 1];
+
+    float acc[kMaxS];
+#pragma unroll
+    for (int k = 0; k < kMaxS; ++k)
+        acc[k] = 0.0f;
+
+    for (int jb = 0; jb < v.n_valid; jb += kJB) {
+        const int nj = min(kJB, v.n_valid - jb);
+        for (int e = tid; e < nj * N; e += kBlock) {
+            const int jj = e / N, n = e % N;
+            Bb[jj * N1 + n] = IO::ld(v.brow(jb + jj), n);
+        }
+        for (int e = tid; e < nj * P; e += kBlock) {
+            const int jj = e / P, p = e % P;
+            xb[jj * P + p] = IO::ld(v.xrow(jb + jj), p);
+        }
+        if (tid < nj)
+            wb[tid] = state_weight(lam_last, lam[jb + tid], dlt[jb + tid]);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMaxS; ++k) {
+            if (k < ne) {
+                const int e = tid + kBlock * k;
+                const int p = e / N, n = e % N;
+                float a = acc[k];
+                for (int jj = 0; jj < nj; ++jj)
+                    a = fmaf(wb[jj] * xb[jj * P + p], Bb[jj * N1 + n], a);
+                acc[k] = a;
+            }
+        }
+        __syncthreads();
+    }
+    const float dec = decay_exp(lam_last);
+#pragma unroll
+    for (int k = 0; k < kMaxS; ++k) {
+        if (k < ne) {
+            const int e = tid + kBlock * k;
+            const int p = e / N, n = e % N;
+            S[p * N1 + n] = fmaf(dec, S[p * N1 + n], acc[k]);
+        }
+    }
+    __syncthreads();
+}
+
+__device__ void state_load(float *S, const float *src, int P, int N) {
+    const int N1 = N + 1;
+    for (int e = threadIdx.x; e < P * N; e += kBlock) {
+        const int p = e / N, n = e % N;
+        S[p * N1 + n] = src ? src[e] : 0.0f;
+    }
+    __syncthreads();
+}
+
+__device__ void state_store(float *dst, const float *S, int P, int N) {
+    const int N1 = N + 1;
+    for (int e = threadIdx.x; e < P * N; e += kBlock) {
+        const int p = e / N, n = e % N;
+        dst[e] = S[p * N1 + n];
+    }
+}
+
+// One workgroup per (head, sequence); chunks in order, the fp32 state stays
+// in LDS from one chunk to the next.
+template <class IO, class DT>
+__global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
+    extern __shared__ float lds[];
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, P = d.P, N = d.N, Q = d.Q;
+    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    const int g = h / (H / G);
+    const int64_t PN = (int64_t)P * N;
+    const LdsLayout L(P, N);
+
+    const int64_t t0 = a.cu[s];
+    const int len = a.cu[s + 1] - a.cu[s];
+    const int slot = a.replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
+    if (a.replay && (len == 0 || slot < 0 || slot >= a.num_slots))
+        return;
+    const int nbuf = a.replay ? a.buf_len[slot] : 0;
+    if (nbuf < 0 || nbuf >= Q)  // corrupt slot metadata: leave the slot alone
+        return;
+
+    const float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+                                 : (a.init_state ? a.init_state + ((int64_t)s * H + h) * PN
+                                                 : nullptr);
+    state_load(lds + L.S, init, P, N);
+
+    ChunkView<IO, DT> v;
+    v.x = static_cast<const T *>(a.x);
+    v.B = static_cast<const T *>(a.B);
+    v.C = static_cast<const T *>(a.C);
+    v.dt = static_cast<const TD *>(a.dt);
+    v.bx = a.replay ? static_cast<const T *>(a.buf_x) + (int64_t)slot * Q * H * P : nullptr;
+    v.bB = a.replay ? static_cast<const T *>(a.buf_B) + (int64_t)slot * Q * G * N : nullptr;
+    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H : nullptr;
+    v.h = h; v.g = g; v.H = H; v.G = G; v.P = P; v.N = N;
+
+    const float A_h = a.A[h];
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const int total = nbuf + len;
+    const int nchunks = (total + Q - 1) / Q;
+    const int nfull = total / Q;
+    float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+                          : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
+                                              : nullptr);
+    const bool write_bnd = bnd && (!a.replay || nfull > 0);
+    T *y = static_cast<T *>(a.y);
+
+    for (int c = 0; c < nchunks; ++c) {
+        if (c == nfull && write_bnd)
+            state_store(bnd, lds + L.S, P, N);
+        v.nb = (c == 0) ? nbuf : 0;
+        v.n_valid = min(Q, total - c * Q);
+        v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
+        prepare_chunk(v, A_h, bias, d.softplus, lds, L);
+        for (int rt = (v.nb / kRows) * kRows; rt < v.n_valid; rt += kRows)
+            emit_rows(v, max(rt, v.nb), min(rt + kRows, v.n_valid), D_h, y, lds, L);
+        if (v.n_valid == Q || (!a.replay && a.final_state))
+            chunk_state_update(v, lds, L);
+    }
+    if (nfull == nchunks && write_bnd)
+        state_store(bnd, lds + L.S, P, N);
+    if (!a.replay && a.final_state)
+        state_store(a.final_state + ((int64_t)s * H + h) * PN, lds + L.S, P, N);
+}
+
+// One workgroup per (head, batch row): replay the slot's buffered tokens
+// plus the new token, emit the new row, append the token, and commit the
+// chunk-end state when the chunk fills.
+template <class IO, class DT>
+__global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
+    extern __shared__ float lds[];
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, P = d.P, N = d.N, Q = d.Q;
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int hpg = H / G, g = h / hpg;
+    const int64_t PN = (int64_t)P * N;
+    const LdsLayout L(P, N);
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0 || slot >= a.num_slots)
+        return;
+    const int k = a.buf_len[slot];
+    if (k < 0 || k >= Q)
+        return;
+    float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
+    state_load(lds + L.S, st, P, N);
+
+    T *bx = static_cast<T *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    T *bB = static_cast<T *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+
+    ChunkView<IO, DT> v;
+    v.x = static_cast<const T *>(a.x);
+    v.B = static_cast<const T *>(a.B);
+    v.C = static_cast<const T *>(a.C);
+    v.dt = static_cast<const TD *>(a.dt);
+    v.bx = bx; v.bB = bB; v.bdt = bdt;
+    v.h = h; v.g = g; v.H = H; v.G = G; v.P = P; v.N = N;
+    v.tok_base = b;
+    v.nb = k;
+    v.n_valid = k + 1;
+
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    prepare_chunk(v, a.A[h], bias, d.softplus, lds, L);
+    emit_rows(v, k, k + 1, a.D ? a.D[h] : 0.0f, static_cast<T *>(a.y), lds, L);
+
+    // append the new token at buffer position k (reads above touch only
+    // positions < k of the buffer)
+    const int tid = threadIdx.x;
+    const T *xin = static_cast<const T *>(a.x) + ((int64_t)b * H + h) * P;
+    for (int p = tid; p < P; p += kBlock)
+        bx[((int64_t)k * H + h) * P + p] = xin[p];
+    if (tid == 0)
+        bdt[(int64_t)k * H + h] = static_cast<const TD *>(a.dt)[(int64_t)b * H + h];
+    if (h % hpg == 0) {
+        const T *bin = static_cast<const T *>(a.B) + ((int64_t)b * G + g) * N;
+        for (int n = tid; n < N; n += kBlock)
+            bB[((int64_t)k * G + g) * N + n] = bin[n];
+        if (a.buf_C) {
+            T *bC = static_cast<T *>(a.buf_C) + (int64_t)slot * Q * G * N;
+            const T *cin = static_cast<const T *>(a.C) + ((int64_t)b * G + g) * N;
+            for (int n = tid; n < N; n += kBlock)
+                bC[((int64_t)k * G + g) * N + n] = cin[n];
+        }
+    }
+    if (k + 1 == Q) {
+        chunk_state_update(v, lds, L);
+        state_store(st, lds + L.S, P, N);
+    }
+}
+
+// buf_len / boundary_pos advance after a decode step (separate launch: every
+// head's workgroup of a slot reads buf_len first).
+__global__ void k_decode_advance(int batch, const int32_t *slot_idx, int32_t *buf_len,
+                                 int64_t *boundary_pos, int Q, int num_slots) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch)
+        return;
+    const int slot = slot_idx ? slot_idx[b] : b;
+    if (slot < 0 || slot >= num_slots)
+        return;
+    const int k = buf_len[slot];
+    if (k < 0 || k >= Q)
+        return;
+    if (k + 1 == Q) {
+        buf_len[slot] = 0;
+        boundary_pos[slot] += Q;
+    } else {
+        buf_len[slot] = k + 1;
+    }
+}
+
+// Trailing partial chunk -> slot buffers; buf_len / boundary_pos update;
+// optional boundary-state copy. One workgroup per sequence.
+template <class IO, class DT>
+__global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int H = d.H, G = d.G, P = d.P, N = d.N, Q = d.Q;
+    const int slot = a.slot_idx ? a.slot_idx[s] : s;
+    const int64_t t0 = a.cu[s];
+    const int len = a.cu[s + 1] - a.cu[s];
+    if ((!a.fresh && len == 0) || slot < 0 || slot >= a.num_slots)
+        return;
+    const int nbuf = a.fresh ? 0 : a.buf_len[slot];
+    if (nbuf < 0 || nbuf >= Q)
+        return;
+    const int total = nbuf + len;
+    const int nfull = total / Q, tail = total % Q;
+    // new tokens [src0, len) go to buffer positions dst0..
+    const int src0 = nfull == 0 ? 0 : len - tail;
+    const int dst0 = nfull == 0 ? nbuf : 0;
+    const int ntok = len - src0;
+
+    const T *x = static_cast<const T *>(a.x);
+    const T *B = static_cast<const T *>(a.B);
+    const T *C = static_cast<const T *>(a.C);
+    const TD *dt = static_cast<const TD *>(a.dt);
+    T *bx = static_cast<T *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    T *bB = static_cast<T *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
+    for (int64_t e = tid; e < ntok * HP; e += kBlock)
+        bx[dst0 * HP + e] = x[(t0 + src0) * HP + e];
+    for (int64_t e = tid; e < (int64_t)ntok * H; e += kBlock)
+        bdt[(int64_t)dst0 * H + e] = dt[(t0 + src0) * H + e];
+    for (int64_t e = tid; e < ntok * GN; e += kBlock)
+        bB[dst0 * GN + e] = B[(t0 + src0) * GN + e];
+    if (a.buf_C) {
+        T *bC = static_cast<T *>(a.buf_C) + (int64_t)slot * Q * G * N;
+        for (int64_t e = tid; e < ntok * GN; e += kBlock)
+            bC[dst0 * GN + e] = C[(t0 + src0) * GN + e];
+    }
+    if (a.state_src) {
+        const int64_t HPN = HP * N;
+        const float *src = a.state_src + (int64_t)s * HPN;
+        float *dst = a.cache_state + (int64_t)slot * HPN;
+        for (int64_t e = tid; e < HPN; e += kBlock)
+            dst[e] = src[e];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        a.buf_len[slot] = nfull == 0 ? total : tail;
+        a.boundary_pos[slot] = (a.fresh ? 0 : a.boundary_pos[slot]) + (int64_t)nfull * Q;
+    }
+}
+
+// Recurrent update, one workgroup per (head, batch row). Thread t owns the
+// float4 groups f = t + 256 i of the [P, N] state (coalesced rows); row p's
+// output is a butterfly sum over the N/4 lanes that hold it.
+template <class IO, class DT>
+__global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, P = d.P, N = d.N;
+    const int b = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x;
+    const int g = h / (H / G);
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0 || slot >= a.num_slots)
+        return;
+    const int n4 = N / 4;
+    const int q = tid % n4;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float dl = delta_of(DT::ld(static_cast<const TD *>(a.dt), (int64_t)b * H + h), bias,
+                              d.softplus);
+    const float alpha = decay_exp(dl * a.A[h]);
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    const T *Bt = static_cast<const T *>(a.B) + ((int64_t)b * G + g) * N + 4 * q;
+    const T *Ct = static_cast<const T *>(a.C) + ((int64_t)b * G + g) * N + 4 * q;
+    float bv[4], cv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bv[i] = IO::ld(Bt, i);
+        cv[i] = IO::ld(Ct, i);
+    }
+    const T *xt = static_cast<const T *>(a.x) + ((int64_t)b * H + h) * P;
+    float4 *st = reinterpret_cast<float4 *>(a.state + ((int64_t)slot * H + h) * P * N);
+    T *y = static_cast<T *>(a.y) + ((int64_t)b * H + h) * P;
+    const int nf = P * n4;
+    for (int f = tid; f < nf; f += kBlock) {
+        const int p = f / n4;
+        const float xv = IO::ld(xt, p);
+        const float dx = dl * xv;
+        float4 s4 = st[f];
+        s4.x = fmaf(alpha, s4.x, dx * bv[0]);
+        s4.y = fmaf(alpha, s4.y, dx * bv[1]);
+        s4.z = fmaf(alpha, s4.z, dx * bv[2]);
+        s4.w = fmaf(alpha, s4.w, dx * bv[3]);
+        st[f] = s4;
+        float part = s4.x * cv[0];
+        part = fmaf(s4.y, cv[1], part);
+        part = fmaf(s4.z, cv[2], part);
+        part = fmaf(s4.w, cv[3], part);
+        for (int off = 1; off < n4; off <<= 1)
+            part = part + __shfl_xor(part, off, 64);
+        if (q == 0) {
+            float yv = fmaf(D_h, xv, part);
+            y[p] = IO::cvt(yv + 0.0f);
+        }
+    }
+}
+
+template <class K>
+hipError_t prep_lds(K kernel, size_t bytes) {
+    if (bytes > 64 * 1024)
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    return hipSuccess;
+}
+
+template <class IO, class DT>
+hipError_t scan_impl(const ScanArgs &a, hipStream_t stream) {
+    const LdsLayout L(a.d.P, a.d.N);
+    const size_t bytes = sizeof(float) * L.total;
+    hipError_t e = prep_lds(k_scan<IO, DT>, bytes);
+    if (e != hipSuccess)
+        return e;
+    k_scan<IO, DT><<<dim3(a.d.H * a.S), dim3(kBlock), bytes, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <class IO, class DT>
+hipError_t decode_impl(const DecodeArgs &a, hipStream_t stream) {
+    const LdsLayout L(a.d.P, a.d.N);
+    const size_t bytes = sizeof(float) * L.total;
+    hipError_t e = prep_lds(k_decode<IO, DT>, bytes);
+    if (e != hipSuccess)
+        return e;
+    k_decode<IO, DT><<<dim3(a.d.H * a.batch), dim3(kBlock), bytes, stream>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_decode_advance, dim3((a.batch + 255) / 256), dim3(256), 0, stream,
+                       a.batch, a.slot_idx, a.buf_len, a.boundary_pos, a.d.Q, a.num_slots);
+    return hipGetLastError();
+}
+
+template <class IO, class DT>
+hipError_t commit_impl(const CommitArgs &a, hipStream_t stream) {
+    k_commit<IO, DT><<<dim3(a.S), dim3(kBlock), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <class IO, class DT>
+hipError_t ssu_impl(const SsuArgs &a, hipStream_t stream) {
+    k_ssu<IO, DT><<<dim3(a.d.H * a.batch), dim3(kBlock), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <template <class, class> class F, class Args>
+hipError_t dispatch(const Args &a, hipStream_t stream) {
+    if (a.d.io_bf16)
+        return a.d.dt_bf16 ? F<IoBF16, IoBF16>::run(a, stream) : F<IoBF16, IoF32>::run(a, stream);
+    return a.d.dt_bf16 ? F<IoF32, IoBF16>::run(a, stream) : F<IoF32, IoF32>::run(a, stream);
+}
+
+template <class IO, class DT> struct ScanF { static hipError_t run(const ScanArgs &a, hipStream_t s) { return scan_impl<IO, DT>(a, s); } };
+template <class IO, class DT> struct DecodeF { static hipError_t run(const DecodeArgs &a, hipStream_t s) { return decode_impl<IO, DT>(a, s); } };
+template <class IO, class DT> struct CommitF { static hipError_t run(const CommitArgs &a, hipStream_t s) { return commit_impl<IO, DT>(a, s); } };
+template <class IO, class DT> struct SsuF { static hipError_t run(const SsuArgs &a, hipStream_t s) { return ssu_impl<IO, DT>(a, s); } };
+
+}  // namespace
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) { return dispatch<ScanF>(a, stream); }
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return dispatch<DecodeF>(a, stream); }
+hipError_t launch_commit(const CommitArgs &a, hipStream_t stream) { return dispatch<CommitF>(a, stream); }
+hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream) { return dispatch<SsuF>(a, stream); }
+
+}  // namespace ssd

@@ -136,3 +136,22 @@ def replay_prefix_lengths(batch: int, chunk_size: int, seed: int) -> np.ndarray:
     boundary state and k_i buffered tokens."""
     rng = np.random.default_rng([seed, 0xDEC0DE])
     return chunk_size + rng.integers(0, chunk_size, size=batch)
+
+
+def make_tokens_torch(T: int, H: int, G: int, P: int, N: int, seed: int, device,
+                      io_dtype: str = "bf16", dt_dtype: str | None = None):
+    """Device-side draw of the same distributions for large workloads:
+    x, B, C ~ N(0, 1) and raw dt ~ 0.5 N(0, 1), drawn in float32 by torch's
+    generator on `device` and rounded to the storage dtype (round to nearest
+    even). Returns torch tensors (x[T,H,P], dt[T,H], B[T,G,N], C[T,G,N]).
+    Consumers that need float64 copies read these tensors back exactly."""
+    import torch
+    dt_dtype = dt_dtype or io_dtype
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 0x5EED)
+    x = torch.randn((T, H, P), generator=g, device=device).to(tdt[io_dtype])
+    dt = (0.5 * torch.randn((T, H), generator=g, device=device)).to(tdt[dt_dtype])
+    Bm = torch.randn((T, G, N), generator=g, device=device).to(tdt[io_dtype])
+    Cm = torch.randn((T, G, N), generator=g, device=device).to(tdt[io_dtype])
+    return x, dt, Bm, Cm

@@ -1,0 +1,202 @@
+/*
+ * ssd_replay.h -- C ABI of the MI355X (gfx950) Mamba2 SSD scan with
+ * exact-replay decode.
+ *
+ * Sources (web pages; the code cites them by title and section):
+ *  [RFC]  vLLM RFC "Mamba2: exact-replay decode so that prefill, chunked
+ *         prefill and decode produce identical bits".
+ *  [RSSM] ReplaySSM reproduction README, "Cache SSM inputs instead of
+ *         writing back state for every token".
+ *
+ * The scan (per head h, group g = h / (H/G), token t):
+ *   delta_t = softplus(dt_t + dt_bias[h])      (dt_softplus = 1)
+ *           = dt_t + dt_bias[h]                (dt_softplus = 0)
+ *   state   = exp(delta_t A[h]) state + delta_t x_t (outer) B_t   [P x N]
+ *   y_t     = state . C_t + D[h] x_t                               [P]
+ * computed chunk by chunk ([RFC] section 1 names the chunked scan; [RSSM]
+ * "Core equations" give the per-chunk closed form) on a chunk grid anchored
+ * at each sequence's boundary position.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless their name ends in _host. Arrays are
+ *    row-major and contiguous with the layouts given below.
+ *  - T = packed token count, S = number of sequences, Q = chunk_size.
+ *    x, y: [T,H,P]; dt: [T,H] (raw dt); B, C: [T,G,N]; A, D, dt_bias: [H]
+ *    fp32; states: [.,H,P,N] fp32; cu_seqlens: [S+1] int32, cu[0] = 0,
+ *    non-decreasing, cu[S] = T.
+ *  - Every call is asynchronous on `stream`, allocates no device memory and
+ *    returns SSD_OK (0) or a negative ssd_status. All argument checks run on
+ *    the host before anything is launched, so a failed check launches
+ *    nothing. Launch failures map to SSD_ERR_HIP. No exception crosses the
+ *    ABI.
+ *  - The caller owns every buffer; the library frees nothing and keeps no
+ *    per-call state. Outputs must not alias inputs unless stated.
+ *  - Results are deterministic: fixed tile shapes, fixed reduction orders,
+ *    no atomics in arithmetic.
+ */
+#ifndef SSD_REPLAY_H
+#define SSD_REPLAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,            /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,           /* sizes inconsistent (H % G, cu_seqlens, counts) */
+    SSD_ERR_DTYPE = -3,           /* unknown dtype code */
+    SSD_ERR_STATE_NOT_FP32 = -4,  /* [RFC] section 4: fp32 state is required */
+    SSD_ERR_CHUNK_MISMATCH = -5,  /* [RFC] section 4: one chunk size for prefill and decode */
+    SSD_ERR_WORKSPACE = -6,       /* workspace missing or too small */
+    SSD_ERR_UNSUPPORTED = -7,     /* P, N or chunk_size outside the built set */
+    SSD_ERR_HIP = -8              /* a HIP launch or runtime call failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Problem shape shared by all calls.
+ * Supported: chunk_size in {16,32,64,128,256}; P and N in {16,32,64,128};
+ * H % G == 0; io_dtype (x, B, C, y) and dt_dtype in {SSD_F32, SSD_BF16};
+ * state_dtype must be SSD_F32. */
+typedef struct {
+    int32_t H, G, P, N, chunk_size;
+    int32_t io_dtype;
+    int32_t dt_dtype;
+    int32_t state_dtype;
+    int32_t dt_softplus;
+} ssd_shape;
+
+/* Exact-replay cache for num_slots sequences ([RFC] section 3, "State
+ * representation"): the fp32 state at the last multiple of the chunk size
+ * plus a token-major buffer of the inputs received since then.
+ *   state         [num_slots,H,P,N] fp32   boundary state
+ *   buf_x         [num_slots,Q,H,P] io     buffered x
+ *   buf_dt        [num_slots,Q,H]   dt     buffered raw dt ([RFC] section 3:
+ *                                          raw dt, not softplus(dt + bias))
+ *   buf_B, buf_C  [num_slots,Q,G,N] io     buffered B and C; buf_C may be NULL
+ *                                          (the scan never reads buffered C)
+ *   buf_len       [num_slots] int32        tokens buffered, in [0, Q)
+ *   boundary_pos  [num_slots] int64        sequence position of the boundary,
+ *                                          a multiple of Q
+ * A fresh slot is all zeros. The struct itself is a host object; the
+ * pointers in it are device pointers. */
+typedef struct {
+    float *state;
+    void *buf_x;
+    void *buf_dt;
+    void *buf_B;
+    void *buf_C;
+    int32_t *buf_len;
+    int64_t *boundary_pos;
+    int32_t num_slots;
+    int32_t chunk_size;
+    int32_t state_dtype;
+} ssd_replay_cache;
+
+/* Human-readable name of a status code. Never NULL. */
+const char *ssd_status_string(int status);
+
+/* Bytes of device memory one exact-replay cache of num_slots slots needs
+ * (state + buffers + metadata), with or without the C buffer; 0 for a bad
+ * shape. [RFC] section 4 sizes the buffer at about 1.16 MiB and the fp32
+ * state at 1 MiB per layer and sequence for H=32, G=1, P=64, N=128, Q=256. */
+size_t ssd_replay_cache_bytes(const ssd_shape *shape, int32_t num_slots,
+                              int32_t with_C);
+
+/* Workspace bytes ssd_prefill_varlen needs (currently 0: the prefill kernel
+ * carries the inter-chunk state on chip). */
+size_t ssd_prefill_workspace_bytes(const ssd_shape *shape, int32_t num_seqs,
+                                   int64_t total_tokens);
+
+/* Chunked scan over a varlen pack ([RFC] section 1: the prefill kernel;
+ * section 2, item 3: prefix- and packing-invariant; item 4: fp32 carry
+ * between chunks).
+ * Each sequence s starts from init_state[s] (NULL = zeros) on a chunk grid
+ * anchored at its first token; chunks never straddle sequences.
+ *   y              [T,H,P]   all rows written
+ *   final_state    [S,H,P,N] state after the last token (NULL = not stored)
+ *   boundary_state [S,H,P,N] state after the last full chunk, i.e. after
+ *                  len - len % Q tokens; init_state when len < Q (NULL = not
+ *                  stored)
+ * cu_seqlens_host is read synchronously for the checks; cu_seqlens is the
+ * same array on the device. */
+int ssd_prefill_varlen(const ssd_shape *shape, int32_t num_seqs,
+                       int64_t total_tokens, const int32_t *cu_seqlens_host,
+                       const int32_t *cu_seqlens, const void *x, const void *dt,
+                       const float *A, const void *B, const void *C,
+                       const float *D, const float *dt_bias,
+                       const float *init_state, void *y, float *final_state,
+                       float *boundary_state, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Store a fresh prefill into replay-cache slots ([RFC] section 3, "Prefill
+ * / chunked prefill / recompute": the boundary state comes from the last
+ * full chunk and the trailing partial chunk's inputs go to the buffer).
+ * For sequence s of the pack (its x/dt/B/C as passed to ssd_prefill_varlen,
+ * its boundary_state[s] as that call returned it) and slot = slot_idx[s]
+ * (NULL = s): state <- boundary_state[s]; buffer <- the last len % Q
+ * tokens; buf_len <- len % Q; boundary_pos <- len - len % Q.
+ * slot_idx entries must be distinct and < cache->num_slots. */
+int ssd_commit_boundary(const ssd_shape *shape, int32_t num_seqs,
+                        int64_t total_tokens, const int32_t *cu_seqlens_host,
+                        const int32_t *cu_seqlens, const int32_t *slot_idx,
+                        const void *x, const void *dt, const void *B,
+                        const void *C, const float *boundary_state,
+                        const ssd_replay_cache *cache, hipStream_t stream);
+
+/* Exact-replay prefill, chunked prefill or recompute ([RFC] section 3,
+ * second bullet): every sequence resumes at its slot's boundary. The
+ * buffered tokens are put in front of the new ones, their outputs are not
+ * written, the chunk grid is the slot's, and afterwards the slot holds the
+ * state after the last full chunk and the trailing partial chunk.
+ * Sequence s has new tokens cu[s]..cu[s+1]-1 and uses slot slot_idx[s]
+ * (NULL = s); y[T,H,P] receives the new tokens' outputs. Zero-length
+ * sequences leave their slot untouched. Slots must be distinct. */
+int ssd_replay_prefill(const ssd_shape *shape, const ssd_replay_cache *cache,
+                       int32_t num_seqs, int64_t total_tokens,
+                       const int32_t *cu_seqlens_host, const int32_t *cu_seqlens,
+                       const int32_t *slot_idx, const void *x, const void *dt,
+                       const void *B, const void *C, const float *A,
+                       const float *D, const float *dt_bias, void *y,
+                       hipStream_t stream);
+
+/* Exact-replay decode step ([RFC] section 3, first bullet): one new token
+ * per sequence. For slot = slot_idx[b] (NULL = b) holding k = buf_len
+ * tokens, the chunk made of the k buffered tokens plus the new token is
+ * replayed from the boundary state through the prefill's chunk arithmetic,
+ * and the new token's output row goes to y[b]. The token is appended to the
+ * buffer; when it fills the chunk (k + 1 == Q) the chunk's end state becomes
+ * the boundary state, buf_len returns to 0 and boundary_pos advances by Q.
+ * y[b] is bit-identical to the row a single ssd_prefill_varlen over the
+ * whole sequence produces. Inputs x[batch,H,P], dt[batch,H],
+ * B/C[batch,G,N]; y[batch,H,P]. Slots must be distinct. */
+int ssd_replay_decode(const ssd_shape *shape, const ssd_replay_cache *cache,
+                      int32_t batch, const int32_t *slot_idx, const void *x,
+                      const void *dt, const void *B, const void *C,
+                      const float *A, const float *D, const float *dt_bias,
+                      void *y, hipStream_t stream);
+
+/* Recurrent selective-state update, the conventional decode path the RFC
+ * compares against ([RFC] section 1; [RSSM] "Motivation and method": it
+ * reads and writes the full state every token). For slot = slot_idx[b]
+ * (NULL = b): state[slot] <- exp(delta A) state[slot] + delta x (outer) B;
+ * y[b] <- state[slot] . C + D x. state is [num_slots,H,P,N] fp32, updated in
+ * place; x[batch,H,P], dt[batch,H], B/C[batch,G,N], y[batch,H,P].
+ * Slots must be distinct. */
+int ssm_state_update(const ssd_shape *shape, int32_t batch, int32_t num_slots,
+                     const int32_t *slot_idx, float *state, const void *x,
+                     const void *dt, const float *A, const void *B,
+                     const void *C, const float *D, const float *dt_bias,
+                     void *y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_REPLAY_H */

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/ssd_replay.h declares, and rejects bad arguments on the host
+with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import exact_replay_decode_amd as erd
+from exact_replay_decode_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "ssd_replay.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    want = {"ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
+            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
+            "ssd_replay_decode", "ssm_state_update"}
+    assert set(declared_functions()) == want
+    assert set(_lib.EXPORTS) == want
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS.items():
+        assert _lib.status_string(code).startswith(name)
+    assert _lib.status_string(12345) == "unknown ssd_status"
+
+
+def test_cache_bytes_match_printed_memory():
+    """RFC section 4: about 1.16 MiB of buffer (x, dt, B, C with 4-byte dt)
+    plus 1 MiB of fp32 state per layer and sequence at H=32, G=1, P=64,
+    N=128, chunk 256."""
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "rfc_printed_numbers.json")))
+    sh = erd.Shape(32, 1, 64, 128, 256, "bf16", "f32")
+    total = erd.ssd_replay_cache_bytes(sh, 1, with_C=True)
+    state = 32 * 64 * 128 * 4
+    buf = total - state - 4 - 8
+    assert state / 2 ** 20 == g["fp32_state_mib_per_layer_per_seq"]["value"]
+    assert round(buf / 2 ** 20, 2) == g["buffer_mib_per_layer_per_seq"]["value"]
+    assert erd.ssd_replay_cache_bytes(sh, 27, with_C=True) == 27 * total
+    # the scan never reads buffered C: without it the buffer shrinks by G*N*2*Q
+    assert total - erd.ssd_replay_cache_bytes(sh, 1, with_C=False) == 256 * 128 * 2
+
+
+# ---- fail-closed validation (no launch; fake device pointers) -------------
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def shape(**kw):
+    base = dict(H=4, G=1, P=16, N=16, chunk_size=16, io_dtype=1, dt_dtype=1, state_dtype=0,
+                dt_softplus=1)
+    base.update(kw)
+    return _lib.ssd_shape(**base)
+
+
+def prefill(sh, cu=(0, 8), T=8, **over):
+    lib = _lib.load()
+    cu = np.asarray(cu, dtype=np.int32)
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, cu_dev=FAKE)
+    args.update(over)
+    return lib.ssd_prefill_varlen(ctypes.byref(sh), len(cu) - 1, T,
+                                  cu.ctypes.data_as(ctypes.c_void_p), args["cu_dev"], args["x"],
+                                  args["dt"], args["A"], args["B"], args["C"], None, None, None,
+                                  args["y"], None, None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state_dtype=1), -4), (dict(io_dtype=7), -3), (dict(dt_dtype=-1), -3),
+    (dict(H=6, G=4), -2), (dict(H=0), -2), (dict(G=0), -2),
+    (dict(chunk_size=512), -7), (dict(chunk_size=48), -7), (dict(P=256), -7),
+    (dict(N=8), -7), (dict(P=24), -7)])
+def test_prefill_rejects_bad_shapes(kw, code):
+    assert prefill(shape(**kw)) == code
+
+
+def test_prefill_rejects_bad_seqlens_and_nulls():
+    sh = shape()
+    assert prefill(sh, cu=(0, 5), T=8) == -2          # cu[S] != T
+    assert prefill(sh, cu=(1, 8), T=8) == -2          # cu[0] != 0
+    assert prefill(sh, cu=(0, 6, 4, 8), T=8) == -2    # decreasing
+    assert prefill(sh, x=None) == -1
+    assert prefill(sh, A=None) == -1
+    assert prefill(sh, cu_dev=None) == -1
+    assert prefill(shape(), cu=(0,), T=0) == 0        # nothing to do, no launch
+
+
+def cache(sh_c, **kw):
+    base = dict(state=0x1000, buf_x=0x1000, buf_dt=0x1000, buf_B=0x1000, buf_C=None,
+                buf_len=0x1000, boundary_pos=0x1000, num_slots=4, chunk_size=16, state_dtype=0)
+    base.update(kw)
+    return _lib.ssd_replay_cache(**base)
+
+
+def decode(sh, c, batch=2):
+    lib = _lib.load()
+    return lib.ssd_replay_decode(ctypes.byref(sh), ctypes.byref(c), batch, None, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, None, None, FAKE, None)
+
+
+def test_replay_fails_closed():
+    sh = shape()
+    assert decode(sh, cache(sh, state_dtype=1)) == -4        # non-fp32 state
+    assert decode(sh, cache(sh, chunk_size=32)) == -5        # chunk mismatch
+    assert decode(sh, cache(sh, buf_B=None)) == -1
+    assert decode(sh, cache(sh, num_slots=0)) == -2
+    assert decode(sh, cache(sh), batch=5) == -2              # more rows than slots
+    assert decode(shape(state_dtype=1), cache(sh)) == -4
+    assert decode(sh, cache(sh), batch=0) == 0
+    lib = _lib.load()
+    cu = np.asarray([0, 8], dtype=np.int32)
+    c = cache(sh, chunk_size=64)
+    assert lib.ssd_replay_prefill(ctypes.byref(sh), ctypes.byref(c), 1, 8,
+                                  cu.ctypes.data_as(ctypes.c_void_p), FAKE, None, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, None, None, FAKE, None) == -5
+    assert lib.ssd_commit_boundary(ctypes.byref(sh), 1, 8, cu.ctypes.data_as(ctypes.c_void_p),
+                                   FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
+                                   ctypes.byref(cache(sh)), None) == -1
+    assert lib.ssm_state_update(ctypes.byref(shape(state_dtype=1)), 1, 1, None, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == -4
+    assert lib.ssm_state_update(ctypes.byref(sh), 3, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, None, FAKE, None) == -2
+
+
+def test_python_binding_checks_extents():
+    torch = pytest.importorskip("torch")
+    sh = erd.Shape(4, 1, 16, 16, 16, "f32", "f32")
+    x = torch.zeros((8, 4, 16))
+    with pytest.raises(ValueError):
+        erd.ssd_prefill_varlen(sh, [0, 8], x, torch.zeros((8, 3)), torch.zeros(4),
+                               torch.zeros((8, 1, 16)), torch.zeros((8, 1, 16)))

@@ -1,0 +1,272 @@
+"""GPU exact-replay decode and recurrent update, through the C ABI.
+
+Replay decode must reproduce single-shot prefill bit for bit (outputs,
+committed boundary states, buffers); both paths are checked against the
+fp64 oracle within tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_replay_decode_amd as erd
+from exact_replay_decode_amd import synth
+from gpu_cases import (DEV, headwise_max_rel, make_problem, mean_rel_err, same_bits,
+                       y_headwise_max_rel)
+
+pytestmark = pytest.mark.gpu
+
+BF16_MEAN_REL = 3e-3
+STATE_REL = 1e-4
+F32_Y_REL = 1e-4
+
+
+def decode_tokens(shape, cache, x, dt, B, C, A, D, bias, slot=0):
+    """Decode tokens x[0..n) one at a time for one slot; returns y[n,H,P]."""
+    sl = torch.tensor([slot], dtype=torch.int32, device=DEV)
+    ys = []
+    for t in range(x.shape[0]):
+        ys.append(erd.ssd_replay_decode(shape, cache, x[t:t + 1], dt[t:t + 1], B[t:t + 1],
+                                        C[t:t + 1], A, D, bias, slot_idx=sl))
+    return torch.cat(ys)
+
+
+# ---- C0: decode every token of a tiny fp32 scan ----------------------------
+
+def test_c0_decode_every_token():
+    pr = make_problem([64], H=4, G=1, P=16, N=16, Q=16, io="f32")
+    x, dt, B, C = pr.dev(None)
+    y, fin, bnd = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias)
+    cache = erd.ReplayCache(pr.shape, 1, DEV, with_C=True)
+    yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
+    assert same_bits(yd, y)
+    assert same_bits(cache.state[0], bnd[0])
+    assert int(cache.buf_len[0]) == 0 and int(cache.boundary_pos[0]) == 64
+    ref = pr.oracle()
+    assert y_headwise_max_rel(yd, ref.y, pr.cu) <= F32_Y_REL
+
+
+def test_c0_decode_after_split_prefill():
+    pr = make_problem([64], H=4, G=1, P=16, N=16, Q=16, io="f32", seed=4)
+    x, dt, B, C = pr.dev(None)
+    y, _, _ = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias)
+    cache = erd.ReplayCache(pr.shape, 1, DEV)
+    y0 = erd.ssd_replay_prefill(pr.shape, cache, [0, 24], x[:24], dt[:24], B[:24], C[:24],
+                                pr.A, pr.D, pr.bias)
+    assert int(cache.buf_len[0]) == 8 and int(cache.boundary_pos[0]) == 16
+    yd = decode_tokens(pr.shape, cache, x[24:], dt[24:], B[24:], C[24:], pr.A, pr.D, pr.bias)
+    assert same_bits(torch.cat([y0, yd]), y)
+
+
+# ---- C1: 2048 token-by-token decode steps ---------------------------------
+
+@pytest.fixture(scope="module")
+def c1():
+    pr = make_problem([2048], H=32, G=1, P=64, N=128, Q=256)
+    x, dt, B, C = pr.dev(None)
+    y, fin, bnd = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias)
+    return pr, (x, dt, B, C), y, fin, bnd
+
+
+def test_c1_decode_2048_steps_bitwise(c1):
+    pr, (x, dt, B, C), y, fin, bnd = c1
+    cache = erd.ReplayCache(pr.shape, 1, DEV, with_C=True)
+    yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
+    assert same_bits(yd, y)
+    assert same_bits(cache.state[0], bnd[0])
+    # the buffer holds the last chunk's tokens, C included
+    assert int(cache.buf_len[0]) == 0 and int(cache.boundary_pos[0]) == 2048
+    assert same_bits(cache.buf_x[0], x[1792:]) and same_bits(cache.buf_C[0], C[1792:])
+    assert same_bits(cache.buf_B[0], B[1792:]) and same_bits(cache.buf_dt[0], dt[1792:])
+
+
+def test_c1_commit_boundary_then_decode(c1):
+    """Plain prefill of 600 tokens + ssd_commit_boundary, then decode the
+    rest: rows 600..767 replay the partial chunk, 768.. follow a commit."""
+    pr, (x, dt, B, C), y, fin, bnd = c1
+    y6, f6, b6 = erd.ssd_prefill_varlen(pr.shape, [0, 600], x[:600], dt[:600], pr.A, B[:600],
+                                        C[:600], pr.D, pr.bias)
+    cache = erd.ReplayCache(pr.shape, 1, DEV)
+    erd.ssd_commit_boundary(pr.shape, cache, [0, 600], x[:600], dt[:600], B[:600], C[:600], b6)
+    assert int(cache.buf_len[0]) == 88 and int(cache.boundary_pos[0]) == 512
+    yd = decode_tokens(pr.shape, cache, x[600:900], dt[600:900], B[600:900], C[600:900],
+                       pr.A, pr.D, pr.bias)
+    assert same_bits(torch.cat([y6, yd]), y[:900])
+    mism = (yd.view(torch.int16) != y[600:900].view(torch.int16)).flatten(1).any(1)
+    assert int(mism.sum()) == 0
+
+
+def test_c1_preemption_recompute(c1):
+    """Decode to token 600, drop everything but the cache snapshot, recompute
+    tokens 600..899 as one unaligned prefill, then keep decoding."""
+    pr, (x, dt, B, C), y, _, _ = c1
+    cache = erd.ReplayCache(pr.shape, 1, DEV)
+    decode_tokens(pr.shape, cache, x[:600], dt[:600], B[:600], C[:600], pr.A, pr.D, pr.bias)
+    snap = cache.clone()
+    del cache
+    y_re = erd.ssd_replay_prefill(pr.shape, snap, [0, 300], x[600:900], dt[600:900],
+                                  B[600:900], C[600:900], pr.A, pr.D, pr.bias)
+    yd = decode_tokens(pr.shape, snap, x[900:1000], dt[900:1000], B[900:1000], C[900:1000],
+                       pr.A, pr.D, pr.bias)
+    assert same_bits(y_re, y[600:900]) and same_bits(yd, y[900:1000])
+
+
+def test_c1_ssu_differs_in_bits_but_matches_oracle(c1):
+    """Negative control: the recurrent update is a different rounding of the
+    same math, so its rows differ in bits from the chunked scan while both
+    sit within tolerance of the oracle."""
+    pr, (x, dt, B, C), y, _, _ = c1
+    state = torch.zeros((1, 32, 64, 128), dtype=torch.float32, device=DEV)
+    ys = []
+    for t in range(512):
+        ys.append(erd.ssm_state_update(pr.shape, state, x[t:t + 1], dt[t:t + 1], B[t:t + 1],
+                                       C[t:t + 1], pr.A, pr.D, pr.bias))
+    ys = torch.cat(ys)
+    assert not same_bits(ys, y[:512])
+    frac_equal = float((ys.view(torch.int16) == y[:512].view(torch.int16)).float().mean())
+    print(f"SSU vs SSD bit-identical elements: {100 * frac_equal:.1f} %")
+    ref = pr.oracle()
+    assert mean_rel_err(ys, ref.y[:512]) <= BF16_MEAN_REL
+
+
+# ---- C3: batched decode, B = 256 ------------------------------------------
+
+def _c3_setup(Q, steps=300, seed=0):
+    S, H, P, N = 256, 32, 64, 128
+    shape = erd.Shape(H, 1, P, N, Q, "bf16", "bf16")
+    hp = synth.make_head_params(H, seed)
+    pre = synth.replay_prefix_lengths(S, 256, seed)   # 256 + k_i, k_i in [0, 256)
+    lengths = pre + steps
+    cu = synth.cu_seqlens(lengths)
+    x, dt, B, C = synth.make_tokens_torch(int(cu[-1]), H, 1, P, N, seed, DEV)
+    A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    return shape, hp, pre, lengths, cu, (x, dt, B, C), (A, D, bias)
+
+
+def _c3_run(Q):
+    shape, hp, pre, lengths, cu, (x, dt, B, C), (A, D, bias) = _c3_setup(Q)
+    S = len(pre)
+    y_ss, fin_ss, bnd_ss = erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias)
+    # replay: prefill the prefixes, then 300 batched decode steps
+    idx_pre = np.concatenate([np.arange(cu[s], cu[s] + pre[s]) for s in range(S)])
+    ip = torch.from_numpy(idx_pre).to(DEV)
+    cache = erd.ReplayCache(shape, S, DEV)
+    y_pre = erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip],
+                                   C[ip], A, D, bias)
+    assert same_bits(y_pre, y_ss[ip])
+    steps = int(lengths[0] - pre[0])
+    ydec = []
+    for k in range(steps):
+        it = torch.from_numpy((cu[:-1] + pre + k).astype(np.int64)).to(DEV)
+        ydec.append(erd.ssd_replay_decode(shape, cache, x[it], dt[it], B[it], C[it], A, D, bias))
+    ydec = torch.stack(ydec, 1)                       # [S, steps, H, P]
+    idx_dec = np.stack([cu[:-1] + pre + k for k in range(steps)], 1)
+    want = y_ss[torch.from_numpy(idx_dec.astype(np.int64)).to(DEV)]
+    return shape, hp, pre, lengths, cu, (x, dt, B, C), ydec, want, cache, bnd_ss, fin_ss
+
+
+@pytest.mark.parametrize("Q", [256, 16])
+def test_c3_batched_replay_decode_bitwise(Q):
+    shape, hp, pre, lengths, cu, (x, dt, B, C), ydec, want, cache, bnd, fin = _c3_run(Q)
+    assert same_bits(ydec, want)
+    # offset invariant: every committed boundary sits on the chunk grid and
+    # holds exactly the single-shot state at that position
+    bp = cache.boundary_pos.cpu().numpy()
+    assert np.all(bp % Q == 0)
+    assert np.array_equal(bp, (lengths // Q) * Q)
+    assert np.array_equal(cache.buf_len.cpu().numpy(), lengths % Q)
+    assert same_bits(cache.state, bnd)
+    # oracle parity on sampled sequences (decode rows and boundary state)
+    from oracle import scan
+    for s in (0, 131, 255):
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref = scan(erd.to_f64(x[a:b]), erd.to_f64(dt[a:b]), hp.A, erd.to_f64(B[a:b]),
+                   erd.to_f64(C[a:b]), [0, b - a], Q, D=hp.D, dt_bias=hp.dt_bias)
+        assert mean_rel_err(ydec[s], ref.y[pre[s]:]) <= BF16_MEAN_REL
+        assert headwise_max_rel(cache.state[s:s + 1].cpu().numpy(), ref.boundary_state) <= STATE_REL
+
+
+def test_c3_replay_batch_invariance():
+    """A slot's decode output does not depend on which other slots share
+    the call, nor on their offsets."""
+    shape, hp, pre, lengths, cu, (x, dt, B, C), (A, D, bias) = _c3_setup(256, steps=4)
+    S = len(pre)
+    idx_pre = np.concatenate([np.arange(cu[s], cu[s] + pre[s]) for s in range(S)])
+    ip = torch.from_numpy(idx_pre).to(DEV)
+    cache = erd.ReplayCache(shape, S, DEV)
+    erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip], C[ip],
+                           A, D, bias)
+    it = torch.from_numpy((cu[:-1] + pre).astype(np.int64)).to(DEV)
+    full = erd.ssd_replay_decode(shape, cache.clone(), x[it], dt[it], B[it], C[it], A, D, bias)
+    for sub in ([5], [17, 200, 3], list(range(0, 256, 7))):
+        sl = torch.tensor(sub, dtype=torch.int32, device=DEV)
+        c2 = cache.clone()
+        ys = erd.ssd_replay_decode(shape, c2, x[it][sl.long()], dt[it][sl.long()],
+                                   B[it][sl.long()], C[it][sl.long()], A, D, bias, slot_idx=sl)
+        assert same_bits(ys, full[sl.long()])
+
+
+def test_ssu_batch_invariance():
+    shape, hp, pre, lengths, cu, (x, dt, B, C), (A, D, bias) = _c3_setup(256, steps=1)
+    S = 256
+    st0 = torch.randn((S, 32, 64, 128), generator=torch.Generator(device=DEV).manual_seed(3),
+                      device=DEV)
+    it = torch.from_numpy((cu[:-1] + pre).astype(np.int64)).to(DEV)
+    xs, dts, Bs, Cs = x[it], dt[it], B[it], C[it]
+    st_full = st0.clone()
+    y_full = erd.ssm_state_update(shape, st_full, xs, dts, Bs, Cs, A, D, bias)
+    for b in (1, 4, 16, 64, 256):
+        st = st0.clone()
+        yb = erd.ssm_state_update(shape, st, xs[:b], dts[:b], Bs[:b], Cs[:b], A, D, bias)
+        assert same_bits(yb, y_full[:b]) and same_bits(st[:b], st_full[:b])
+        assert same_bits(st[b:], st0[b:])
+
+
+def test_ssu_matches_oracle_from_a_state():
+    """40 recurrent steps from the fp32 state after each prefix."""
+    shape, hp, pre, lengths, cu, (x, dt, B, C), (A, D, bias) = _c3_setup(256, steps=40)
+    from oracle import scan
+    S = len(pre)
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    _, state, _ = erd.ssd_prefill_varlen(shape, synth.cu_seqlens(pre), x[ip], dt[ip], A,
+                                         B[ip], C[ip], D, bias)
+    ys = []
+    for k in range(40):
+        it = torch.from_numpy((cu[:-1] + pre + k).astype(np.int64)).to(DEV)
+        ys.append(erd.ssm_state_update(shape, state, x[it], dt[it], B[it], C[it], A, D, bias))
+    ys = torch.stack(ys, 1)
+    for s in (0, 99):
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref = scan(erd.to_f64(x[a:b]), erd.to_f64(dt[a:b]), hp.A, erd.to_f64(B[a:b]),
+                   erd.to_f64(C[a:b]), [0, b - a], 256, D=hp.D, dt_bias=hp.dt_bias)
+        assert mean_rel_err(ys[s], ref.y[pre[s]:]) <= BF16_MEAN_REL
+        assert headwise_max_rel(state[s:s + 1].cpu().numpy(), ref.final_state) <= STATE_REL
+
+
+# ---- C4: 24-layer scan stack, 600-token prompt + 300 decode steps ---------
+
+def test_c4_layer_stack():
+    H, P, N, Q = 24, 64, 128, 256
+    for layer in range(24):
+        pr = make_problem([900], H=H, G=1, P=P, N=N, Q=Q, seed=100 + layer)
+        x, dt, B, C = pr.dev(None)
+        y, _, bnd = erd.ssd_prefill_varlen(pr.shape, [0, 900], x, dt, pr.A, B, C, pr.D, pr.bias)
+        cache = erd.ReplayCache(pr.shape, 1, DEV)
+        y0 = erd.ssd_replay_prefill(pr.shape, cache, [0, 600], x[:600], dt[:600], B[:600],
+                                    C[:600], pr.A, pr.D, pr.bias)
+        yd = decode_tokens(pr.shape, cache, x[600:], dt[600:], B[600:], C[600:], pr.A, pr.D,
+                           pr.bias)
+        rows = (yd.view(torch.int16) != y[600:].view(torch.int16)).flatten(1).any(1)
+        assert same_bits(y0, y[:600]) and int(rows.sum()) == 0, layer
+        assert same_bits(cache.state[0], bnd[0])
+        # chunked prefill at most 100 tokens per call
+        c2 = erd.ReplayCache(pr.shape, 1, DEV)
+        parts = []
+        for a in range(0, 900, 100):
+            parts.append(erd.ssd_replay_prefill(pr.shape, c2, [0, 100], x[a:a + 100],
+                                                dt[a:a + 100], B[a:a + 100], C[a:a + 100],
+                                                pr.A, pr.D, pr.bias))
+        assert same_bits(torch.cat(parts), y), layer
+        if layer == 0:
+            ref = pr.oracle()
+            assert mean_rel_err(yd, ref.y[600:]) <= BF16_MEAN_REL
