@@ -1,0 +1,299 @@
+"""Benchmark of the Mamba2 SSD hot path on one MI355X.
+
+One step = one pass over every stage of the path on synthetic inputs:
+  1. chunked-scan prefill of 256 sequences x 2048 tokens (H=32, G=1, P=64,
+     N=128, chunk 256, bf16 x/dt/B/C/y, fp32 state), boundary states out;
+  2. boundary commit of those sequences into an exact-replay cache;
+  3. R exact-replay decode steps over a batch of 256 sequences whose caches
+     hold a boundary state plus 0..255 buffered tokens (chunk 256);
+  4. R recurrent state-update steps over the same batch (comparison path);
+  5. R exact-replay decode steps with chunk 16 (refresh every 16 tokens).
+Inputs are resident in HBM before timing starts. Every stage is timed with
+HIP events on the stream the library launches on. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps R]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD prefill tokens/s + replay-decode steps/s at B=256; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
+                  "ssd_internal.hpp"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_replay_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_bytes(T, S, H, G, P, N, io=2, dtb=2):
+    """Algorithmic HBM bytes of one prefill launch: read x, dt, B, C once,
+    write y and the per-sequence fp32 boundary state."""
+    return T * H * P * io * 2 + T * H * dtb + 2 * T * G * N * io + S * H * P * N * 4
+
+
+def prefill_flops(T, H, G, P, N, Q):
+    """Algorithmic flops (2 per MAC, causal half): per token and head
+    (Q+1)P for the intra-chunk product and 4NP for chunk state and the
+    state read-out; per token and group (Q+1)N for C.B^T."""
+    return T * (H * ((Q + 1) * P + 4 * N * P) + G * (Q + 1) * N)
+
+
+def replay_step_bytes(ks, Q, H, G, P, N, io=2, dtb=2, with_C=False):
+    """Algorithmic bytes of one replay-decode step for buffer fills ks."""
+    ks = np.asarray(ks, dtype=np.int64)
+    state = H * P * N * 4
+    per_buf_tok = H * P * io + G * N * io + H * dtb          # x, B, raw dt re-read
+    new_tok = H * P * io + H * dtb + 2 * G * N * io          # inputs
+    append = H * P * io + H * dtb + G * N * io * (2 if with_C else 1)
+    y = H * P * io
+    commits = int(np.sum(ks + 1 == Q))
+    return int(len(ks) * (state + new_tok + append + y) + ks.sum() * per_buf_tok
+               + commits * state)
+
+
+def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):
+    return batch * (2 * H * P * N * 4 + 2 * H * P * io + H * dtb + 2 * G * N * io)
+
+
+def load_traffic(sha):
+    """HBM traffic per prefill launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "prefill_w1b_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(x, dt, B, C, hp, Q, T, target_s=10.0):
+    """Time the fp64 oracle on a bounded sample of the prefill workload
+    (whole 2048-token sequences, read back exactly from the device)."""
+    from exact_replay_decode_amd import to_f64
+    from oracle import scan, threads
+
+    def run(n):
+        xs, dts = to_f64(x[:n * T]), to_f64(dt[:n * T])
+        Bs, Cs = to_f64(B[:n * T]), to_f64(C[:n * T])
+        cu = np.arange(n + 1, dtype=np.int64) * T
+        t0 = time.perf_counter()
+        scan(xs, dts, hp.A, Bs, Cs, cu, Q, D=hp.D, dt_bias=hp.dt_bias)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = int(max(1, min(256, round(target_s / max(t1, 1e-3)))))
+    tn = run(n) if n > 1 else t1
+    return {"value": n * T / tn, "unit": "tokens/s", "cores": threads(), "kind": "oracle",
+            "sample": f"{n} of 256 sequences x {T} tokens of the prefill workload "
+                      f"({tn:.1f} s, fp64 sequential recurrence, OpenMP over sequence x head)",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan shards by sequence and head with no "
+              "exchange, so multi-GPU runs are not part of this build (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_replay_decode_amd as erd
+    from exact_replay_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S, T, H, G, P, N, Q = 256, 2048, 32, 1, 64, 128, 256
+    R = args.decode_steps
+    total_decode = R * (args.steps + args.warmup)
+    shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    shape16 = erd.Shape(H, G, P, N, 16, "bf16", "bf16")
+    hp = synth.make_head_params(H, 0)
+    A, D, bias = (torch.from_numpy(v).to(dev) for v in (hp.A, hp.D, hp.dt_bias))
+
+    # ---- prefill workload (resident in HBM) ----
+    x, dt, B, C = synth.make_tokens_torch(S * T, H, G, P, N, 0, dev)
+    cu_host = synth.cu_seqlens([T] * S)
+    cu = torch.from_numpy(cu_host).to(dev)
+    y = torch.empty_like(x)
+    bnd = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    commit_cache = erd.ReplayCache(shape, S, dev)
+
+    # ---- decode workload: prefix 256 + k_i, then R*(K+W) decode tokens ----
+    pre = synth.replay_prefix_lengths(S, Q, 1)
+    px, pdt, pB, pC = synth.make_tokens_torch(int(pre.sum()), H, G, P, N, 1, dev)
+    dx, ddt, dB, dC = synth.make_tokens_torch(total_decode * S, H, G, P, N, 2, dev)
+    dx, ddt = dx.view(total_decode, S, H, P), ddt.view(total_decode, S, H)
+    dB, dC = dB.view(total_decode, S, G, N), dC.view(total_decode, S, G, N)
+    ydec = torch.empty((S, H, P), dtype=torch.bfloat16, device=dev)
+    cu_pre = synth.cu_seqlens(pre)
+    cache256 = erd.ReplayCache(shape, S, dev)
+    cache16 = erd.ReplayCache(shape16, S, dev)
+    erd.ssd_replay_prefill(shape, cache256, cu_pre, px, pdt, pB, pC, A, D, bias)
+    erd.ssd_replay_prefill(shape16, cache16, cu_pre, px, pdt, pB, pC, A, D, bias)
+    _, ssu_state, _ = erd.ssd_prefill_varlen(shape, cu_pre, px, pdt, A, pB, pC, D, bias,
+                                             want_boundary=False)
+    plan256 = erd.DecodePlan(shape, S, A, D, bias, cache=cache256)
+    plan16 = erd.DecodePlan(shape16, S, A, D, bias, cache=cache16)
+    plan_ssu = erd.DecodePlan(shape, S, A, D, bias, state=ssu_state)
+    plan256.check(dx[0], ddt[0], dB[0], dC[0], ydec)
+    ks256 = (pre % Q).astype(np.int64)
+    ks16 = (pre % 16).astype(np.int64)
+
+    # plain copy of known size: calibrates the HBM byte counters
+    calib_src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    bytes_decode256 = bytes_decode16 = 0
+    decode_i = 0
+
+    def step(record):
+        nonlocal decode_i, bytes_decode256, bytes_decode16, ks256, ks16
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
+        if record:
+            ev[0].record(stream)
+        erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
+                               cu_seqlens_host=cu_host, want_final=False)
+        if record:
+            ev[1].record(stream)
+        erd.ssd_commit_boundary(shape, commit_cache, cu, x, dt, B, C, bnd,
+                                cu_seqlens_host=cu_host)
+        if record:
+            ev[2].record(stream)
+        for r in range(R):
+            k = decode_i + r
+            plan256(dx[k], ddt[k], dB[k], dC[k], ydec)
+            if record:
+                bytes_decode256 += replay_step_bytes(ks256, Q, H, G, P, N)
+            ks256 = (ks256 + 1) % Q
+        if record:
+            ev[3].record(stream)
+        for r in range(R):
+            k = decode_i + r
+            plan_ssu(dx[k], ddt[k], dB[k], dC[k], ydec)
+        if record:
+            ev[4].record(stream)
+        for r in range(R):
+            k = decode_i + r
+            plan16(dx[k], ddt[k], dB[k], dC[k], ydec)
+            if record:
+                bytes_decode16 += replay_step_bytes(ks16, 16, H, G, P, N)
+            ks16 = (ks16 + 1) % 16
+        if record:
+            ev[5].record(stream)
+        decode_i += R
+        return ev
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def span(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) / 1e3   # seconds, summed
+
+    K = args.steps
+    t_prefill = span(0, 1)
+    t_commit = span(1, 2)
+    t_dec256 = span(2, 3)
+    t_ssu = span(3, 4)
+    t_dec16 = span(4, 5)
+    t_total = span(0, 5)
+
+    pb = prefill_bytes(S * T, S, H, G, P, N)
+    pf = prefill_flops(S * T, H, G, P, N, Q)
+    prefill_launch_s = t_prefill / K
+    achieved = pb / prefill_launch_s / 1e9
+    sha = kernel_source_sha()
+    traffic = load_traffic(sha)
+    dec_steps = K * R
+    dec256_gbs = bytes_decode256 / t_dec256 / 1e9
+    dec16_gbs = bytes_decode16 / t_dec16 / 1e9
+    ssu_gbs = ssu_step_bytes(S, H, G, P, N) * dec_steps / t_ssu / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": S * T / prefill_launch_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * t_total / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill 256 seqs x 2048 tokens (H=32 G=1 P=64 N=128 chunk 256, "
+                        "bf16 x/dt/B/C/y, fp32 state) + boundary commit + replay decode "
+                        "B=256 (chunk 256 and 16, 0..255 buffered tokens) + recurrent "
+                        "update B=256",
+            "global_batch": S, "seq_len": T, "heads": H, "groups": G, "headdim": P,
+            "dstate": N, "chunk_size": Q, "decode_steps_per_step": R,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "k_scan (prefill)", "algorithmic_bytes_per_launch": pb,
+            "avg_launch_ms": 1e3 * prefill_launch_s,
+            "mfma_util": pf / prefill_launch_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": pf,
+        },
+        "decode": {
+            "replay_q256_steps_per_s": dec_steps / t_dec256,
+            "replay_q256_hbm_gbs": dec256_gbs,
+            "replay_q256_frac": dec256_gbs / HBM_PEAK_GBS,
+            "replay_q16_steps_per_s": dec_steps / t_dec16,
+            "replay_q16_hbm_gbs": dec16_gbs,
+            "replay_q16_frac": dec16_gbs / HBM_PEAK_GBS,
+            "ssu_steps_per_s": dec_steps / t_ssu,
+            "ssu_hbm_gbs": ssu_gbs,
+            "ssu_frac": ssu_gbs / HBM_PEAK_GBS,
+            "batch": S,
+        },
+        "commit_ms": 1e3 * t_commit / K,
+        "wall_s": wall,
+        "kernel_source_sha": sha,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, dt, B, C, hp, Q, T)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,7 @@ The compute lives in libssd_replay.so (hand-written HIP, C ABI in
 include/ssd_replay.h); this package is its torch binding plus the seeded
 synthetic input generator (synth).
 """
-from .api import (Shape, ReplayCache, ssd_prefill_varlen, ssd_commit_boundary,  # noqa: F401
+from .api import (Shape, ReplayCache, DecodePlan, ssd_prefill_varlen, ssd_commit_boundary,  # noqa: F401
                   ssd_replay_prefill, ssd_replay_decode, ssm_state_update,
                   ssd_replay_cache_bytes, to_device, to_f64)
 from ._lib import SsdError, load as load_library  # noqa: F401

@@ -287,3 +287,64 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16 / fp32 tensor."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+class DecodePlan:
+    """Pre-marshalled ssd_replay_decode / ssm_state_update calls for a hot
+    loop: argument checks and ctypes structs are built once; each call only
+    passes the step's token pointers. Inputs per step are contiguous
+    [batch, ...] tensors of the planned shapes."""
+
+    def __init__(self, shape: Shape, batch: int, A, D=None, dt_bias=None, cache=None,
+                 state=None, slot_idx=None, stream=None):
+        if (cache is None) == (state is None):
+            raise ValueError("give exactly one of cache (replay) or state (recurrent)")
+        self.shape, self.batch = shape, batch
+        dev = cache.device if cache is not None else state.device
+        H = shape.H
+        _need(A, "A", (H,), torch.float32, dev)
+        _opt(D, "D", (H,), torch.float32, dev)
+        _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+        self._keep = (A, D, dt_bias, cache, state, slot_idx)
+        self.device = dev
+        self._sh = shape.c()
+        self._lib = _lib.load()
+        self._st = _stream(stream)
+        self._sl = _ptr(_slots(slot_idx, batch, dev))
+        self._A, self._D, self._b = _ptr(A), _ptr(D), _ptr(dt_bias)
+        if cache is not None:
+            if slot_idx is None and batch > cache.num_slots:
+                raise ValueError("batch exceeds cache slots")
+            self._cs = cache.struct()
+            self._state = None
+        else:
+            _need(state, "state", tuple(state.shape), torch.float32, dev)
+            if state.dim() != 4 or tuple(state.shape[1:]) != (H, shape.P, shape.N):
+                raise ValueError("state must be [num_slots, H, P, N]")
+            self._state = state
+            self._ns = int(state.shape[0])
+            if slot_idx is None and batch > self._ns:
+                raise ValueError("batch exceeds state slots")
+
+    def check(self, x, dt, B, C, y):
+        sh, dev, nb = self.shape, self.device, self.batch
+        _need(x, "x", (nb, sh.H, sh.P), sh.io, dev)
+        _need(dt, "dt", (nb, sh.H), sh.dtt, dev)
+        _need(B, "B", (nb, sh.G, sh.N), sh.io, dev)
+        _need(C, "C", (nb, sh.G, sh.N), sh.io, dev)
+        _need(y, "y", (nb, sh.H, sh.P), sh.io, dev)
+
+    def __call__(self, x, dt, B, C, y):
+        """Launch one step; tensors must already satisfy check()."""
+        if self._state is None:
+            rc = self._lib.ssd_replay_decode(
+                ctypes.byref(self._sh), ctypes.byref(self._cs), self.batch, self._sl,
+                x.data_ptr(), dt.data_ptr(), B.data_ptr(), C.data_ptr(), self._A, self._D,
+                self._b, y.data_ptr(), self._st)
+        else:
+            rc = self._lib.ssm_state_update(
+                ctypes.byref(self._sh), self.batch, self._ns, self._sl, self._state.data_ptr(),
+                x.data_ptr(), dt.data_ptr(), self._A, B.data_ptr(), C.data_ptr(), self._D,
+                self._b, y.data_ptr(), self._st)
+        if rc != 0:
+            _lib.check(rc, "DecodePlan")

@@ -76,6 +76,13 @@ int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// One engine per shape, so prefill and decode of a shape always share the
+// same chunk arithmetic.
+hipError_t launch_scan_any(const ssd::ScanArgs &a, hipStream_t stream) {
+    return ssd::mfma_supported(a.d) ? ssd::launch_scan_mfma(a, stream)
+                                    : ssd::launch_scan(a, stream);
+}
+
 size_t dtype_bytes(int dt) { return dt == SSD_BF16 ? 2 : 4; }
 
 }  // namespace
@@ -147,7 +154,7 @@ int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t 
     a.final_state = final_state;
     a.boundary_state = boundary_state;
     a.replay = 0;
-    return hip_status(ssd::launch_scan(a, (hipStream_t)stream));
+    return hip_status(launch_scan_any(a, (hipStream_t)stream));
 }
 
 int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t *cu_host,
@@ -218,7 +225,7 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
     a.cache_state = cache->state;
     a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
     a.buf_len = cache->buf_len;
-    hipError_t e = ssd::launch_scan(a, (hipStream_t)stream);
+    hipError_t e = launch_scan_any(a, (hipStream_t)stream);
     if (e != hipSuccess)
         return SSD_ERR_HIP;
     ssd::CommitArgs c = {};
@@ -268,7 +275,8 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
-    return hip_status(ssd::launch_decode(a, (hipStream_t)stream));
+    return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
+                                             : ssd::launch_decode(a, (hipStream_t)stream));
 }
 
 int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,

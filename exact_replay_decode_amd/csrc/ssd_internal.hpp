@@ -78,9 +78,16 @@ struct SsuArgs {
     void *y;
 };
 
+// fp32-FMA engine (any supported shape; the only engine for fp32 x/B/C)
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
-hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// matrix-core engine (bf16 x/B/C/y, P in {32, 64}, N in {32, 64, 128})
+bool mfma_supported(const Dims &d);
+hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+// shared by both engines
+hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
 
 }  // namespace ssd

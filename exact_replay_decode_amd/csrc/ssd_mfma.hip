@@ -1,0 +1,655 @@
+// ssd_mfma.hip -- the chunked scan and exact-replay decode on gfx950 matrix
+// cores (bf16 inputs, fp32 accumulation, fp32 state).
+//
+// Per chunk of Q tokens (ReplaySSM reproduction page, "Core equations"; the
+// vLLM RFC "Mamba2: exact-replay decode ...", section 3, replays the same
+// chunk arithmetic for decode), for one head with state S (P x N):
+//   G^T[s][t]  = B_s . C_t                                  (MFMA, K = N)
+//   M[t][s]    = bf16( G[t][s] exp(lam_t - lam_s) delta_s ),  s <= t, else 0
+//   Y^T[p][t]  = exp(lam_t) (S_bf . C_t)[p] + (X^T M^T)[p][t] (MFMA, K = N, s)
+//   y[t][p]    = fmaf(D, x[t][p], Y^T[p][t])
+//   S_loc^T[n][p] = sum_s B_s[n] (w_s x_s[p]),  w_s = exp(lam_last - lam_s) delta_s
+//                 (MFMA, K = s; w x split into bf16 hi + lo)
+//   S          = fmaf(exp(lam_last), S, S_loc)              (fp32, registers)
+// S_bf is S rounded to bf16 for the read-out contraction; C.B^T operands are
+// exact bf16; the state path keeps about 16 mantissa bits through the hi/lo
+// split and is never rounded between chunks.
+//
+// Bit identity between prefill and decode: a 32-row block of chunk rows
+// ("t-block") is always computed by tblock_output() with the same MFMA
+// shapes and the same K order; decode calls it for the t-block holding the
+// new token with the rows after it zero-filled. Each output element of an
+// MFMA depends only on its own row and column operands, masked weights are
+// selected to +0 (never multiplied), so the rows after the new token cannot
+// change it. The chunk-end state is computed by chunk_state_update() in both
+// paths.
+//
+// LDS tiles are row-major with 16 bytes of padding per row; operands that
+// contract over tokens are fetched transposed with ds_read_b64_tr_b16.
+#include "ssd_device.hpp"
+#include "ssd_internal.hpp"
+
+namespace ssd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kPad = 8;  // bf16 elements of padding per LDS row
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+    __bf16 b = static_cast<__bf16>(f);  // round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ float bf16_float(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS layout, in bytes, for a chunk of Qp rows (Qp = max(Q, 32)).
+struct MLayout {
+    int XS, BS, SS;                 // row strides in bf16 elements
+    int X, B, S, lam, dlt, el, w, tot, bytes;
+    __host__ __device__ MLayout(int Qp, int P, int N) {
+        XS = P + kPad;
+        BS = N + kPad;
+        SS = N + kPad;
+        int o = 0;
+        X = o;   o += Qp * XS * 2;
+        B = o;   o += Qp * BS * 2;
+        S = o;   o += P * SS * 2;
+        lam = o; o += kMaxQ * 4;
+        dlt = o; o += kMaxQ * 4;
+        el = o;  o += kMaxQ * 4;
+        w = o;   o += kMaxQ * 4;
+        tot = o; o += 32;
+        bytes = o;
+    }
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const char *lds, int byte_off) {
+    return *reinterpret_cast<const bf16x8 *>(lds + byte_off);
+}
+
+// Transposed fetch of an MFMA operand from a row-major bf16 tile: the lane
+// gets rows r0 + 0..3 (read 1) and r1 + 0..3 (read 2) of column c, where
+// r0/r1 are the rows of the lane's k-group and c = c16 + (lane % 16). The
+// 16 lanes of a group supply addresses row (lane%16)/4, columns 4*(lane%4).
+// Returned as raw bf16 bit patterns (elements are read out individually by
+// the state contraction).
+__device__ __forceinline__ i16x8 lds_tr8(const char *lds, int base, int stride, int r0,
+                                         int r1, int c16) {
+    const int l = threadIdx.x & 15;
+    const int rr = l >> 2, cc = c16 + 4 * (l & 3);
+    const lds_char *p = (const lds_char *)lds;
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(p + base + ((r0 + rr) * stride + cc) * 2));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(p + base + ((r1 + rr) * stride + cc) * 2));
+    i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const i16x8 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------------------
+// Output of one 32-row t-block: p-tiles [pt0, pt1) of Y^T for chunk rows
+// t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7] (g = lane/32),
+// zero for rows that are not outputs. acc[pt] receives Y^T[p][t] (without
+// the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
+template <int P, int N>
+__device__ __forceinline__ void tblock_output(int tau, int pt0, int pt1, const bf16x8 *cf,
+                                              const char *lds, const MLayout &L,
+                                              f32x16 *acc) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5, c = lane & 31;
+    const float *lam = reinterpret_cast<const float *>(lds + L.lam);
+    const float *dlt = reinterpret_cast<const float *>(lds + L.dlt);
+    const float *el = reinterpret_cast<const float *>(lds + L.el);
+    const int t = 32 * tau + c;
+
+    // state read-out C . S_bf, K = n in ascending steps of 16
+#pragma unroll
+    for (int pt = 0; pt < P / 32; ++pt) {
+        if (pt < pt0 || pt >= pt1)
+            continue;
+        f32x16 a = {};
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k)
+            a = mfma(lds_b128(lds, L.S + ((32 * pt + c) * L.SS + 16 * k + 8 * g) * 2), cf[k], a);
+        const float e = el[t];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            a[r] = a[r] * e;
+        acc[pt] = a;
+    }
+
+    const float lam_t = lam[t];
+    for (int sg = 0; sg <= tau; ++sg) {
+        f32x16 gt = {};
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k)
+            gt = mfma(lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2), cf[k], gt);
+        // gt[r] = G[t][s], s = 32 sg + 8 (r/4) + 4 g + r % 4
+        uint16_t mb[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int s = 32 * sg + 8 * (r >> 2) + 4 * g + (r & 3);
+            float m = 0.0f;
+            if (s <= t)
+                m = intra_weight(gt[r], lam_t, lam[s], dlt[s]);
+            mb[r] = bf16_bits(m);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            i16x8 bv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                bv[j] = (short)mb[8 * half + j];
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
+            const int r0 = 32 * sg + 16 * half + 4 * ((threadIdx.x & 63) >> 5);
+#pragma unroll
+            for (int pt = 0; pt < P / 32; ++pt) {
+                if (pt < pt0 || pt >= pt1)
+                    continue;
+                const int c16 = 32 * pt + 16 * ((lane >> 4) & 1);
+                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.X, L.XS, r0, r0 + 8, c16));
+                acc[pt] = mfma(aop, bop, acc[pt]);
+            }
+        }
+    }
+}
+
+// Number of chunk-state tiles a wave owns: tiles (pt, nt) of 32 x 32 are
+// dealt round-robin, ti = wave, wave + 4, ...; ti = pt + (P/32) nt.
+template <int P, int N>
+struct StateTiles {
+    static constexpr int total = (P / 32) * (N / 32);
+    static constexpr int per_wave = (total + 3) / 4;
+};
+
+// S (this wave's tiles, accumulator layout S^T[n][p]) <-
+//   fmaf(exp(lam_last), S, sum_s B_s[n] w_s x_s[p]) over the Qp chunk rows in LDS.
+template <int P, int N>
+__device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const char *lds,
+                                                   const MLayout &L,
+                                                   f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5;
+    const float *lam = reinterpret_cast<const float *>(lds + L.lam);
+    const float *w = reinterpret_cast<const float *>(lds + L.w);
+    constexpr int NTW = StateTiles<P, N>::per_wave;
+    constexpr int TOT = StateTiles<P, N>::total;
+    const int pt = wave % (P / 32);
+    f32x16 acc[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+        acc[i] = f32x16{};
+    if (wave < TOT) {
+        for (int k = 0; k < Qp / 16; ++k) {
+            const int r0 = 16 * k + 8 * g;
+            const int c16p = 32 * pt + 16 * ((lane >> 4) & 1);
+            const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16p);
+            i16x8 hv, lv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = bf16_float((uint16_t)xv[j]) * w[r0 + j];
+                const uint16_t hi = bf16_bits(v);
+                hv[j] = (short)hi;
+                lv[j] = (short)bf16_bits(v - bf16_float(hi));
+            }
+            const bf16x8 bhi = __builtin_bit_cast(bf16x8, hv);
+            const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int ti = wave + 4 * i;
+                if (ti >= TOT)
+                    continue;
+                const int nt = ti / (P / 32);
+                const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
+                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
+                acc[i] = mfma(aop, bhi, acc[i]);
+                acc[i] = mfma(aop, blo, acc[i]);
+            }
+        }
+    }
+    const float dec = decay_exp(lam[n_valid - 1]);
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            S[i][r] = fmaf(dec, S[i][r], acc[i][r]);
+}
+
+// State tiles <-> global [P][N] fp32 (one float4 per lane per r-group).
+template <int P, int N, bool LOAD>
+__device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    constexpr int TOT = StateTiles<P, N>::total;
+#pragma unroll
+    for (int i = 0; i < StateTiles<P, N>::per_wave; ++i) {
+        const int ti = wave + 4 * i;
+        if (ti >= TOT)
+            continue;
+        const int pt = ti % (P / 32), nt = ti / (P / 32);
+        const int p = 32 * pt + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 32 * nt + 8 * q + 4 * g;
+            if (LOAD) {
+                const float4 v = gst ? *reinterpret_cast<const float4 *>(gst + (int64_t)p * N + n)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                S[i][4 * q + 0] = v.x;
+                S[i][4 * q + 1] = v.y;
+                S[i][4 * q + 2] = v.z;
+                S[i][4 * q + 3] = v.w;
+            } else {
+                *reinterpret_cast<float4 *>(gst + (int64_t)p * N + n) =
+                    make_float4(S[i][4 * q + 0], S[i][4 * q + 1], S[i][4 * q + 2],
+                                S[i][4 * q + 3]);
+            }
+        }
+    }
+}
+
+// S_bf[p][n] <- bf16(S) from this wave's tiles.
+template <int P, int N>
+__device__ __forceinline__ void state_to_lds(char *lds, const MLayout &L,
+                                             const f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    constexpr int TOT = StateTiles<P, N>::total;
+#pragma unroll
+    for (int i = 0; i < StateTiles<P, N>::per_wave; ++i) {
+        const int ti = wave + 4 * i;
+        if (ti >= TOT)
+            continue;
+        const int pt = ti % (P / 32), nt = ti / (P / 32);
+        const int p = 32 * pt + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 32 * nt + 8 * q + 4 * g;
+            const uint32_t lo = bf16_bits(S[i][4 * q + 0]) | ((uint32_t)bf16_bits(S[i][4 * q + 1]) << 16);
+            const uint32_t hi = bf16_bits(S[i][4 * q + 2]) | ((uint32_t)bf16_bits(S[i][4 * q + 3]) << 16);
+            *reinterpret_cast<uint2 *>(lds + L.S + (p * L.SS + n) * 2) = make_uint2(lo, hi);
+        }
+    }
+}
+
+// Chunk positions: [0, nb) from the slot buffer, [nb, n_valid) from the
+// packed input starting at token tok_base; later rows are zero.
+template <class DT>
+struct MView {
+    using TD = typename DT::T;
+    const uint16_t *x, *B, *C;
+    const TD *dt;
+    const uint16_t *bx, *bB;
+    const TD *bdt;
+    int64_t tok_base;
+    int nb, n_valid;
+    int h, g, H, G;
+    __device__ int64_t token(int j) const { return tok_base + (j - nb); }
+};
+
+// Stage X and B rows [0, rows) of the chunk into LDS (zeros past n_valid),
+// and delta / lam / exp(lam) / state weights.
+template <int P, int N, class DT>
+__device__ void stage_chunk(const MView<DT> &v, int rows, float A_h, float bias, int softplus,
+                            bool weights, char *lds, const MLayout &L) {
+    const int tid = threadIdx.x;
+    constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
+    for (int e = tid; e < rows * XC; e += kBlock) {
+        const int j = e / XC, q = e % XC;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (j < v.n_valid) {
+            const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
+                                           : v.x + (v.token(j) * v.H + v.h) * P;
+            val = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+        *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) = val;
+    }
+    for (int e = tid; e < rows * BC; e += kBlock) {
+        const int j = e / BC, q = e % BC;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (j < v.n_valid) {
+            const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
+                                           : v.B + (v.token(j) * v.G + v.g) * N;
+            val = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+        *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) = val;
+    }
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *dlt = reinterpret_cast<float *>(lds + L.dlt);
+    float *el = reinterpret_cast<float *>(lds + L.el);
+    float *w = reinterpret_cast<float *>(lds + L.w);
+    const int j = tid;
+    float d = 0.0f, a = 0.0f;
+    if (j < v.n_valid) {
+        const float raw = j < v.nb ? DT::ld(v.bdt, (int64_t)j * v.H + v.h)
+                                   : DT::ld(v.dt, v.token(j) * v.H + v.h);
+        d = delta_of(raw, bias, softplus);
+        a = d * A_h;
+    }
+    const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
+    lam[j] = l;
+    dlt[j] = d;
+    el[j] = decay_exp(l);
+    __syncthreads();
+    if (weights)
+        w[j] = state_weight(lam[v.n_valid - 1], l, d);
+}
+
+// C fragments of t-block tau: lane gets C[t][16k + 8g .. +7] for rows t that
+// produce output (t in [row_lo, n_valid)), zeros otherwise.
+template <int N, class DT>
+__device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_lo,
+                                           bf16x8 (&cf)[N / 16]) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5, t = 32 * tau + (lane & 31);
+    const bool ok = t >= row_lo && t < v.n_valid && t >= v.nb;
+    const uint16_t *src = ok ? v.C + (v.token(t) * v.G + v.g) * N : nullptr;
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k) {
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (ok)
+            val = *reinterpret_cast<const uint4 *>(src + 16 * k + 8 * g);
+        cf[k] = __builtin_bit_cast(bf16x8, val);
+    }
+}
+
+// y rows [row_lo, row_hi) of t-block tau: y = fmaf(D, x, acc), -0 -> +0.
+template <int P, class V>
+__device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int row_hi, int pt0,
+                                            int pt1, float D_h, const char *lds,
+                                            const MLayout &L, const f32x16 *acc, uint16_t *y) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5, c = lane & 31;
+    const int t = 32 * tau + c;
+    if (t < row_lo || t >= row_hi)
+        return;
+    uint16_t *yrow = y + (v.token(t) * v.H + v.h) * P;
+#pragma unroll
+    for (int pt = 0; pt < P / 32; ++pt) {
+        if (pt < pt0 || pt >= pt1)
+            continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int p = 32 * pt + 8 * q + 4 * g;
+            const uint2 xr = *reinterpret_cast<const uint2 *>(lds + L.X + (t * L.XS + p) * 2);
+            const float xs[4] = {bf16_float(xr.x & 0xffff), bf16_float(xr.x >> 16),
+                                 bf16_float(xr.y & 0xffff), bf16_float(xr.y >> 16)};
+            uint16_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float yv = fmaf(D_h, xs[e], acc[pt][4 * q + e]);
+                yv = yv + 0.0f;  // -0 -> +0
+                o[e] = bf16_bits(yv);
+            }
+            *reinterpret_cast<uint2 *>(yrow + p) =
+                make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+        }
+    }
+}
+
+// t-blocks of a chunk handled by a wave in prefill: with 8 t-blocks, wave w
+// takes w and 7 - w (equal causal work); otherwise t-block w.
+__device__ __forceinline__ int wave_tblocks(int nT, int wave, int *out) {
+    if (nT == 8) {
+        out[0] = wave;
+        out[1] = 7 - wave;
+        return 2;
+    }
+    out[0] = wave;
+    return wave < nT ? 1 : 0;
+}
+
+template <int P, int N, class DT>
+__global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    const int g = h / (H / G);
+    const int wave = threadIdx.x >> 6;
+    constexpr int PN = P * N;
+    const MLayout L(Qp, P, N);
+
+    const int64_t t0 = a.cu[s];
+    const int len = a.cu[s + 1] - a.cu[s];
+    const int slot = a.replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
+    if (a.replay && (len == 0 || slot < 0 || slot >= a.num_slots))
+        return;
+    const int nbuf = a.replay ? a.buf_len[slot] : 0;
+    if (nbuf < 0 || nbuf >= Q)
+        return;
+
+    float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+                           : (a.init_state ? const_cast<float *>(a.init_state) +
+                                                 ((int64_t)s * H + h) * PN
+                                           : nullptr);
+    f32x16 S[StateTiles<P, N>::per_wave];
+    state_io<P, N, true>(init, S);
+    state_to_lds<P, N>(lds, L, S);
+
+    MView<DT> v;
+    v.x = static_cast<const uint16_t *>(a.x);
+    v.B = static_cast<const uint16_t *>(a.B);
+    v.C = static_cast<const uint16_t *>(a.C);
+    v.dt = static_cast<const TD *>(a.dt);
+    v.bx = a.replay ? static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P : nullptr;
+    v.bB = a.replay ? static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N : nullptr;
+    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H : nullptr;
+    v.h = h; v.g = g; v.H = H; v.G = G;
+
+    const float A_h = a.A[h];
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const int total = nbuf + len;
+    const int nchunks = (total + Q - 1) / Q;
+    const int nfull = total / Q;
+    float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+                          : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
+                                              : nullptr);
+    const bool write_bnd = bnd && (!a.replay || nfull > 0);
+    uint16_t *y = static_cast<uint16_t *>(a.y);
+    const int nT = Qp / 32;
+
+    for (int c = 0; c < nchunks; ++c) {
+        if (c == nfull && write_bnd)
+            state_io<P, N, false>(bnd, S);
+        v.nb = (c == 0) ? nbuf : 0;
+        v.n_valid = min(Q, total - c * Q);
+        v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
+        const bool upd = v.n_valid == Q || (!a.replay && a.final_state);
+        __syncthreads();  // previous chunk's LDS reads are done
+        stage_chunk<P, N, DT>(v, Qp, A_h, bias, d.softplus, upd, lds, L);
+        int tb[2];
+        const int ntb = wave_tblocks(nT, wave, tb);
+        __syncthreads();
+        for (int i = 0; i < ntb; ++i) {
+            const int tau = tb[i];
+            const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, v.n_valid);
+            if (lo >= hi)
+                continue;
+            bf16x8 cf[N / 16];
+            load_cfrag<N, DT>(v, tau, lo, cf);
+            f32x16 acc[P / 32];
+            tblock_output<P, N>(tau, 0, P / 32, cf, lds, L, acc);
+            emit_tblock<P>(v, tau, lo, hi, 0, P / 32, D_h, lds, L, acc, y);
+        }
+        if (upd) {
+            chunk_state_update<P, N>(Qp, v.n_valid, lds, L, S);
+            __syncthreads();  // all waves are done reading S_bf
+            state_to_lds<P, N>(lds, L, S);
+        }
+    }
+    if (nfull == nchunks && write_bnd)
+        state_io<P, N, false>(bnd, S);
+    if (!a.replay && a.final_state)
+        state_io<P, N, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
+}
+
+template <int P, int N, class DT>
+__global__ __launch_bounds__(kBlock) void k_decode_mfma(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int hpg = H / G, g = h / hpg;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    constexpr int PN = P * N;
+    const MLayout L(Qp, P, N);
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0 || slot >= a.num_slots)
+        return;
+    const int k = a.buf_len[slot];
+    if (k < 0 || k >= Q)
+        return;
+    const bool commit = k + 1 == Q;
+    float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
+
+    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+
+    MView<DT> v;
+    v.x = static_cast<const uint16_t *>(a.x);
+    v.B = static_cast<const uint16_t *>(a.B);
+    v.C = static_cast<const uint16_t *>(a.C);
+    v.dt = static_cast<const TD *>(a.dt);
+    v.bx = bx; v.bB = bB; v.bdt = bdt;
+    v.h = h; v.g = g; v.H = H; v.G = G;
+    v.tok_base = b;
+    v.nb = k;
+    v.n_valid = k + 1;
+
+    const int tau = k >> 5;
+    const int rows = commit ? Qp : 32 * (tau + 1);
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    // S_bf from the fp32 boundary state
+    for (int e = tid; e < PN / 4; e += kBlock) {
+        const int p = (4 * e) / N, n = (4 * e) % N;
+        const float4 sv = reinterpret_cast<const float4 *>(st)[e];
+        const uint32_t lo = bf16_bits(sv.x) | ((uint32_t)bf16_bits(sv.y) << 16);
+        const uint32_t hi = bf16_bits(sv.z) | ((uint32_t)bf16_bits(sv.w) << 16);
+        *reinterpret_cast<uint2 *>(lds + L.S + (p * L.SS + n) * 2) = make_uint2(lo, hi);
+    }
+    stage_chunk<P, N, DT>(v, rows, a.A[h], bias, d.softplus, commit, lds, L);
+    __syncthreads();
+
+    if (wave < P / 32) {
+        bf16x8 cf[N / 16];
+        load_cfrag<N, DT>(v, tau, k, cf);
+        f32x16 acc[P / 32];
+        tblock_output<P, N>(tau, wave, wave + 1, cf, lds, L, acc);
+        emit_tblock<P>(v, tau, k, k + 1, wave, wave + 1, a.D ? a.D[h] : 0.0f, lds, L, acc,
+                       static_cast<uint16_t *>(a.y));
+    }
+
+    // append the new token at buffer position k (reads above used LDS or
+    // positions < k of the buffer)
+    const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
+    for (int p = tid; p < P; p += kBlock)
+        bx[((int64_t)k * H + h) * P + p] = xin[p];
+    if (tid == 0)
+        bdt[(int64_t)k * H + h] = static_cast<const TD *>(a.dt)[(int64_t)b * H + h];
+    if (h % hpg == 0) {
+        const uint16_t *bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
+        for (int n = tid; n < N; n += kBlock)
+            bB[((int64_t)k * G + g) * N + n] = bin[n];
+        if (a.buf_C) {
+            uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
+            const uint16_t *cin = static_cast<const uint16_t *>(a.C) + ((int64_t)b * G + g) * N;
+            for (int n = tid; n < N; n += kBlock)
+                bC[((int64_t)k * G + g) * N + n] = cin[n];
+        }
+    }
+    if (commit) {
+        f32x16 S[StateTiles<P, N>::per_wave];
+        state_io<P, N, true>(st, S);
+        chunk_state_update<P, N>(Qp, Q, lds, L, S);
+        __syncthreads();  // every wave has read the old state
+        state_io<P, N, false>(st, S);
+    }
+}
+
+template <class K>
+hipError_t set_lds(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int P, int N, class DT>
+hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
+    const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
+    const MLayout L(Qp, P, N);
+    hipError_t e = set_lds(k_scan_mfma<P, N, DT>, L.bytes);
+    if (e != hipSuccess)
+        return e;
+    k_scan_mfma<P, N, DT><<<dim3(a.d.H * a.S), dim3(kBlock), L.bytes, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N, class DT>
+hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+    const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
+    const MLayout L(Qp, P, N);
+    hipError_t e = set_lds(k_decode_mfma<P, N, DT>, L.bytes);
+    if (e != hipSuccess)
+        return e;
+    k_decode_mfma<P, N, DT><<<dim3(a.d.H * a.batch), dim3(kBlock), L.bytes, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+hipError_t scan_pn(const ScanArgs &a, hipStream_t s) {
+    return a.d.dt_bf16 ? scan_mfma<P, N, IoBF16>(a, s) : scan_mfma<P, N, IoF32>(a, s);
+}
+template <int P, int N>
+hipError_t decode_pn(const DecodeArgs &a, hipStream_t s) {
+    return a.d.dt_bf16 ? decode_mfma<P, N, IoBF16>(a, s) : decode_mfma<P, N, IoF32>(a, s);
+}
+
+#define SSD_PN_SWITCH(FN, A, S)                                   \
+    switch (A.d.P * 1000 + A.d.N) {                               \
+    case 32032: return FN<32, 32>(A, S);                          \
+    case 32064: return FN<32, 64>(A, S);                          \
+    case 32128: return FN<32, 128>(A, S);                         \
+    case 64032: return FN<64, 32>(A, S);                          \
+    case 64064: return FN<64, 64>(A, S);                          \
+    case 64128: return FN<64, 128>(A, S);                         \
+    default: return hipErrorInvalidValue;                         \
+    }
+
+}  // namespace
+
+bool mfma_supported(const Dims &d) {
+    return d.io_bf16 && (d.P == 32 || d.P == 64) && (d.N == 32 || d.N == 64 || d.N == 128);
+}
+
+hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream) { SSD_PN_SWITCH(scan_pn, a, stream) }
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+    hipError_t e;
+    {
+        auto run = [&]() -> hipError_t { SSD_PN_SWITCH(decode_pn, a, stream) };
+        e = run();
+    }
+    if (e != hipSuccess)
+        return e;
+    return launch_decode_advance(a, stream);
+}
+
+}  // namespace ssd

@@ -545,9 +545,7 @@ hipError_t decode_impl(const DecodeArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_decode_advance, dim3((a.batch + 255) / 256), dim3(256), 0, stream,
-                       a.batch, a.slot_idx, a.buf_len, a.boundary_pos, a.d.Q, a.num_slots);
-    return hipGetLastError();
+    return launch_decode_advance(a, stream);
 }
 
 template <class IO, class DT>
@@ -577,6 +575,11 @@ template <class IO, class DT> struct SsuF { static hipError_t run(const SsuArgs 
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) { return dispatch<ScanF>(a, stream); }
+hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream) {
+    k_decode_advance<<<dim3((a.batch + 255) / 256), dim3(256), 0, stream>>>(
+        a.batch, a.slot_idx, a.buf_len, a.boundary_pos, a.d.Q, a.num_slots);
+    return hipGetLastError();
+}
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return dispatch<DecodeF>(a, stream); }
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream) { return dispatch<CommitF>(a, stream); }
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream) { return dispatch<SsuF>(a, stream); }
