@@ -6,6 +6,8 @@
 // chunk arithmetic for decode), for one head with state S (P x N):
 //   G^T[s][t]  = B_s . C_t                                  (MFMA, K = N)
 //   M[t][s]    = bf16( G[t][s] exp(lam_t - lam_s) delta_s ),  s <= t, else 0
+//                evaluated as G 2^(l_t - u_s), l = lam log2(e) and
+//                u_s = l_s - log2(delta_s), both precomputed per token
 //   Y^T[p][t]  = exp(lam_t) (S_bf . C_t)[p] + (X^T M^T)[p][t] (MFMA, K = N, s)
 //   y[t][p]    = fmaf(D, x[t][p], Y^T[p][t])
 //   S_loc^T[n][p] = sum_s B_s[n] (w_s x_s[p]),  w_s = exp(lam_last - lam_s) delta_s
@@ -48,6 +50,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 __device__ __forceinline__ float bf16_float(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
+__device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float flog2(float v) { return __builtin_amdgcn_logf(v); }
+
+// two floats -> packed bf16 pair (round to nearest even), low half = a
+__device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -56,7 +68,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 // LDS layout, in bytes, for a chunk of Qp rows (Qp = max(Q, 32)).
 struct MLayout {
     int XS, BS, SS;                 // row strides in bf16 elements
-    int X, B, S, lam, dlt, el, w, tot, bytes;
+    int X, B, S, lam, u, el, w, tot, bytes;
     __host__ __device__ MLayout(int Qp, int P, int N) {
         XS = P + kPad;
         BS = N + kPad;
@@ -65,8 +77,8 @@ struct MLayout {
         X = o;   o += Qp * XS * 2;
         B = o;   o += Qp * BS * 2;
         S = o;   o += P * SS * 2;
-        lam = o; o += kMaxQ * 4;
-        dlt = o; o += kMaxQ * 4;
+        lam = o; o += kMaxQ * 4;   // in-chunk cumulative sum, log2 units
+        u = o;   o += kMaxQ * 4;   // lam - log2(delta)
         el = o;  o += kMaxQ * 4;
         w = o;   o += kMaxQ * 4;
         tot = o; o += 32;
@@ -104,22 +116,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const i16x8 &v) { return __builtin_b
 // t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7] (g = lane/32),
 // zero for rows that are not outputs. acc[pt] receives Y^T[p][t] (without
 // the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
-template <int P, int N>
-__device__ __forceinline__ void tblock_output(int tau, int pt0, int pt1, const bf16x8 *cf,
-                                              const char *lds, const MLayout &L,
-                                              f32x16 *acc) {
+template <int P, int N, int PT0, int PT1>
+__device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const char *lds,
+                                              const MLayout &L, f32x16 *acc) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, c = lane & 31;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
-    const float *dlt = reinterpret_cast<const float *>(lds + L.dlt);
+    const float *uu = reinterpret_cast<const float *>(lds + L.u);
     const float *el = reinterpret_cast<const float *>(lds + L.el);
     const int t = 32 * tau + c;
 
     // state read-out C . S_bf, K = n in ascending steps of 16
 #pragma unroll
-    for (int pt = 0; pt < P / 32; ++pt) {
-        if (pt < pt0 || pt >= pt1)
-            continue;
+    for (int pt = PT0; pt < PT1; ++pt) {
         f32x16 a = {};
 #pragma unroll
         for (int k = 0; k < N / 16; ++k)
@@ -137,28 +146,33 @@ __device__ __forceinline__ void tblock_output(int tau, int pt0, int pt1, const b
 #pragma unroll
         for (int k = 0; k < N / 16; ++k)
             gt = mfma(lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2), cf[k], gt);
-        // gt[r] = G[t][s], s = 32 sg + 8 (r/4) + 4 g + r % 4
-        uint16_t mb[16];
+        // gt[r] = G[t][s], s = 32 sg + 8 (r/4) + 4 g + r % 4. On the diagonal
+        // block the weights with s > t are selected to +0.
+        const bool diag = sg == tau;
+        uint32_t mb[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int s = 32 * sg + 8 * (r >> 2) + 4 * g + (r & 3);
-            float m = 0.0f;
-            if (s <= t)
-                m = intra_weight(gt[r], lam_t, lam[s], dlt[s]);
-            mb[r] = bf16_bits(m);
+        for (int q = 0; q < 4; ++q) {
+            const int s0 = 32 * sg + 8 * q + 4 * g;
+            const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
+            const float us[4] = {u4.x, u4.y, u4.z, u4.w};
+            float m[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m[e] = gt[4 * q + e] * fexp2(lam_t - us[e]);
+                if (diag)
+                    m[e] = (s0 + e <= t) ? m[e] : 0.0f;
+            }
+            mb[2 * q] = bf16_pack(m[0], m[1]);
+            mb[2 * q + 1] = bf16_pack(m[2], m[3]);
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            i16x8 bv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                bv[j] = (short)mb[8 * half + j];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 bv = {mb[4 * half], mb[4 * half + 1], mb[4 * half + 2], mb[4 * half + 3]};
             const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
-            const int r0 = 32 * sg + 16 * half + 4 * ((threadIdx.x & 63) >> 5);
+            const int r0 = 32 * sg + 16 * half + 4 * g;
 #pragma unroll
-            for (int pt = 0; pt < P / 32; ++pt) {
-                if (pt < pt0 || pt >= pt1)
-                    continue;
+            for (int pt = PT0; pt < PT1; ++pt) {
                 const int c16 = 32 * pt + 16 * ((lane >> 4) & 1);
                 const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.X, L.XS, r0, r0 + 8, c16));
                 acc[pt] = mfma(aop, bop, acc[pt]);
@@ -197,20 +211,29 @@ __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const ch
             const int r0 = 16 * k + 8 * g;
             const int c16p = 32 * pt + 16 * ((lane >> 4) & 1);
             const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16p);
-            i16x8 hv, lv;
+            const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
+            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            float v[8], lo[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float v = bf16_float((uint16_t)xv[j]) * w[r0 + j];
-                const uint16_t hi = bf16_bits(v);
-                hv[j] = (short)hi;
-                lv[j] = (short)bf16_bits(v - bf16_float(hi));
+            for (int j = 0; j < 8; ++j)
+                v[j] = bf16_float((uint16_t)xv[j]) * ws[j];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            u32x4 hv, lv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t h2 = bf16_pack(v[2 * j], v[2 * j + 1]);
+                hv[j] = h2;
+                lo[2 * j] = v[2 * j] - bf16_float(h2 & 0xffff);
+                lo[2 * j + 1] = v[2 * j + 1] - bf16_float(h2 >> 16);
+                lv[j] = bf16_pack(lo[2 * j], lo[2 * j + 1]);
             }
             const bf16x8 bhi = __builtin_bit_cast(bf16x8, hv);
             const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
                 const int ti = wave + 4 * i;
-                if (ti >= TOT)
+                if (TOT % 4 != 0 && ti >= TOT)
                     continue;
                 const int nt = ti / (P / 32);
                 const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
@@ -220,7 +243,7 @@ __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const ch
             }
         }
     }
-    const float dec = decay_exp(lam[n_valid - 1]);
+    const float dec = fexp2(lam[n_valid - 1]);
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
@@ -301,8 +324,9 @@ struct MView {
 
 // Stage X and B rows [0, rows) of the chunk into LDS (zeros past n_valid),
 // and delta / lam / exp(lam) / state weights.
+// A2_h = A[h] log2(e): the cumulative sums are kept in log2 units.
 template <int P, int N, class DT>
-__device__ void stage_chunk(const MView<DT> &v, int rows, float A_h, float bias, int softplus,
+__device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias, int softplus,
                             bool weights, char *lds, const MLayout &L) {
     const int tid = threadIdx.x;
     constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
@@ -327,7 +351,7 @@ __device__ void stage_chunk(const MView<DT> &v, int rows, float A_h, float bias,
         *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) = val;
     }
     float *lam = reinterpret_cast<float *>(lds + L.lam);
-    float *dlt = reinterpret_cast<float *>(lds + L.dlt);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
     float *el = reinterpret_cast<float *>(lds + L.el);
     float *w = reinterpret_cast<float *>(lds + L.w);
     const int j = tid;
@@ -336,15 +360,15 @@ __device__ void stage_chunk(const MView<DT> &v, int rows, float A_h, float bias,
         const float raw = j < v.nb ? DT::ld(v.bdt, (int64_t)j * v.H + v.h)
                                    : DT::ld(v.dt, v.token(j) * v.H + v.h);
         d = delta_of(raw, bias, softplus);
-        a = d * A_h;
+        a = d * A2_h;
     }
     const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
     lam[j] = l;
-    dlt[j] = d;
-    el[j] = decay_exp(l);
+    uu[j] = l - flog2(d);   // +inf where delta is 0: its weights are exactly 0
+    el[j] = fexp2(l);
     __syncthreads();
     if (weights)
-        w[j] = state_weight(lam[v.n_valid - 1], l, d);
+        w[j] = fexp2(lam[v.n_valid - 1] - l) * d;
 }
 
 // C fragments of t-block tau: lane gets C[t][16k + 8g .. +7] for rows t that
@@ -366,10 +390,10 @@ __device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_
 }
 
 // y rows [row_lo, row_hi) of t-block tau: y = fmaf(D, x, acc), -0 -> +0.
-template <int P, class V>
-__device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int row_hi, int pt0,
-                                            int pt1, float D_h, const char *lds,
-                                            const MLayout &L, const f32x16 *acc, uint16_t *y) {
+template <int P, int PT0, int PT1, class V>
+__device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int row_hi,
+                                            float D_h, const char *lds, const MLayout &L,
+                                            const f32x16 *acc, uint16_t *y) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, c = lane & 31;
     const int t = 32 * tau + c;
@@ -377,9 +401,7 @@ __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int
         return;
     uint16_t *yrow = y + (v.token(t) * v.H + v.h) * P;
 #pragma unroll
-    for (int pt = 0; pt < P / 32; ++pt) {
-        if (pt < pt0 || pt >= pt1)
-            continue;
+    for (int pt = PT0; pt < PT1; ++pt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int p = 32 * pt + 8 * q + 4 * g;
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
     v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H : nullptr;
     v.h = h; v.g = g; v.H = H; v.G = G;
 
-    const float A_h = a.A[h];
+    const float A2_h = a.A[h] * kLog2e;
     const float D_h = a.D ? a.D[h] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const int total = nbuf + len;
@@ -472,7 +494,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
         const bool upd = v.n_valid == Q || (!a.replay && a.final_state);
         __syncthreads();  // previous chunk's LDS reads are done
-        stage_chunk<P, N, DT>(v, Qp, A_h, bias, d.softplus, upd, lds, L);
+        stage_chunk<P, N, DT>(v, Qp, A2_h, bias, d.softplus, upd, lds, L);
         int tb[2];
         const int ntb = wave_tblocks(nT, wave, tb);
         __syncthreads();
@@ -484,8 +506,8 @@ __global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
             bf16x8 cf[N / 16];
             load_cfrag<N, DT>(v, tau, lo, cf);
             f32x16 acc[P / 32];
-            tblock_output<P, N>(tau, 0, P / 32, cf, lds, L, acc);
-            emit_tblock<P>(v, tau, lo, hi, 0, P / 32, D_h, lds, L, acc, y);
+            tblock_output<P, N, 0, P / 32>(tau, cf, lds, L, acc);
+            emit_tblock<P, 0, P / 32>(v, tau, lo, hi, D_h, lds, L, acc, y);
         }
         if (upd) {
             chunk_state_update<P, N>(Qp, v.n_valid, lds, L, S);
@@ -546,16 +568,24 @@ __global__ __launch_bounds__(kBlock) void k_decode_mfma(DecodeArgs a) {
         const uint32_t hi = bf16_bits(sv.z) | ((uint32_t)bf16_bits(sv.w) << 16);
         *reinterpret_cast<uint2 *>(lds + L.S + (p * L.SS + n) * 2) = make_uint2(lo, hi);
     }
-    stage_chunk<P, N, DT>(v, rows, a.A[h], bias, d.softplus, commit, lds, L);
+    stage_chunk<P, N, DT>(v, rows, a.A[h] * kLog2e, bias, d.softplus, commit, lds, L);
     __syncthreads();
 
+    // one wave per 32-column p-tile of the output row
     if (wave < P / 32) {
         bf16x8 cf[N / 16];
         load_cfrag<N, DT>(v, tau, k, cf);
         f32x16 acc[P / 32];
-        tblock_output<P, N>(tau, wave, wave + 1, cf, lds, L, acc);
-        emit_tblock<P>(v, tau, k, k + 1, wave, wave + 1, a.D ? a.D[h] : 0.0f, lds, L, acc,
-                       static_cast<uint16_t *>(a.y));
+        const float D_h = a.D ? a.D[h] : 0.0f;
+        uint16_t *y = static_cast<uint16_t *>(a.y);
+        if (wave == 0) {
+            tblock_output<P, N, 0, 1>(tau, cf, lds, L, acc);
+            emit_tblock<P, 0, 1>(v, tau, k, k + 1, D_h, lds, L, acc, y);
+        } else if (P / 32 > 1 && wave == 1) {
+            tblock_output<P, N, (P / 32 > 1 ? 1 : 0), (P / 32 > 1 ? 2 : 1)>(tau, cf, lds, L, acc);
+            emit_tblock<P, (P / 32 > 1 ? 1 : 0), (P / 32 > 1 ? 2 : 1)>(v, tau, k, k + 1, D_h, lds,
+                                                                          L, acc, y);
+        }
     }
 
     // append the new token at buffer position k (reads above used LDS or
