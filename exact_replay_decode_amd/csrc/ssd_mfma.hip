@@ -81,7 +81,7 @@ struct MLayout {
         u = o;   o += kMaxQ * 4;   // lam - log2(delta)
         el = o;  o += kMaxQ * 4;
         w = o;   o += kMaxQ * 4;
-        tot = o; o += 32;
+        tot = o; o += 64;     // one float per wave
         bytes = o;
     }
 };
@@ -181,26 +181,27 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     }
 }
 
-// Number of chunk-state tiles a wave owns: tiles (pt, nt) of 32 x 32 are
-// dealt round-robin, ti = wave, wave + 4, ...; ti = pt + (P/32) nt.
-template <int P, int N>
+// Chunk-state tiles (pt, nt) of 32 x 32 are dealt round-robin over the NW
+// waves of the workgroup, ti = wave, wave + NW, ...; ti = pt + (P/32) nt.
+// Which wave computes a tile does not change its arithmetic.
+template <int P, int N, int NW>
 struct StateTiles {
     static constexpr int total = (P / 32) * (N / 32);
-    static constexpr int per_wave = (total + 3) / 4;
+    static constexpr int per_wave = (total + NW - 1) / NW;
 };
 
 // S (this wave's tiles, accumulator layout S^T[n][p]) <-
 //   fmaf(exp(lam_last), S, sum_s B_s[n] w_s x_s[p]) over the Qp chunk rows in LDS.
-template <int P, int N>
+template <int P, int N, int NW>
 __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const char *lds,
                                                    const MLayout &L,
-                                                   f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+                                                   f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
     const float *w = reinterpret_cast<const float *>(lds + L.w);
-    constexpr int NTW = StateTiles<P, N>::per_wave;
-    constexpr int TOT = StateTiles<P, N>::total;
+    constexpr int NTW = StateTiles<P, N, NW>::per_wave;
+    constexpr int TOT = StateTiles<P, N, NW>::total;
     const int pt = wave % (P / 32);
     f32x16 acc[NTW];
 #pragma unroll
@@ -232,8 +233,8 @@ __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const ch
             const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
-                const int ti = wave + 4 * i;
-                if (TOT % 4 != 0 && ti >= TOT)
+                const int ti = wave + NW * i;
+                if (TOT % NW != 0 && ti >= TOT)
                     continue;
                 const int nt = ti / (P / 32);
                 const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
@@ -252,14 +253,14 @@ __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const ch
 }
 
 // State tiles <-> global [P][N] fp32 (one float4 per lane per r-group).
-template <int P, int N, bool LOAD>
-__device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+template <int P, int N, int NW, bool LOAD>
+__device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
-    constexpr int TOT = StateTiles<P, N>::total;
+    constexpr int TOT = StateTiles<P, N, NW>::total;
 #pragma unroll
-    for (int i = 0; i < StateTiles<P, N>::per_wave; ++i) {
-        const int ti = wave + 4 * i;
+    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
+        const int ti = wave + NW * i;
         if (ti >= TOT)
             continue;
         const int pt = ti % (P / 32), nt = ti / (P / 32);
@@ -284,15 +285,15 @@ __device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N
 }
 
 // S_bf[p][n] <- bf16(S) from this wave's tiles.
-template <int P, int N>
+template <int P, int N, int NW>
 __device__ __forceinline__ void state_to_lds(char *lds, const MLayout &L,
-                                             const f32x16 (&S)[StateTiles<P, N>::per_wave]) {
+                                             const f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
-    constexpr int TOT = StateTiles<P, N>::total;
+    constexpr int TOT = StateTiles<P, N, NW>::total;
 #pragma unroll
-    for (int i = 0; i < StateTiles<P, N>::per_wave; ++i) {
-        const int ti = wave + 4 * i;
+    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
+        const int ti = wave + NW * i;
         if (ti >= TOT)
             continue;
         const int pt = ti % (P / 32), nt = ti / (P / 32);
@@ -328,9 +329,9 @@ struct MView {
 template <int P, int N, class DT>
 __device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias, int softplus,
                             bool weights, char *lds, const MLayout &L) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nthr = blockDim.x;
     constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
-    for (int e = tid; e < rows * XC; e += kBlock) {
+    for (int e = tid; e < rows * XC; e += nthr) {
         const int j = e / XC, q = e % XC;
         uint4 val = make_uint4(0, 0, 0, 0);
         if (j < v.n_valid) {
@@ -340,7 +341,7 @@ __device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias
         }
         *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) = val;
     }
-    for (int e = tid; e < rows * BC; e += kBlock) {
+    for (int e = tid; e < rows * BC; e += nthr) {
         const int j = e / BC, q = e % BC;
         uint4 val = make_uint4(0, 0, 0, 0);
         if (j < v.n_valid) {
@@ -362,13 +363,101 @@ __device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias
         d = delta_of(raw, bias, softplus);
         a = d * A2_h;
     }
+    // threads past the chunk (j >= kMaxQ) scan zeros and store nothing
     const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
-    lam[j] = l;
-    uu[j] = l - flog2(d);   // +inf where delta is 0: its weights are exactly 0
-    el[j] = fexp2(l);
+    if (j < kMaxQ) {
+        lam[j] = l;
+        uu[j] = l - flog2(d);   // +inf where delta is 0: its weights are exactly 0
+        el[j] = fexp2(l);
+    }
     __syncthreads();
-    if (weights)
+    if (weights && j < kMaxQ)
         w[j] = fexp2(lam[v.n_valid - 1] - l) * d;
+}
+
+// Register-staged copy of a chunk's X / B rows and raw dt, loaded one chunk
+// ahead by the prefill workgroup (NT threads) so the global-load latency
+// overlaps the previous chunk's matrix work.
+template <int P, int N, int NT>
+struct ChunkRegs {
+    static constexpr int XC = P / 8, BC = N / 8;
+    static constexpr int XPT = (kMaxQ * XC + NT - 1) / NT;
+    static constexpr int BPT = (kMaxQ * BC + NT - 1) / NT;
+    uint4 x[XPT], b[BPT];
+    float dt;
+};
+
+template <int P, int N, int NT, class DT>
+__device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
+                                                ChunkRegs<P, N, NT> &r) {
+    using CR = ChunkRegs<P, N, NT>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CR::XPT; ++i) {
+        const int e = tid + NT * i, j = e / CR::XC, q = e % CR::XC;
+        r.x[i] = make_uint4(0, 0, 0, 0);
+        if (e < rows * CR::XC && j < v.n_valid) {
+            const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
+                                           : v.x + (v.token(j) * v.H + v.h) * P;
+            r.x[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CR::BPT; ++i) {
+        const int e = tid + NT * i, j = e / CR::BC, q = e % CR::BC;
+        r.b[i] = make_uint4(0, 0, 0, 0);
+        if (e < rows * CR::BC && j < v.n_valid) {
+            const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
+                                           : v.B + (v.token(j) * v.G + v.g) * N;
+            r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+    }
+    r.dt = 0.0f;
+    if (tid < v.n_valid)
+        r.dt = tid < v.nb ? DT::ld(v.bdt, (int64_t)tid * v.H + v.h)
+                          : DT::ld(v.dt, v.token(tid) * v.H + v.h);
+}
+
+// LDS copy of the register-staged chunk plus delta / lam / u / exp(lam) /
+// state weights; the arithmetic is that of stage_chunk.
+template <int P, int N, int NT>
+__device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, int rows,
+                                                 int n_valid, float A2_h, float bias,
+                                                 int softplus, bool weights, char *lds,
+                                                 const MLayout &L) {
+    using CR = ChunkRegs<P, N, NT>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CR::XPT; ++i) {
+        const int e = tid + NT * i, j = e / CR::XC, q = e % CR::XC;
+        if (e < rows * CR::XC)
+            *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) = r.x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CR::BPT; ++i) {
+        const int e = tid + NT * i, j = e / CR::BC, q = e % CR::BC;
+        if (e < rows * CR::BC)
+            *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) = r.b[i];
+    }
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *el = reinterpret_cast<float *>(lds + L.el);
+    float *w = reinterpret_cast<float *>(lds + L.w);
+    const int j = tid;
+    float d = 0.0f, a = 0.0f;
+    if (j < n_valid) {
+        d = delta_of(r.dt, bias, softplus);
+        a = d * A2_h;
+    }
+    const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
+    if (j < kMaxQ) {
+        lam[j] = l;
+        uu[j] = l - flog2(d);
+        el[j] = fexp2(l);
+    }
+    __syncthreads();
+    if (weights && j < kMaxQ)
+        w[j] = fexp2(lam[n_valid - 1] - l) * d;
 }
 
 // C fragments of t-block tau: lane gets C[t][16k + 8g .. +7] for rows t that
@@ -421,22 +510,22 @@ __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int
     }
 }
 
-// t-blocks of a chunk handled by a wave in prefill: with 8 t-blocks, wave w
-// takes w and 7 - w (equal causal work); otherwise t-block w.
-__device__ __forceinline__ int wave_tblocks(int nT, int wave, int *out) {
-    if (nT == 8) {
-        out[0] = wave;
-        out[1] = 7 - wave;
-        return 2;
-    }
-    out[0] = wave;
-    return wave < nT ? 1 : 0;
+// Prefill workgroups have 8 waves (two per SIMD). With 8 t-blocks, waves w
+// and w + 4 (same SIMD) take t-blocks w and 7 - w: equal causal work per
+// SIMD. With fewer t-blocks, wave w takes t-block w.
+constexpr int kPrefillWaves = 8;
+
+__device__ __forceinline__ int wave_tblock(int nT, int wave) {
+    if (nT == 8)
+        return wave < 4 ? wave : 11 - wave;
+    return wave < nT ? wave : -1;
 }
 
 template <int P, int N, class DT>
-__global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using TD = typename DT::T;
+    constexpr int NW = kPrefillWaves;
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
@@ -459,9 +548,9 @@ __global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
                            : (a.init_state ? const_cast<float *>(a.init_state) +
                                                  ((int64_t)s * H + h) * PN
                                            : nullptr);
-    f32x16 S[StateTiles<P, N>::per_wave];
-    state_io<P, N, true>(init, S);
-    state_to_lds<P, N>(lds, L, S);
+    f32x16 S[StateTiles<P, N, NW>::per_wave];
+    state_io<P, N, NW, true>(init, S);
+    state_to_lds<P, N, NW>(lds, L, S);
 
     MView<DT> v;
     v.x = static_cast<const uint16_t *>(a.x);
@@ -484,41 +573,55 @@ __global__ __launch_bounds__(kBlock, 1) void k_scan_mfma(ScanArgs a) {
                                               : nullptr);
     const bool write_bnd = bnd && (!a.replay || nfull > 0);
     uint16_t *y = static_cast<uint16_t *>(a.y);
-    const int nT = Qp / 32;
-
-    for (int c = 0; c < nchunks; ++c) {
-        if (c == nfull && write_bnd)
-            state_io<P, N, false>(bnd, S);
+    const int tau = wave_tblock(Qp / 32, wave);
+    auto set_chunk = [&](int c) {
         v.nb = (c == 0) ? nbuf : 0;
         v.n_valid = min(Q, total - c * Q);
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
-        const bool upd = v.n_valid == Q || (!a.replay && a.final_state);
+    };
+
+    ChunkRegs<P, N, 64 * NW> regs;
+    if (nchunks > 0) {
+        set_chunk(0);
+        load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        if (c == nfull && write_bnd)
+            state_io<P, N, NW, false>(bnd, S);
+        set_chunk(c);
+        const int n_valid = v.n_valid;
+        const bool upd = n_valid == Q || (!a.replay && a.final_state);
         __syncthreads();  // previous chunk's LDS reads are done
-        stage_chunk<P, N, DT>(v, Qp, A2_h, bias, d.softplus, upd, lds, L);
-        int tb[2];
-        const int ntb = wave_tblocks(nT, wave, tb);
+        store_chunk_regs<P, N, 64 * NW>(regs, Qp, n_valid, A2_h, bias, d.softplus, upd, lds, L);
         __syncthreads();
-        for (int i = 0; i < ntb; ++i) {
-            const int tau = tb[i];
-            const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, v.n_valid);
-            if (lo >= hi)
-                continue;
-            bf16x8 cf[N / 16];
+        const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, n_valid);
+        const bool has_rows = tau >= 0 && lo < hi;
+        bf16x8 cf[N / 16];
+        if (has_rows)
             load_cfrag<N, DT>(v, tau, lo, cf);
+        // next chunk's inputs: in flight during this chunk's matrix work
+        const MView<DT> vc = v;
+        if (c + 1 < nchunks) {
+            set_chunk(c + 1);
+            load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
+        }
+        // new state first (registers only; S_bf keeps the chunk-start state)
+        if (upd)
+            chunk_state_update<P, N, NW>(Qp, n_valid, lds, L, S);
+        if (has_rows) {
             f32x16 acc[P / 32];
             tblock_output<P, N, 0, P / 32>(tau, cf, lds, L, acc);
-            emit_tblock<P, 0, P / 32>(v, tau, lo, hi, D_h, lds, L, acc, y);
+            emit_tblock<P, 0, P / 32>(vc, tau, lo, hi, D_h, lds, L, acc, y);
         }
         if (upd) {
-            chunk_state_update<P, N>(Qp, v.n_valid, lds, L, S);
             __syncthreads();  // all waves are done reading S_bf
-            state_to_lds<P, N>(lds, L, S);
+            state_to_lds<P, N, NW>(lds, L, S);
         }
     }
     if (nfull == nchunks && write_bnd)
-        state_io<P, N, false>(bnd, S);
+        state_io<P, N, NW, false>(bnd, S);
     if (!a.replay && a.final_state)
-        state_io<P, N, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
+        state_io<P, N, NW, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
 }
 
 template <int P, int N, class DT>
@@ -607,11 +710,12 @@ __global__ __launch_bounds__(kBlock) void k_decode_mfma(DecodeArgs a) {
         }
     }
     if (commit) {
-        f32x16 S[StateTiles<P, N>::per_wave];
-        state_io<P, N, true>(st, S);
-        chunk_state_update<P, N>(Qp, Q, lds, L, S);
+        constexpr int NW = kBlock / 64;
+        f32x16 S[StateTiles<P, N, NW>::per_wave];
+        state_io<P, N, NW, true>(st, S);
+        chunk_state_update<P, N, NW>(Qp, Q, lds, L, S);
         __syncthreads();  // every wave has read the old state
-        state_io<P, N, false>(st, S);
+        state_io<P, N, NW, false>(st, S);
     }
 }
 
@@ -628,7 +732,7 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     hipError_t e = set_lds(k_scan_mfma<P, N, DT>, L.bytes);
     if (e != hipSuccess)
         return e;
-    k_scan_mfma<P, N, DT><<<dim3(a.d.H * a.S), dim3(kBlock), L.bytes, stream>>>(a);
+    k_scan_mfma<P, N, DT><<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
     return hipGetLastError();
 }
 
