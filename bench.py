@@ -12,10 +12,16 @@ Inputs are resident in HBM before timing starts. Every stage is timed with
 HIP events on the stream the library launches on. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps R]
+
+Counter runs: `--prefill-only` launches only the prefill (W + K times) and
+then one plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE readings
+scale the prefill's; `--traffic FETCH.csv WRITE.csv` turns the two rocprofv3
+counter files into profiles/prefill_w1b_traffic.json (no GPU needed).
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -86,6 +92,54 @@ def load_traffic(sha):
     return rec.get("traffic_bytes_per_launch")
 
 
+CALIB_BYTES = 512 * 2 ** 20
+PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16>"
+COPY_KERNEL = "copyBuffer"
+
+
+def counter_means(path, counter):
+    """Per-dispatch value of one counter for the prefill kernel (mean over its
+    dispatches) and for the calibration copy (the largest copy dispatch: the
+    run's other copies are small host-to-device transfers), from a rocprofv3
+    *_counter_collection.csv file."""
+    vals = {"prefill": [], "copy": []}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = "prefill" if PREFILL_KERNEL in name else "copy" if COPY_KERNEL in name else None
+            if key:
+                vals[key].append(float(row["Counter_Value"]))
+    if not vals["prefill"] or not vals["copy"]:
+        raise SystemExit(f"{path}: no {counter} rows for the prefill kernel and the copy")
+    return {"prefill": sum(vals["prefill"]) / len(vals["prefill"]), "copy": max(vals["copy"])}
+
+
+def write_traffic(fetch_csv, write_csv, cmds):
+    S, T, H, G, P, N = 256, 2048, 32, 1, 64, 128
+    f = counter_means(fetch_csv, "FETCH_SIZE")
+    w = counter_means(write_csv, "WRITE_SIZE")
+    ff = CALIB_BYTES / 1024 / f["copy"]          # bytes a copy reads, over what the counter says
+    wf = CALIB_BYTES / 1024 / w["copy"]
+    traffic = 1024 * (f["prefill"] * ff + w["prefill"] * wf)
+    rec = {
+        "what": "HBM traffic of one prefill launch on 256 sequences x 2048 tokens (H=32, G=1, "
+                "P=64, N=128, chunk 256, bf16 I/O, fp32 state), kernel " + PREFILL_KERNEL,
+        "commands": cmds,
+        "fetch_kib_per_dispatch": f["prefill"], "write_kib_per_dispatch": w["prefill"],
+        "copy_calibration": {"bytes": CALIB_BYTES, "fetch_kib": f["copy"],
+                             "write_kib": w["copy"], "fetch_factor": ff, "write_factor": wf},
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": prefill_bytes(S * T, S, H, G, P, N),
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    out = os.path.join(ROOT, "profiles", "prefill_w1b_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(x, dt, B, C, hp, Q, T, target_s=10.0):
     """Time the fp64 oracle on a bounded sample of the prefill workload
     (whole 2048-token sequences, read back exactly from the device)."""
@@ -116,7 +170,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill launches, then one 512 MiB calibration copy")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 counter files")
     args = ap.parse_args()
+    if args.traffic:
+        cmds = [f"cd /tmp && rocprofv3 --pmc {c} -f csv -d <out> -o run -- python3 "
+                f"<repo>/bench.py --prefill-only --steps 1 --warmup 1"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds.append("python3 bench.py --traffic <fetch counter csv> <write counter csv>")
+        write_traffic(*args.traffic, cmds)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan shards by sequence and head with no "
               "exchange, so multi-GPU runs are not part of this build (use --gpus 1)",
@@ -146,6 +211,32 @@ def main():
     bnd = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
     commit_cache = erd.ReplayCache(shape, S, dev)
 
+    if args.prefill_only:
+        def launch():
+            erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
+                                   cu_seqlens_host=cu_host, want_final=False)
+        for _ in range(args.warmup):
+            launch()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        calib_dst = torch.empty_like(calib_src)
+        torch.cuda.synchronize()
+        calib_dst.copy_(calib_src)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"prefill_avg_launch_ms": ms, "steps": args.steps,
+                          "achieved_gbs": prefill_bytes(S * T, S, H, G, P, N) / ms / 1e6,
+                          "calibration_copy_bytes": CALIB_BYTES,
+                          "kernel_source_sha": kernel_source_sha()}), flush=True)
+        return
+
     # ---- decode workload: prefix 256 + k_i, then R*(K+W) decode tokens ----
     pre = synth.replay_prefix_lengths(S, Q, 1)
     px, pdt, pB, pC = synth.make_tokens_torch(int(pre.sum()), H, G, P, N, 1, dev)
@@ -167,10 +258,6 @@ def main():
     ks256 = (pre % Q).astype(np.int64)
     ks16 = (pre % 16).astype(np.int64)
 
-    # plain copy of known size: calibrates the HBM byte counters
-    calib_src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
-    calib_dst = torch.empty_like(calib_src)
-    calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()

@@ -7,12 +7,15 @@
 //   G^T[s][t]  = B_s . C_t                                  (MFMA, K = N)
 //   M[t][s]    = bf16( G[t][s] exp(lam_t - lam_s) delta_s ),  s <= t, else 0
 //                evaluated as G 2^(l_t - u_s), l = lam log2(e) and
-//                u_s = l_s - log2(delta_s), both precomputed per token
+//                u_s = l_s - log2(delta_s), both precomputed per token; off the
+//                diagonal block as (G 2^(l_t - c)) 2^(c - u_s), c = l at the end
+//                of the 32-token block of s (both factors <= 1, no overflow)
 //   Y^T[p][t]  = exp(lam_t) (S_bf . C_t)[p] + (X^T M^T)[p][t] (MFMA, K = N, s)
 //   y[t][p]    = fmaf(D, x[t][p], Y^T[p][t])
-//   S_loc^T[n][p] = sum_s B_s[n] (w_s x_s[p]),  w_s = exp(lam_last - lam_s) delta_s
-//                 (MFMA, K = s; w x split into bf16 hi + lo)
-//   S          = fmaf(exp(lam_last), S, S_loc)              (fp32, registers)
+//   S^T[n][p]  = exp(lam_last) S^T[n][p] + sum_s B_s[n] (w_s x_s[p]),
+//                w_s = exp(lam_last - lam_s) delta_s: the decayed state is the
+//                MFMA accumulator the chunk's inputs are added into
+//                (K = s ascending; w x split into bf16 hi + lo)
 // S_bf is S rounded to bf16 for the read-out contraction; C.B^T operands are
 // exact bf16; the state path keeps about 16 mantissa bits through the hi/lo
 // split and is never rounded between chunks.
@@ -68,7 +71,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 // LDS layout, in bytes, for a chunk of Qp rows (Qp = max(Q, 32)).
 struct MLayout {
     int XS, BS, SS;                 // row strides in bf16 elements
-    int X, B, S, lam, u, el, w, tot, bytes;
+    int X, B, S, lam, u, el, w, beta, tot, bytes;
     __host__ __device__ MLayout(int Qp, int P, int N) {
         XS = P + kPad;
         BS = N + kPad;
@@ -81,6 +84,7 @@ struct MLayout {
         u = o;   o += kMaxQ * 4;   // lam - log2(delta)
         el = o;  o += kMaxQ * 4;
         w = o;   o += kMaxQ * 4;
+        beta = o; o += kMaxQ * 4;  // 2^(c - u_s), c = l at the end of s's 32-block
         tot = o; o += 64;     // one float per wave
         bytes = o;
     }
@@ -123,6 +127,7 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     const int g = lane >> 5, c = lane & 31;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
     const float *uu = reinterpret_cast<const float *>(lds + L.u);
+    const float *bt = reinterpret_cast<const float *>(lds + L.beta);
     const float *el = reinterpret_cast<const float *>(lds + L.el);
     const int t = 32 * tau + c;
 
@@ -148,22 +153,32 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
             gt = mfma(lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2), cf[k], gt);
         // gt[r] = G[t][s], s = 32 sg + 8 (r/4) + 4 g + r % 4. On the diagonal
         // block the weights with s > t are selected to +0.
-        const bool diag = sg == tau;
         uint32_t mb[8];
+        if (sg == tau) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int s0 = 32 * sg + 8 * q + 4 * g;
-            const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
-            const float us[4] = {u4.x, u4.y, u4.z, u4.w};
-            float m[4];
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 32 * sg + 8 * q + 4 * g;
+                const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
+                const float us[4] = {u4.x, u4.y, u4.z, u4.w};
+                float m[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                m[e] = gt[4 * q + e] * fexp2(lam_t - us[e]);
-                if (diag)
+                for (int e = 0; e < 4; ++e) {
+                    m[e] = gt[4 * q + e] * fexp2(lam_t - us[e]);
                     m[e] = (s0 + e <= t) ? m[e] : 0.0f;
+                }
+                mb[2 * q] = bf16_pack(m[0], m[1]);
+                mb[2 * q + 1] = bf16_pack(m[2], m[3]);
             }
-            mb[2 * q] = bf16_pack(m[0], m[1]);
-            mb[2 * q + 1] = bf16_pack(m[2], m[3]);
+        } else {
+            const float alpha = fexp2(lam_t - lam[32 * sg + 31]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 32 * sg + 8 * q + 4 * g;
+                const float4 b4 = *reinterpret_cast<const float4 *>(bt + s0);
+                mb[2 * q] = bf16_pack((gt[4 * q] * alpha) * b4.x, (gt[4 * q + 1] * alpha) * b4.y);
+                mb[2 * q + 1] =
+                    bf16_pack((gt[4 * q + 2] * alpha) * b4.z, (gt[4 * q + 3] * alpha) * b4.w);
+            }
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -181,75 +196,115 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     }
 }
 
-// Chunk-state tiles (pt, nt) of 32 x 32 are dealt round-robin over the NW
-// waves of the workgroup, ti = wave, wave + NW, ...; ti = pt + (P/32) nt.
-// Which wave computes a tile does not change its arithmetic.
+// Chunk-state tiles (pt, nt) of 32 x 32 and the waves that own them. When
+// the n-tiles pair up, wave w < total/2 owns tiles (pt, 2m) and (pt, 2m+1)
+// with pt = w % (P/32), m = w / (P/32): both share the split token operand.
+// Otherwise tiles are dealt round-robin, ti = w + NW i. Which wave computes
+// a tile, and next to which other tile, does not change its arithmetic.
 template <int P, int N, int NW>
 struct StateTiles {
-    static constexpr int total = (P / 32) * (N / 32);
-    static constexpr int per_wave = (total + NW - 1) / NW;
+    static constexpr int NPT = P / 32, NNT = N / 32;
+    static constexpr int total = NPT * NNT;
+    static constexpr bool paired = false;  // pairing raises register pressure past 256 VGPRs
+    static constexpr int per_wave = paired ? 2 : (total + NW - 1) / NW;
+    __device__ static __forceinline__ bool tile(int w, int i, int &pt, int &nt) {
+        if (paired) {
+            pt = w % NPT;
+            nt = 2 * (w / NPT) + i;
+            return w < total / 2;
+        }
+        const int ti = w + NW * i;
+        pt = ti % NPT;
+        nt = ti / NPT;
+        return ti < total;
+    }
 };
 
+template <int P, int N, int NW>
+__device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds, const MLayout &L,
+                                                f32x16 (&acc)[StateTiles<P, N, NW>::per_wave]) {
+    using ST = StateTiles<P, N, NW>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5;
+    const float *w = reinterpret_cast<const float *>(lds + L.w);
+    int pt0, nt0;
+    if (!ST::tile(wave, 0, pt0, nt0))
+        return;
+    for (int k = k0; k < k1; ++k) {
+        const int r0 = 16 * k + 8 * g;
+        // split token operand w_s x_s[p] for p-tile pt0 (shared by the
+        // wave's tiles when they are paired)
+        const int c16p = 32 * pt0 + 16 * ((lane >> 4) & 1);
+        const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16p);
+        const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
+        const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
+        const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float v[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = bf16_float((uint16_t)xv[j]) * ws[j];
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 hv, lv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t h2 = bf16_pack(v[2 * j], v[2 * j + 1]);
+            hv[j] = h2;
+            lo[2 * j] = v[2 * j] - bf16_float(h2 & 0xffff);
+            lo[2 * j + 1] = v[2 * j + 1] - bf16_float(h2 >> 16);
+            lv[j] = bf16_pack(lo[2 * j], lo[2 * j + 1]);
+        }
+        const bf16x8 bhi = __builtin_bit_cast(bf16x8, hv);
+        const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
+#pragma unroll
+        for (int i = 0; i < ST::per_wave; ++i) {
+            int pt, nt;
+            if (!ST::tile(wave, i, pt, nt))
+                continue;
+            if (!ST::paired && pt != pt0) {
+                // round-robin tiles of another p-tile: split that p-tile
+                const int c16q = 32 * pt + 16 * ((lane >> 4) & 1);
+                const i16x8 xq = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16q);
+                float vq[8], lq[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    vq[j] = bf16_float((uint16_t)xq[j]) * ws[j];
+                u32x4 hq, lqv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t h2 = bf16_pack(vq[2 * j], vq[2 * j + 1]);
+                    hq[j] = h2;
+                    lq[2 * j] = vq[2 * j] - bf16_float(h2 & 0xffff);
+                    lq[2 * j + 1] = vq[2 * j + 1] - bf16_float(h2 >> 16);
+                    lqv[j] = bf16_pack(lq[2 * j], lq[2 * j + 1]);
+                }
+                const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
+                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
+                acc[i] = mfma(aop, __builtin_bit_cast(bf16x8, hq), acc[i]);
+                acc[i] = mfma(aop, __builtin_bit_cast(bf16x8, lqv), acc[i]);
+                continue;
+            }
+            const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
+            const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
+            acc[i] = mfma(aop, bhi, acc[i]);
+            acc[i] = mfma(aop, blo, acc[i]);
+        }
+    }
+}
+
 // S (this wave's tiles, accumulator layout S^T[n][p]) <-
-//   fmaf(exp(lam_last), S, sum_s B_s[n] w_s x_s[p]) over the Qp chunk rows in LDS.
+//   exp(lam_last) S + sum_s B_s[n] w_s x_s[p] over the Qp chunk rows in LDS.
 template <int P, int N, int NW>
 __device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const char *lds,
                                                    const MLayout &L,
                                                    f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 5;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
-    const float *w = reinterpret_cast<const float *>(lds + L.w);
-    constexpr int NTW = StateTiles<P, N, NW>::per_wave;
-    constexpr int TOT = StateTiles<P, N, NW>::total;
-    const int pt = wave % (P / 32);
-    f32x16 acc[NTW];
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
-        acc[i] = f32x16{};
-    if (wave < TOT) {
-        for (int k = 0; k < Qp / 16; ++k) {
-            const int r0 = 16 * k + 8 * g;
-            const int c16p = 32 * pt + 16 * ((lane >> 4) & 1);
-            const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16p);
-            const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
-            const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
-            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            float v[8], lo[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = bf16_float((uint16_t)xv[j]) * ws[j];
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            u32x4 hv, lv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t h2 = bf16_pack(v[2 * j], v[2 * j + 1]);
-                hv[j] = h2;
-                lo[2 * j] = v[2 * j] - bf16_float(h2 & 0xffff);
-                lo[2 * j + 1] = v[2 * j + 1] - bf16_float(h2 >> 16);
-                lv[j] = bf16_pack(lo[2 * j], lo[2 * j + 1]);
-            }
-            const bf16x8 bhi = __builtin_bit_cast(bf16x8, hv);
-            const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
-#pragma unroll
-            for (int i = 0; i < NTW; ++i) {
-                const int ti = wave + NW * i;
-                if (TOT % NW != 0 && ti >= TOT)
-                    continue;
-                const int nt = ti / (P / 32);
-                const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
-                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
-                acc[i] = mfma(aop, bhi, acc[i]);
-                acc[i] = mfma(aop, blo, acc[i]);
-            }
-        }
-    }
     const float dec = fexp2(lam[n_valid - 1]);
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            S[i][r] = fmaf(dec, S[i][r], acc[i][r]);
+            S[i][r] = S[i][r] * dec;
+    chunk_state_mma<P, N, NW>(0, Qp / 16, lds, L, S);
 }
 
 // State tiles <-> global [P][N] fp32 (one float4 per lane per r-group).
@@ -257,13 +312,11 @@ template <int P, int N, int NW, bool LOAD>
 __device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
-    constexpr int TOT = StateTiles<P, N, NW>::total;
 #pragma unroll
     for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
-        const int ti = wave + NW * i;
-        if (ti >= TOT)
+        int pt, nt;
+        if (!StateTiles<P, N, NW>::tile(wave, i, pt, nt))
             continue;
-        const int pt = ti % (P / 32), nt = ti / (P / 32);
         const int p = 32 * pt + c;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -290,13 +343,11 @@ __device__ __forceinline__ void state_to_lds(char *lds, const MLayout &L,
                                              const f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, c = lane & 31;
-    constexpr int TOT = StateTiles<P, N, NW>::total;
 #pragma unroll
     for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
-        const int ti = wave + NW * i;
-        if (ti >= TOT)
+        int pt, nt;
+        if (!StateTiles<P, N, NW>::tile(wave, i, pt, nt))
             continue;
-        const int pt = ti % (P / 32), nt = ti / (P / 32);
         const int p = 32 * pt + c;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -371,8 +422,11 @@ __device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias
         el[j] = fexp2(l);
     }
     __syncthreads();
-    if (weights && j < kMaxQ)
-        w[j] = fexp2(lam[v.n_valid - 1] - l) * d;
+    if (j < kMaxQ) {
+        reinterpret_cast<float *>(lds + L.beta)[j] = fexp2(lam[j | 31] - uu[j]);
+        if (weights)
+            w[j] = fexp2(lam[v.n_valid - 1] - l) * d;
+    }
 }
 
 // Register-staged copy of a chunk's X / B rows and raw dt, loaded one chunk
@@ -392,30 +446,51 @@ __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
                                                 ChunkRegs<P, N, NT> &r) {
     using CR = ChunkRegs<P, N, NT>;
     const int tid = threadIdx.x;
+    if (v.nb == 0 && v.n_valid == rows) {
+        // every row is an input token: fixed row stride, no clamping
+        const int64_t xs = (int64_t)(NT / CR::XC) * v.H * P;
+        const uint16_t *xp = v.x + (v.token(tid / CR::XC) * v.H + v.h) * P + 8 * (tid % CR::XC);
+#pragma unroll
+        for (int i = 0; i < CR::XPT; ++i)
+            if (tid + NT * i < rows * CR::XC)
+                r.x[i] = *reinterpret_cast<const uint4 *>(xp + i * xs);
+        const int64_t bs = (int64_t)(NT / CR::BC) * v.G * N;
+        const uint16_t *bp = v.B + (v.token(tid / CR::BC) * v.G + v.g) * N + 8 * (tid % CR::BC);
+#pragma unroll
+        for (int i = 0; i < CR::BPT; ++i)
+            if (tid + NT * i < rows * CR::BC)
+                r.b[i] = *reinterpret_cast<const uint4 *>(bp + i * bs);
+        r.dt = DT::ld(v.dt, v.token(tid < rows ? tid : 0) * v.H + v.h);
+        return;
+    }
+    // General chunk, branch-free: every lane loads a valid row (rows past
+    // the chunk read row 0) so the loads stay in flight together;
+    // store_chunk_regs zeroes the lanes that are not chunk rows.
 #pragma unroll
     for (int i = 0; i < CR::XPT; ++i) {
-        const int e = tid + NT * i, j = e / CR::XC, q = e % CR::XC;
-        r.x[i] = make_uint4(0, 0, 0, 0);
-        if (e < rows * CR::XC && j < v.n_valid) {
-            const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
-                                           : v.x + (v.token(j) * v.H + v.h) * P;
-            r.x[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
+        const int e = tid + NT * i, q = e % CR::XC;
+        int j = e / CR::XC;
+        j = (e < rows * CR::XC && j < v.n_valid) ? j : 0;
+        const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
+                                       : v.x + (v.token(j) * v.H + v.h) * P;
+        r.x[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
 #pragma unroll
     for (int i = 0; i < CR::BPT; ++i) {
-        const int e = tid + NT * i, j = e / CR::BC, q = e % CR::BC;
-        r.b[i] = make_uint4(0, 0, 0, 0);
-        if (e < rows * CR::BC && j < v.n_valid) {
-            const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
-                                           : v.B + (v.token(j) * v.G + v.g) * N;
-            r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
+        const int e = tid + NT * i, q = e % CR::BC;
+        int j = e / CR::BC;
+        j = (e < rows * CR::BC && j < v.n_valid) ? j : 0;
+        const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
+                                       : v.B + (v.token(j) * v.G + v.g) * N;
+        r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
-    r.dt = 0.0f;
-    if (tid < v.n_valid)
-        r.dt = tid < v.nb ? DT::ld(v.bdt, (int64_t)tid * v.H + v.h)
-                          : DT::ld(v.dt, v.token(tid) * v.H + v.h);
+    const int jd = tid < v.n_valid ? tid : 0;
+    r.dt = jd < v.nb ? DT::ld(v.bdt, (int64_t)jd * v.H + v.h)
+                     : DT::ld(v.dt, v.token(jd) * v.H + v.h);
+}
+
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &u) {
+    return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
 }
 
 // LDS copy of the register-staged chunk plus delta / lam / u / exp(lam) /
@@ -427,17 +502,20 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
                                                  const MLayout &L) {
     using CR = ChunkRegs<P, N, NT>;
     const int tid = threadIdx.x;
+    const bool full = n_valid == rows;
 #pragma unroll
     for (int i = 0; i < CR::XPT; ++i) {
         const int e = tid + NT * i, j = e / CR::XC, q = e % CR::XC;
         if (e < rows * CR::XC)
-            *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) = r.x[i];
+            *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) =
+                full ? r.x[i] : keep_if(j < n_valid, r.x[i]);
     }
 #pragma unroll
     for (int i = 0; i < CR::BPT; ++i) {
         const int e = tid + NT * i, j = e / CR::BC, q = e % CR::BC;
         if (e < rows * CR::BC)
-            *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) = r.b[i];
+            *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) =
+                full ? r.b[i] : keep_if(j < n_valid, r.b[i]);
     }
     float *lam = reinterpret_cast<float *>(lds + L.lam);
     float *uu = reinterpret_cast<float *>(lds + L.u);
@@ -448,7 +526,7 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
     if (j < n_valid) {
         d = delta_of(r.dt, bias, softplus);
         a = d * A2_h;
-    }
+    }  // (a lane past the chunk loaded row 0's dt; it is not used)
     const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
     if (j < kMaxQ) {
         lam[j] = l;
@@ -456,8 +534,11 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
         el[j] = fexp2(l);
     }
     __syncthreads();
-    if (weights && j < kMaxQ)
-        w[j] = fexp2(lam[n_valid - 1] - l) * d;
+    if (j < kMaxQ) {
+        reinterpret_cast<float *>(lds + L.beta)[j] = fexp2(lam[j | 31] - uu[j]);
+        if (weights)
+            w[j] = fexp2(lam[n_valid - 1] - l) * d;
+    }
 }
 
 // C fragments of t-block tau: lane gets C[t][16k + 8g .. +7] for rows t that
@@ -465,17 +546,19 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
 template <int N, class DT>
 __device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_lo,
                                            bf16x8 (&cf)[N / 16]) {
+    // rows outside [row_lo, n_valid) load row row_lo and are zeroed after
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, t = 32 * tau + (lane & 31);
     const bool ok = t >= row_lo && t < v.n_valid && t >= v.nb;
-    const uint16_t *src = ok ? v.C + (v.token(t) * v.G + v.g) * N : nullptr;
+    const int tt = ok ? t : row_lo;
+    const uint16_t *src = v.C + (v.token(tt) * v.G + v.g) * N;
+    uint4 raw[N / 16];
 #pragma unroll
-    for (int k = 0; k < N / 16; ++k) {
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (ok)
-            val = *reinterpret_cast<const uint4 *>(src + 16 * k + 8 * g);
-        cf[k] = __builtin_bit_cast(bf16x8, val);
-    }
+    for (int k = 0; k < N / 16; ++k)
+        raw[k] = *reinterpret_cast<const uint4 *>(src + 16 * k + 8 * g);
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k)
+        cf[k] = __builtin_bit_cast(bf16x8, keep_if(ok, raw[k]));
 }
 
 // y rows [row_lo, row_hi) of t-block tau: y = fmaf(D, x, acc), -0 -> +0.
@@ -510,6 +593,16 @@ __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int
     }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Renumber them so that consecutive work items (the heads of one
+// sequence, which share its B and C rows) run on the same XCD.
+__device__ __forceinline__ int xcd_local_index(int bid, int nblocks) {
+    constexpr int kXcds = 8;
+    if (nblocks % kXcds != 0)
+        return bid;
+    return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
 // Prefill workgroups have 8 waves (two per SIMD). With 8 t-blocks, waves w
 // and w + 4 (same SIMD) take t-blocks w and 7 - w: equal causal work per
 // SIMD. With fewer t-blocks, wave w takes t-block w.
@@ -529,7 +622,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
-    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
+    const int s = wid / H, h = wid % H;
     const int g = h / (H / G);
     const int wave = threadIdx.x >> 6;
     constexpr int PN = P * N;
