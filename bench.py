@@ -63,16 +63,20 @@ def prefill_flops(T, H, G, P, N, Q):
 
 
 def replay_step_bytes(ks, Q, H, G, P, N, io=2, dtb=2, with_C=False):
-    """Algorithmic bytes of one replay-decode step for buffer fills ks."""
+    """Algorithmic bytes of one replay-decode step for buffer fills ks: the
+    bf16 copy of the boundary state (the read-out operand), the buffered
+    tokens' x, B and raw dt, the new token, its append and y; when the token
+    fills the chunk, the fp32 state is read and written and its bf16 copy
+    written."""
     ks = np.asarray(ks, dtype=np.int64)
-    state = H * P * N * 4
+    state_bf = H * P * N * 2
     per_buf_tok = H * P * io + G * N * io + H * dtb          # x, B, raw dt re-read
     new_tok = H * P * io + H * dtb + 2 * G * N * io          # inputs
     append = H * P * io + H * dtb + G * N * io * (2 if with_C else 1)
     y = H * P * io
     commits = int(np.sum(ks + 1 == Q))
-    return int(len(ks) * (state + new_tok + append + y) + ks.sum() * per_buf_tok
-               + commits * state)
+    return int(len(ks) * (state_bf + new_tok + append + y) + ks.sum() * per_buf_tok
+               + commits * H * P * N * (4 + 4 + 2))
 
 
 def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):

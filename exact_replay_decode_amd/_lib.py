@@ -16,13 +16,13 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {
     0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_DTYPE",
     -4: "SSD_ERR_STATE_NOT_FP32", -5: "SSD_ERR_CHUNK_MISMATCH",
-    -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_UNSUPPORTED", -8: "SSD_ERR_HIP",
+    -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_UNSUPPORTED", -8: "SSD_ERR_HIP", -9: "SSD_ERR_ALIGN",
 }
 
 # every symbol include/ssd_replay.h declares
 EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
-           "ssd_replay_decode", "ssm_state_update")
+           "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh")
 
 
 class ssd_shape(ctypes.Structure):
@@ -33,10 +33,11 @@ class ssd_shape(ctypes.Structure):
 
 
 class ssd_replay_cache(ctypes.Structure):
-    _fields_ = [("state", ctypes.c_void_p), ("buf_x", ctypes.c_void_p),
-                ("buf_dt", ctypes.c_void_p), ("buf_B", ctypes.c_void_p),
-                ("buf_C", ctypes.c_void_p), ("buf_len", ctypes.c_void_p),
-                ("boundary_pos", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+    _fields_ = [("state", ctypes.c_void_p), ("state_bf", ctypes.c_void_p),
+                ("buf_x", ctypes.c_void_p), ("buf_dt", ctypes.c_void_p),
+                ("buf_B", ctypes.c_void_p), ("buf_C", ctypes.c_void_p),
+                ("buf_len", ctypes.c_void_p), ("boundary_pos", ctypes.c_void_p),
+                ("arrivals", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.ssd_prefill_varlen.restype = ctypes.c_int
     lib.ssd_prefill_varlen.argtypes = [shp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_replay_cache_refresh.restype = ctypes.c_int
+    lib.ssd_replay_cache_refresh.argtypes = [shp, cp, vp]
     lib.ssd_commit_boundary.restype = ctypes.c_int
     lib.ssd_commit_boundary.argtypes = [shp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, cp, vp]
     lib.ssd_replay_prefill.restype = ctypes.c_int

@@ -89,8 +89,9 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, device):
 
 
 class ReplayCache:
-    """Exact-replay cache for num_slots sequences: fp32 boundary state plus
-    the partial-chunk token buffers (all zeros = every slot fresh)."""
+    """Exact-replay cache for num_slots sequences: fp32 boundary state (and
+    its bf16 copy, the read-out operand) plus the partial-chunk token buffers
+    (all zeros = every slot fresh)."""
 
     def __init__(self, shape: Shape, num_slots: int, device="cuda", with_C: bool = False,
                  state_dtype: torch.dtype = torch.float32, _empty: bool = False):
@@ -100,6 +101,9 @@ class ReplayCache:
         self.device = torch.device(device)
         mk = torch.empty if _empty else torch.zeros
         self.state = mk((num_slots, H, P, N), dtype=state_dtype, device=self.device)
+        # bf16 copy of the state in the read-out operand order [N/16, P, 16]
+        self.state_bf = mk((num_slots, H, N // 16, P, 16), dtype=torch.bfloat16,
+                           device=self.device)
         self.buf_x = mk((num_slots, Q, H, P), dtype=shape.io, device=self.device)
         self.buf_dt = mk((num_slots, Q, H), dtype=shape.dtt, device=self.device)
         self.buf_B = mk((num_slots, Q, G, N), dtype=shape.io, device=self.device)
@@ -107,18 +111,34 @@ class ReplayCache:
                       if with_C else None)
         self.buf_len = mk((num_slots,), dtype=torch.int32, device=self.device)
         self.boundary_pos = mk((num_slots,), dtype=torch.int64, device=self.device)
+        # decode bookkeeping, zero between calls (always allocated zeroed)
+        self.arrivals = torch.zeros((num_slots,), dtype=torch.int32, device=self.device)
 
     def struct(self) -> _lib.ssd_replay_cache:
         sd = _lib.SSD_F32 if self.state.dtype == torch.float32 else _lib.SSD_BF16
         return _lib.ssd_replay_cache(
-            self.state.data_ptr(), self.buf_x.data_ptr(), self.buf_dt.data_ptr(),
-            self.buf_B.data_ptr(), None if self.buf_C is None else self.buf_C.data_ptr(),
-            self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.num_slots,
-            self.shape.chunk_size, sd)
+            self.state.data_ptr(), self.state_bf.data_ptr(), self.buf_x.data_ptr(),
+            self.buf_dt.data_ptr(), self.buf_B.data_ptr(),
+            None if self.buf_C is None else self.buf_C.data_ptr(),
+            self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.arrivals.data_ptr(),
+            self.num_slots, self.shape.chunk_size, sd)
+
+    def state_bf_rowmajor(self) -> torch.Tensor:
+        """The bf16 state copy as [num_slots, H, P, N]."""
+        s = self.state_bf
+        return s.permute(0, 1, 3, 2, 4).reshape(s.shape[0], s.shape[1], s.shape[3], -1)
+
+    def refresh(self, stream=None) -> None:
+        """Rebuild the bf16 state copy after writing `state` directly."""
+        c, sh = self.struct(), self.shape.c()
+        rc = _lib.load().ssd_replay_cache_refresh(ctypes.byref(sh), ctypes.byref(c),
+                                                  _stream(stream))
+        _lib.check(rc, "ssd_replay_cache_refresh")
 
     def tensors(self):
-        return [t for t in (self.state, self.buf_x, self.buf_dt, self.buf_B, self.buf_C,
-                            self.buf_len, self.boundary_pos) if t is not None]
+        return [t for t in (self.state, self.state_bf, self.buf_x, self.buf_dt, self.buf_B,
+                            self.buf_C, self.buf_len, self.boundary_pos, self.arrivals)
+                if t is not None]
 
     def clone(self) -> "ReplayCache":
         c = ReplayCache(self.shape, self.num_slots, self.device, self.buf_C is not None,

@@ -60,6 +60,14 @@ int check_seqs(const Dims &d, int32_t S, int64_t T, const int32_t *cu_host, cons
     return SSD_OK;
 }
 
+// Arrays the kernels move in 16-byte pieces (NULL passes).
+bool a16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <class... T>
+bool all_a16(const T *...p) {
+    return (a16(p) && ...);
+}
+
 int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
     if (!c)
         return SSD_ERR_NULL;
@@ -67,10 +75,13 @@ int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
         return SSD_ERR_STATE_NOT_FP32;
     if (c->chunk_size != sh->chunk_size)
         return SSD_ERR_CHUNK_MISMATCH;
-    if (!c->state || !c->buf_x || !c->buf_dt || !c->buf_B || !c->buf_len || !c->boundary_pos)
+    if (!c->state || !c->state_bf || !c->buf_x || !c->buf_dt || !c->buf_B || !c->buf_len ||
+        !c->boundary_pos || !c->arrivals)
         return SSD_ERR_NULL;
     if (c->num_slots <= 0)
         return SSD_ERR_SHAPE;
+    if (!all_a16(c->state, c->state_bf, c->buf_x, c->buf_B, c->buf_C))
+        return SSD_ERR_ALIGN;
     return SSD_OK;
 }
 
@@ -100,6 +111,7 @@ const char *ssd_status_string(int status) {
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
     case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape outside the built set";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP launch or runtime error";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: an array is not 16-byte aligned";
     default: return "unknown ssd_status";
     }
 }
@@ -109,11 +121,25 @@ size_t ssd_replay_cache_bytes(const ssd_shape *sh, int32_t num_slots, int32_t wi
     if (check_shape(sh, &d) != SSD_OK || num_slots < 0)
         return 0;
     const size_t io = dtype_bytes(sh->io_dtype), dtb = dtype_bytes(sh->dt_dtype);
-    const size_t state = (size_t)d.H * d.P * d.N * sizeof(float);
+    const size_t state = (size_t)d.H * d.P * d.N * (sizeof(float) + sizeof(uint16_t));
     const size_t per_tok = (size_t)d.H * d.P * io + (size_t)d.H * dtb +
                            (with_C ? 2 : 1) * (size_t)d.G * d.N * io;
-    const size_t per_slot = state + (size_t)d.Q * per_tok + sizeof(int32_t) + sizeof(int64_t);
+    const size_t per_slot =
+        state + (size_t)d.Q * per_tok + 2 * sizeof(int32_t) + sizeof(int64_t);
     return per_slot * (size_t)num_slots;
+}
+
+int ssd_replay_cache_refresh(const ssd_shape *sh, const ssd_replay_cache *cache,
+                             hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_cache(sh, cache)) != SSD_OK)
+        return st;
+    return hip_status(ssd::launch_refresh_state_bf(cache->state, cache->state_bf,
+                                                   (int64_t)cache->num_slots * d.H, d.P, d.N,
+                                                   (hipStream_t)stream));
 }
 
 size_t ssd_prefill_workspace_bytes(const ssd_shape *sh, int32_t num_seqs, int64_t total_tokens) {
@@ -142,6 +168,8 @@ int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t 
         return SSD_OK;
     if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
         return SSD_ERR_NULL;
+    if (!all_a16(x, B, C, y, init_state, final_state, boundary_state))
+        return SSD_ERR_ALIGN;
     ssd::ScanArgs a = {};
     a.d = d;
     a.S = S;
@@ -176,6 +204,8 @@ int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t
         return SSD_OK;
     if (!boundary_state || (T > 0 && (!x || !dt || !B || (cache->buf_C && !C))))
         return SSD_ERR_NULL;
+    if (!all_a16(x, B, C, boundary_state))
+        return SSD_ERR_ALIGN;
     ssd::CommitArgs a = {};
     a.d = d;
     a.S = S;
@@ -186,6 +216,7 @@ int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t
     a.num_slots = cache->num_slots;
     a.state_src = boundary_state;
     a.cache_state = cache->state;
+    a.cache_state_bf = cache->state_bf;
     a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt;
     a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
     a.buf_len = cache->buf_len;
@@ -212,6 +243,8 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
         return SSD_OK;
     if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
         return SSD_ERR_NULL;
+    if (!all_a16(x, B, C, y))
+        return SSD_ERR_ALIGN;
     ssd::ScanArgs a = {};
     a.d = d;
     a.S = S;
@@ -223,6 +256,7 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
     a.replay = 1;
     a.num_slots = cache->num_slots;
     a.cache_state = cache->state;
+    a.cache_state_bf = cache->state_bf;
     a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
     a.buf_len = cache->buf_len;
     hipError_t e = launch_scan_any(a, (hipStream_t)stream);
@@ -238,6 +272,7 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
     c.num_slots = cache->num_slots;
     c.state_src = nullptr;
     c.cache_state = cache->state;
+    c.cache_state_bf = cache->state_bf;
     c.buf_x = cache->buf_x; c.buf_dt = cache->buf_dt;
     c.buf_B = cache->buf_B; c.buf_C = cache->buf_C;
     c.buf_len = cache->buf_len;
@@ -262,6 +297,8 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
         return SSD_OK;
     if (!x || !dt || !B || !C || !A || !y)
         return SSD_ERR_NULL;
+    if (!all_a16(x, B, C, y))
+        return SSD_ERR_ALIGN;
     ssd::DecodeArgs a = {};
     a.d = d;
     a.batch = batch;
@@ -271,10 +308,12 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.y = y;
     a.num_slots = cache->num_slots;
     a.cache_state = cache->state;
+    a.cache_state_bf = cache->state_bf;
     a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt;
     a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
+    a.arrivals = cache->arrivals;
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
 }
@@ -294,6 +333,8 @@ int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,
         return SSD_OK;
     if (!state || !x || !dt || !A || !B || !C || !y)
         return SSD_ERR_NULL;
+    if (!all_a16(state, x, B, C, y))
+        return SSD_ERR_ALIGN;
     ssd::SsuArgs a = {};
     a.d = d;
     a.batch = batch;

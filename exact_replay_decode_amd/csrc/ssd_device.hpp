@@ -21,6 +21,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct IoF32 {
     using T = float;
     __device__ static __forceinline__ float ld(const T *p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ float val(T v) { return v; }
     __device__ static __forceinline__ T cvt(float v) { return v; }
 };
 
@@ -28,6 +29,9 @@ struct IoBF16 {
     using T = uint16_t;
     __device__ static __forceinline__ float ld(const T *p, int64_t i) {
         return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+    }
+    __device__ static __forceinline__ float val(T v) {
+        return __uint_as_float(static_cast<uint32_t>(v) << 16);
     }
     // round to nearest even; NaN stays NaN
     __device__ static __forceinline__ T cvt(float v) {
@@ -38,6 +42,19 @@ struct IoBF16 {
         return static_cast<T>(u >> 16);
     }
 };
+
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion). Every
+// bf16 copy of the state, and the read-out operand made from it, uses this.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Position of state element (p, n) of one head in the cache's bf16 state
+// copy, laid out [N/16][P][16]: the 16-wide n-blocks of all rows in turn, so
+// that the read-out operand of 32 rows x 16 columns is 1 KiB contiguous.
+__host__ __device__ __forceinline__ int64_t state_bf_index(int p, int n, int P) {
+    return (int64_t)(n >> 4) * 16 * P + 16 * p + (n & 15);
+}
 
 // ---- scalar functions that fix the rounding ------------------------------
 
@@ -67,20 +84,28 @@ __device__ __forceinline__ float state_weight(float lam_last, float lam_j, float
     return decay_exp(lam_last - lam_j) * dlt_j;
 }
 
-// ---- prefix-consistent inclusive scan over one 256-thread workgroup -------
+// ---- prefix-consistent inclusive scan -------------------------------------
 // Lane t's result depends only on the values of lanes 0..t and on a fixed
 // combination tree: a Hillis-Steele scan inside each 64-lane wave, then the
-// totals of the earlier waves added in ascending order. `tot` is 4 floats of
-// LDS. Every thread of the block must call it.
-__device__ __forceinline__ float block_scan_inclusive(float v, float *tot) {
+// totals of the earlier waves added in ascending order.
+
+__device__ __forceinline__ float wave_scan_inclusive(float v) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float o = __shfl_up(v, off, 64);
         if (lane >= off)
             v = v + o;
     }
+    return v;
+}
+
+// Over a whole workgroup (any number of waves up to 8). `tot` is 8 floats of
+// LDS. Every thread of the block must call it.
+__device__ __forceinline__ float block_scan_inclusive(float v, float *tot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    v = wave_scan_inclusive(v);
     if (lane == 63)
         tot[wave] = v;
     __syncthreads();
@@ -93,6 +118,28 @@ __device__ __forceinline__ float block_scan_inclusive(float v, float *tot) {
     }
     __syncthreads();
     return r;
+}
+
+// The same sums computed by a single wave that holds rows lane + 64 i in
+// v[i], i < nseg <= 4: segment i takes the place of the block's wave i.
+__device__ __forceinline__ void wave_scan_segments(float (&v)[4], int nseg) {
+    float tot[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < nseg) {
+            v[i] = wave_scan_inclusive(v[i]);
+            tot[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+        }
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        if (i < nseg) {
+            float pre = tot[0];
+            for (int w = 1; w < i; ++w)
+                pre = pre + tot[w];
+            v[i] = pre + v[i];
+        }
+    }
 }
 
 }  // namespace ssd

@@ -32,6 +32,7 @@ struct ScanArgs {
     int32_t replay;
     int32_t num_slots;
     float *cache_state;       // [slots,H,P,N]
+    void *cache_state_bf;     // [slots,H,P,N] bf16 copy of cache_state
     const void *buf_x, *buf_dt, *buf_B;
     const int32_t *buf_len;   // [slots]
 };
@@ -48,6 +49,7 @@ struct CommitArgs {
     int32_t num_slots;
     const float *state_src;   // [S,H,P,N] copied to the slot state, or null
     float *cache_state;
+    void *cache_state_bf;     // bf16 copy, written with cache_state
     void *buf_x, *buf_dt, *buf_B, *buf_C;  // buf_C may be null
     int32_t *buf_len;
     int64_t *boundary_pos;
@@ -62,9 +64,11 @@ struct DecodeArgs {
     void *y;
     int32_t num_slots;
     float *cache_state;
+    void *cache_state_bf;     // bf16 copy of cache_state
     void *buf_x, *buf_dt, *buf_B, *buf_C;
     int32_t *buf_len;
     int64_t *boundary_pos;
+    int32_t *arrivals;        // [slots], zero between calls
 };
 
 struct SsuArgs {
@@ -89,5 +93,8 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+// bf16 copy of `heads` fp32 [P][N] states (the cache's read-out operand)
+hipError_t launch_refresh_state_bf(const float *state, void *state_bf, int64_t heads, int P, int N,
+                                   hipStream_t stream);
 
 }  // namespace ssd

@@ -46,10 +46,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kPad = 8;  // bf16 elements of padding per LDS row
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    __bf16 b = static_cast<__bf16>(f);  // round to nearest even
-    return __builtin_bit_cast(uint16_t, b);
-}
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return bf16_rne(f); }
 __device__ __forceinline__ float bf16_float(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
@@ -116,10 +113,104 @@ __device__ __forceinline__ i16x8 lds_tr8(const char *lds, int base, int stride, 
 __device__ __forceinline__ bf16x8 as_bf16x8(const i16x8 &v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------------------
-// Output of one 32-row t-block: p-tiles [pt0, pt1) of Y^T for chunk rows
-// t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7] (g = lane/32),
-// zero for rows that are not outputs. acc[pt] receives Y^T[p][t] (without
-// the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
+// The pieces of a t-block's output arithmetic. Prefill and decode build the
+// same operands and call these in the same order, so each output element is
+// produced by the same MFMA sequence in both.
+
+// C . S_bf for one 32-wide p-tile: K = n ascending in steps of 16 (then
+// readout_scale multiplies column t by exp(lam_t)). sa(k) returns the A
+// operand S_bf[p][16k + 8g .. +7].
+template <int N, class F>
+__device__ __forceinline__ f32x16 readout_raw(F sa, const bf16x8 *cf) {
+    f32x16 a = {};
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k)
+        a = mfma(sa(k), cf[k], a);
+    return a;
+}
+
+__device__ __forceinline__ f32x16 readout_scale(f32x16 a, float el_t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        a[r] = a[r] * el_t;
+    return a;
+}
+
+// G^T for one 32-row s-block: K = n ascending. ba(k) returns the A operand
+// B[s][16k + 8g .. +7] for s = 32 sg + lane % 32.
+template <int N, class F>
+__device__ __forceinline__ f32x16 gram_block(F ba, const bf16x8 *cf) {
+    f32x16 gt = {};
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k)
+        gt = mfma(ba(k), cf[k], gt);
+    return gt;
+}
+
+// Weights of the diagonal s-block, packed to bf16 pairs: gt[4q + e] =
+// G[t][s] for s = s_base + 8q + 4g + e; m = G 2^(l_t - u_s) for s <= t and +0
+// otherwise (selected, never multiplied).
+__device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const float *uu, int s_base,
+                                       int t, uint32_t (&mb)[8]) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int s0 = s_base + 8 * q + 4 * g;
+        const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
+        const float us[4] = {u4.x, u4.y, u4.z, u4.w};
+        float m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            m[e] = gt[4 * q + e] * fexp2(lam_t - us[e]);
+            m[e] = (s0 + e <= t) ? m[e] : 0.0f;
+        }
+        mb[2 * q] = bf16_pack(m[0], m[1]);
+        mb[2 * q + 1] = bf16_pack(m[2], m[3]);
+    }
+}
+
+// Weights of an earlier s-block: (G alpha) beta_s with alpha = 2^(l_t - c)
+// and beta_s = 2^(c - u_s), c = l at the end of the s-block.
+__device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float *bt, int s_base,
+                                      uint32_t (&mb)[8]) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int s0 = s_base + 8 * q + 4 * g;
+        const float4 b4 = *reinterpret_cast<const float4 *>(bt + s0);
+        mb[2 * q] = bf16_pack((gt[4 * q] * alpha) * b4.x, (gt[4 * q + 1] * alpha) * b4.y);
+        mb[2 * q + 1] = bf16_pack((gt[4 * q + 2] * alpha) * b4.z, (gt[4 * q + 3] * alpha) * b4.w);
+    }
+}
+
+// Y^T[p][t] += sum_s X^T[p][s] M^T[s][t] over one s-block, K = 16 rows per
+// MFMA: rows r0 = 16 half + 4g .. +3 and r0 + 8 .. +11 of the block, read
+// transposed from the row-major LDS tile (xbase, row stride xs, block row 0
+// at xrow0); mb[4 half .. 4 half + 3] holds the matching M^T rows.
+template <int PT0, int PT1>
+__device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const char *lds, int xbase,
+                                              int xs, int xrow0, f32x16 *acc) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 bv = {mb[4 * half], mb[4 * half + 1], mb[4 * half + 2], mb[4 * half + 3]};
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
+        const int r0 = xrow0 + 16 * half + 4 * g;
+#pragma unroll
+        for (int pt = PT0; pt < PT1; ++pt) {
+            const int c16 = 32 * pt + 16 * ((lane >> 4) & 1);
+            const bf16x8 aop = as_bf16x8(lds_tr8(lds, xbase, xs, r0, r0 + 8, c16));
+            acc[pt] = mfma(aop, bop, acc[pt]);
+        }
+    }
+}
+
+// Output of one 32-row t-block in prefill: p-tiles [PT0, PT1) of Y^T for
+// chunk rows t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7]
+// (g = lane/32), zero for rows that are not outputs. acc[pt] receives
+// Y^T[p][t] (without the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
 template <int P, int N, int PT0, int PT1>
 __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const char *lds,
                                               const MLayout &L, f32x16 *acc) {
@@ -131,68 +222,27 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     const float *el = reinterpret_cast<const float *>(lds + L.el);
     const int t = 32 * tau + c;
 
-    // state read-out C . S_bf, K = n in ascending steps of 16
 #pragma unroll
-    for (int pt = PT0; pt < PT1; ++pt) {
-        f32x16 a = {};
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k)
-            a = mfma(lds_b128(lds, L.S + ((32 * pt + c) * L.SS + 16 * k + 8 * g) * 2), cf[k], a);
-        const float e = el[t];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            a[r] = a[r] * e;
-        acc[pt] = a;
-    }
+    for (int pt = PT0; pt < PT1; ++pt)
+        acc[pt] = readout_scale(
+            readout_raw<N>(
+                [&](int k) {
+                    return lds_b128(lds, L.S + ((32 * pt + c) * L.SS + 16 * k + 8 * g) * 2);
+                },
+                cf),
+            el[t]);
 
     const float lam_t = lam[t];
     for (int sg = 0; sg <= tau; ++sg) {
-        f32x16 gt = {};
-#pragma unroll
-        for (int k = 0; k < N / 16; ++k)
-            gt = mfma(lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2), cf[k], gt);
-        // gt[r] = G[t][s], s = 32 sg + 8 (r/4) + 4 g + r % 4. On the diagonal
-        // block the weights with s > t are selected to +0.
+        const f32x16 gt = gram_block<N>(
+            [&](int k) { return lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2); },
+            cf);
         uint32_t mb[8];
-        if (sg == tau) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s0 = 32 * sg + 8 * q + 4 * g;
-                const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
-                const float us[4] = {u4.x, u4.y, u4.z, u4.w};
-                float m[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    m[e] = gt[4 * q + e] * fexp2(lam_t - us[e]);
-                    m[e] = (s0 + e <= t) ? m[e] : 0.0f;
-                }
-                mb[2 * q] = bf16_pack(m[0], m[1]);
-                mb[2 * q + 1] = bf16_pack(m[2], m[3]);
-            }
-        } else {
-            const float alpha = fexp2(lam_t - lam[32 * sg + 31]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s0 = 32 * sg + 8 * q + 4 * g;
-                const float4 b4 = *reinterpret_cast<const float4 *>(bt + s0);
-                mb[2 * q] = bf16_pack((gt[4 * q] * alpha) * b4.x, (gt[4 * q + 1] * alpha) * b4.y);
-                mb[2 * q + 1] =
-                    bf16_pack((gt[4 * q + 2] * alpha) * b4.z, (gt[4 * q + 3] * alpha) * b4.w);
-            }
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 bv = {mb[4 * half], mb[4 * half + 1], mb[4 * half + 2], mb[4 * half + 3]};
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
-            const int r0 = 32 * sg + 16 * half + 4 * g;
-#pragma unroll
-            for (int pt = PT0; pt < PT1; ++pt) {
-                const int c16 = 32 * pt + 16 * ((lane >> 4) & 1);
-                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.X, L.XS, r0, r0 + 8, c16));
-                acc[pt] = mfma(aop, bop, acc[pt]);
-            }
-        }
+        if (sg == tau)
+            m_diag(gt, lam_t, uu, 32 * sg, t, mb);
+        else
+            m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb);
+        mx_accumulate<PT0, PT1>(mb, lds, L.X, L.XS, 32 * sg, acc);
     }
 }
 
@@ -220,6 +270,35 @@ struct StateTiles {
     }
 };
 
+// bf16 hi + lo split of the chunk-state token operand w_s x_s[p] for the 8
+// rows s a lane holds (xv: raw bf16 x, ws: the rows' state weights).
+__device__ __forceinline__ void split_wx(const i16x8 &xv, const float (&ws)[8], bf16x8 &bhi,
+                                         bf16x8 &blo) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = bf16_float((uint16_t)xv[j]) * ws[j];
+    u32x4 hv, lv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h2 = bf16_pack(v[2 * j], v[2 * j + 1]);
+        hv[j] = h2;
+        const float lo0 = v[2 * j] - bf16_float(h2 & 0xffff);
+        const float lo1 = v[2 * j + 1] - bf16_float(h2 >> 16);
+        lv[j] = bf16_pack(lo0, lo1);
+    }
+    bhi = __builtin_bit_cast(bf16x8, hv);
+    blo = __builtin_bit_cast(bf16x8, lv);
+}
+
+// One K = 16 step of a chunk-state tile: S^T += B^T (w x) as hi then lo.
+__device__ __forceinline__ void state_step(const bf16x8 &aop, const bf16x8 &bhi, const bf16x8 &blo,
+                                           f32x16 &acc) {
+    acc = mfma(aop, bhi, acc);
+    acc = mfma(aop, blo, acc);
+}
+
 template <int P, int N, int NW>
 __device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds, const MLayout &L,
                                                 f32x16 (&acc)[StateTiles<P, N, NW>::per_wave]) {
@@ -232,61 +311,31 @@ __device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds,
         return;
     for (int k = k0; k < k1; ++k) {
         const int r0 = 16 * k + 8 * g;
-        // split token operand w_s x_s[p] for p-tile pt0 (shared by the
-        // wave's tiles when they are paired)
-        const int c16p = 32 * pt0 + 16 * ((lane >> 4) & 1);
-        const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16p);
+        // split token operand for p-tile pt0 (shared by the wave's tiles
+        // when they are paired)
+        const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt0 + 16 * ((lane >> 4) & 1));
         const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
         const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
         const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float v[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = bf16_float((uint16_t)xv[j]) * ws[j];
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 hv, lv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t h2 = bf16_pack(v[2 * j], v[2 * j + 1]);
-            hv[j] = h2;
-            lo[2 * j] = v[2 * j] - bf16_float(h2 & 0xffff);
-            lo[2 * j + 1] = v[2 * j + 1] - bf16_float(h2 >> 16);
-            lv[j] = bf16_pack(lo[2 * j], lo[2 * j + 1]);
-        }
-        const bf16x8 bhi = __builtin_bit_cast(bf16x8, hv);
-        const bf16x8 blo = __builtin_bit_cast(bf16x8, lv);
+        bf16x8 bhi, blo;
+        split_wx(xv, ws, bhi, blo);
 #pragma unroll
         for (int i = 0; i < ST::per_wave; ++i) {
             int pt, nt;
             if (!ST::tile(wave, i, pt, nt))
                 continue;
+            const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
             if (!ST::paired && pt != pt0) {
-                // round-robin tiles of another p-tile: split that p-tile
-                const int c16q = 32 * pt + 16 * ((lane >> 4) & 1);
-                const i16x8 xq = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, c16q);
-                float vq[8], lq[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    vq[j] = bf16_float((uint16_t)xq[j]) * ws[j];
-                u32x4 hq, lqv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t h2 = bf16_pack(vq[2 * j], vq[2 * j + 1]);
-                    hq[j] = h2;
-                    lq[2 * j] = vq[2 * j] - bf16_float(h2 & 0xffff);
-                    lq[2 * j + 1] = vq[2 * j + 1] - bf16_float(h2 >> 16);
-                    lqv[j] = bf16_pack(lq[2 * j], lq[2 * j + 1]);
-                }
-                const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
+                // round-robin tile of another p-tile: split that p-tile
+                bf16x8 qhi, qlo;
+                split_wx(lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt + 16 * ((lane >> 4) & 1)),
+                         ws, qhi, qlo);
                 const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
-                acc[i] = mfma(aop, __builtin_bit_cast(bf16x8, hq), acc[i]);
-                acc[i] = mfma(aop, __builtin_bit_cast(bf16x8, lqv), acc[i]);
+                state_step(aop, qhi, qlo, acc[i]);
                 continue;
             }
-            const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
             const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
-            acc[i] = mfma(aop, bhi, acc[i]);
-            acc[i] = mfma(aop, blo, acc[i]);
+            state_step(aop, bhi, blo, acc[i]);
         }
     }
 }
@@ -359,6 +408,17 @@ __device__ __forceinline__ void state_to_lds(char *lds, const MLayout &L,
     }
 }
 
+// S_bf (the LDS bf16 copy of the state, made by state_to_lds) -> the cache's
+// bf16 state copy ([N/16][P][16]), by the whole workgroup.
+template <int P, int N>
+__device__ __forceinline__ void state_bf_from_lds(uint16_t *gbf, const char *lds, const MLayout &L) {
+    for (int e = threadIdx.x; e < P * N / 8; e += blockDim.x) {
+        const int half = e & 1, p = (e >> 1) % P, kk = (e >> 1) / P;
+        *reinterpret_cast<uint4 *>(gbf + 8 * (int64_t)e) =
+            *reinterpret_cast<const uint4 *>(lds + L.S + (p * L.SS + 16 * kk + 8 * half) * 2);
+    }
+}
+
 // Chunk positions: [0, nb) from the slot buffer, [nb, n_valid) from the
 // packed input starting at token tok_base; later rows are zero.
 template <class DT>
@@ -373,61 +433,6 @@ struct MView {
     int h, g, H, G;
     __device__ int64_t token(int j) const { return tok_base + (j - nb); }
 };
-
-// Stage X and B rows [0, rows) of the chunk into LDS (zeros past n_valid),
-// and delta / lam / exp(lam) / state weights.
-// A2_h = A[h] log2(e): the cumulative sums are kept in log2 units.
-template <int P, int N, class DT>
-__device__ void stage_chunk(const MView<DT> &v, int rows, float A2_h, float bias, int softplus,
-                            bool weights, char *lds, const MLayout &L) {
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
-    for (int e = tid; e < rows * XC; e += nthr) {
-        const int j = e / XC, q = e % XC;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (j < v.n_valid) {
-            const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
-                                           : v.x + (v.token(j) * v.H + v.h) * P;
-            val = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
-        *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) = val;
-    }
-    for (int e = tid; e < rows * BC; e += nthr) {
-        const int j = e / BC, q = e % BC;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (j < v.n_valid) {
-            const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
-                                           : v.B + (v.token(j) * v.G + v.g) * N;
-            val = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
-        *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) = val;
-    }
-    float *lam = reinterpret_cast<float *>(lds + L.lam);
-    float *uu = reinterpret_cast<float *>(lds + L.u);
-    float *el = reinterpret_cast<float *>(lds + L.el);
-    float *w = reinterpret_cast<float *>(lds + L.w);
-    const int j = tid;
-    float d = 0.0f, a = 0.0f;
-    if (j < v.n_valid) {
-        const float raw = j < v.nb ? DT::ld(v.bdt, (int64_t)j * v.H + v.h)
-                                   : DT::ld(v.dt, v.token(j) * v.H + v.h);
-        d = delta_of(raw, bias, softplus);
-        a = d * A2_h;
-    }
-    // threads past the chunk (j >= kMaxQ) scan zeros and store nothing
-    const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
-    if (j < kMaxQ) {
-        lam[j] = l;
-        uu[j] = l - flog2(d);   // +inf where delta is 0: its weights are exactly 0
-        el[j] = fexp2(l);
-    }
-    __syncthreads();
-    if (j < kMaxQ) {
-        reinterpret_cast<float *>(lds + L.beta)[j] = fexp2(lam[j | 31] - uu[j]);
-        if (weights)
-            w[j] = fexp2(lam[v.n_valid - 1] - l) * d;
-    }
-}
 
 // Register-staged copy of a chunk's X / B rows and raw dt, loaded one chunk
 // ahead by the prefill workgroup (NT threads) so the global-load latency
@@ -665,6 +670,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
                                               : nullptr);
+    uint16_t *bnd_bf = a.replay ? static_cast<uint16_t *>(a.cache_state_bf) +
+                                      ((int64_t)slot * H + h) * PN
+                                : nullptr;
     const bool write_bnd = bnd && (!a.replay || nfull > 0);
     uint16_t *y = static_cast<uint16_t *>(a.y);
     const int tau = wave_tblock(Qp / 32, wave);
@@ -680,12 +688,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
         load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
     }
     for (int c = 0; c < nchunks; ++c) {
+        const bool mirror = c == nfull && write_bnd && bnd_bf;
         if (c == nfull && write_bnd)
             state_io<P, N, NW, false>(bnd, S);
         set_chunk(c);
         const int n_valid = v.n_valid;
         const bool upd = n_valid == Q || (!a.replay && a.final_state);
-        __syncthreads();  // previous chunk's LDS reads are done
+        __syncthreads();  // previous chunk's LDS reads (and S_bf writes) are done
+        if (mirror)  // S_bf in LDS is the bf16 copy of the state just stored
+            state_bf_from_lds<P, N>(bnd_bf, lds, L);
         store_chunk_regs<P, N, 64 * NW>(regs, Qp, n_valid, A2_h, bias, d.softplus, upd, lds, L);
         __syncthreads();
         const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, n_valid);
@@ -712,104 +723,358 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
             state_to_lds<P, N, NW>(lds, L, S);
         }
     }
-    if (nfull == nchunks && write_bnd)
+    if (nfull == nchunks && write_bnd) {
         state_io<P, N, NW, false>(bnd, S);
+        if (bnd_bf) {
+            __syncthreads();
+            state_bf_from_lds<P, N>(bnd_bf, lds, L);
+        }
+    }
     if (!a.replay && a.final_state)
         state_io<P, N, NW, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
 }
 
+// ---------------------------------------------------------------------------
+// Exact-replay decode. One single-wave workgroup per (slot, head). The wave computes the one output row k = buf_len of
+// the t-block that holds it, with the prefill's operands and MFMA order:
+//   - the read-out operand S_bf comes from the cache's bf16 state copy, the
+//     bf16 rounding the prefill applies to the same fp32 state;
+//   - C . B^T and the weights are built for column k % 32 only (the other
+//     columns of C are zero, their weights are selected to zero): an MFMA
+//     output element depends only on its own row and column;
+//   - the buffer's B rows are A operands read straight from global memory;
+//     the X rows of each s-block pass through a small per-wave LDS tile for
+//     the transposed read; rows after k are zero;
+//   - the in-chunk scan is the prefill's block scan, one 64-row segment at a
+//     time (wave_scan_segments).
+// When the token fills the chunk the wave also runs the chunk-state update
+// of its head (per 16-row K step, staged through the same LDS tile) and
+// writes the new fp32 state and its bf16 copy. The last workgroup of a slot
+// to finish advances buf_len / boundary_pos (arrivals counter).
+constexpr int kDecodeWaves = 1;
+
+// Per-wave LDS of the decode kernel, in bytes.
+struct DLayout {
+    int XS, BS;
+    int lam, u, beta, w, X, B, bytes;
+    __host__ __device__ DLayout(int Qp, int P, int N) {
+        XS = P + kPad;
+        BS = N + kPad;
+        int o = 0;
+        lam = o;  o += Qp * 4;
+        u = o;    o += Qp * 4;
+        beta = o; o += Qp * 4;
+        w = o;    o += Qp * 4;
+        X = o;    o += 32 * XS * 2;   // 32 rows of x (16 in the state update)
+        B = o;    o += 16 * BS * 2;   // 16 rows of B (state update)
+        bytes = (o + 15) & ~15;
+    }
+};
+
 template <int P, int N, class DT>
-__global__ __launch_bounds__(kBlock) void k_decode_mfma(DecodeArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot, int h, int k,
+                                            char *lds, const DLayout &L) {
     using TD = typename DT::T;
+    constexpr int NPT = P / 32, NK = N / 16;
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
-    const int b = blockIdx.x / H, h = blockIdx.x % H;
-    const int hpg = H / G, g = h / hpg;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    constexpr int PN = P * N;
-    const MLayout L(Qp, P, N);
+    const int g = h / (H / G);
+    const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
+    const int tau = k >> 5;
+    const bool commit = k + 1 == Q;
+    const bool col = c == (k & 31);   // lanes of output column k % 32
+    const int64_t PN = (int64_t)P * N;
+    const int64_t hoff = ((int64_t)slot * H + h) * PN;
+    const uint16_t *sbf = static_cast<const uint16_t *>(a.cache_state_bf) + hoff;
+    const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
+    const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
+    const uint16_t *Cin = static_cast<const uint16_t *>(a.C) + ((int64_t)b * G + g) * N;
+    const TD *dtin = static_cast<const TD *>(a.dt) + (int64_t)b * H + h;
+    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *bt = reinterpret_cast<float *>(lds + L.beta);
+
+    // Every load that does not depend on earlier results is issued first:
+    // the token (for y and the append), raw dt of rows 0..k, C_k, S_bf.
+    const int nseg_max = commit ? (Qp + 63) >> 6 : ((32 * (tau + 1)) + 63) >> 6;
+    TD rawdt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        rawdt[i] = j < k ? bdt[(int64_t)j * H + h] : dtin[0];
+    }
+    uint4 xtok = make_uint4(0, 0, 0, 0), btok = make_uint4(0, 0, 0, 0);
+    if (lane < P / 8)
+        xtok = *reinterpret_cast<const uint4 *>(xin + 8 * lane);
+    if (lane < N / 8)
+        btok = *reinterpret_cast<const uint4 *>(Bin + 8 * lane);
+    bf16x8 cf[NK];
+    {
+        uint4 raw[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            raw[kk] = *reinterpret_cast<const uint4 *>(Cin + 16 * kk + 8 * gl);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            cf[kk] = __builtin_bit_cast(bf16x8, keep_if(col, raw[kk]));
+    }
+    // read-out C . S_bf (operand (pt, kk) is 1 KiB contiguous in the copy)
+    f32x16 acc[NPT];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+        acc[pt] = readout_raw<N>(
+            [&](int kk) {
+                return *reinterpret_cast<const bf16x8 *>(sbf + ((int64_t)kk * P + 32 * pt + c) * 16 +
+                                                         8 * gl);
+            },
+            cf);
+
+    // delta and the in-chunk cumulative sum (log2 units) over rows j = lane + 64 i
+    const float A2 = a.A[h] * kLog2e;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const int nseg = nseg_max;
+    float dv[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        float dd = 0.0f, aa = 0.0f;
+        if (i < nseg && j <= k) {
+            dd = delta_of(DT::val(rawdt[i]), bias, d.softplus);
+            aa = dd * A2;
+        }
+        dv[i] = dd;
+        lv[i] = aa;
+    }
+    wave_scan_segments(lv, nseg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const float lend = __shfl(lv[i], lane | 31, 64);   // lam[j | 31]
+        if (i < nseg && j < Qp) {
+            const float l = lv[i];
+            const float u = l - flog2(dv[i]);  // +inf where delta is 0
+            lam[j] = l;
+            uu[j] = u;
+            bt[j] = fexp2(lend - u);
+        }
+    }
+    const float lam_k = lam[k];
+    const float el_k = fexp2(lam_k);
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+        acc[pt] = readout_scale(acc[pt], el_k);
+
+    // s-blocks 0..tau: G^T, weights of column k % 32, M.X
+    constexpr int XPL = P / 16;  // 16-byte pieces of a 32-row x block per lane
+    for (int sg = 0; sg <= tau; ++sg) {
+        const int s = 32 * sg + c;
+        const uint16_t *brow = s < k ? bB + ((int64_t)s * G + g) * N : Bin;
+        uint4 braw[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            braw[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
+        uint4 xraw[XPL];
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+            const int row = 32 * sg + r;
+            const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
+            xraw[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+        const f32x16 gt = gram_block<N>(
+            [&](int kk) { return __builtin_bit_cast(bf16x8, keep_if(s <= k, braw[kk])); }, cf);
+        uint32_t mb[8];
+        if (sg == tau)
+            m_diag(gt, lam_k, uu, 32 * sg, k, mb);
+        else
+            m_off(gt, fexp2(lam_k - lam[32 * sg + 31]), bt, 32 * sg, mb);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            mb[q] = col ? mb[q] : 0u;
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+            *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
+                keep_if(32 * sg + r <= k, xraw[i]);
+        }
+        mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc);
+    }
+
+    // y row k: fmaf(D, x, Y^T) -> bf16, -0 -> +0 (lanes of column k % 32);
+    // x_k is row k - 32 tau of the last x tile
+    if (col) {
+        const float D_h = a.D ? a.D[h] : 0.0f;
+        uint16_t *yrow = static_cast<uint16_t *>(a.y) + ((int64_t)b * H + h) * P;
+        const char *xk = lds + L.X + (k - 32 * tau) * L.XS * 2;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int p = 32 * pt + 8 * q + 4 * gl;
+                const uint2 xr = *reinterpret_cast<const uint2 *>(xk + 2 * p);
+                const float xs[4] = {bf16_float(xr.x & 0xffff), bf16_float(xr.x >> 16),
+                                     bf16_float(xr.y & 0xffff), bf16_float(xr.y >> 16)};
+                uint16_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float yv = fmaf(D_h, xs[e], acc[pt][4 * q + e]);
+                    yv = yv + 0.0f;
+                    o[e] = bf16_bits(yv);
+                }
+                *reinterpret_cast<uint2 *>(yrow + p) =
+                    make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+            }
+        }
+    }
+
+    // append the token at buffer position k (this step reads positions < k)
+    if (lane < P / 8)
+        *reinterpret_cast<uint4 *>(bx + ((int64_t)k * H + h) * P + 8 * lane) = xtok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == k)
+            bdt[(int64_t)k * H + h] = rawdt[i];
+    if (h % (H / G) == 0 && lane < N / 8) {
+        *reinterpret_cast<uint4 *>(bB + ((int64_t)k * G + g) * N + 8 * lane) = btok;
+        if (a.buf_C) {
+            uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
+            *reinterpret_cast<uint4 *>(bC + ((int64_t)k * G + g) * N + 8 * lane) =
+                *reinterpret_cast<const uint4 *>(Cin + 8 * lane);
+        }
+    }
+    if (!commit)
+        return;
+
+    // chunk-state update S <- 2^(l_last) S + sum_s B_s (w_s x_s), as in the
+    // prefill (tiles of 32 x 32, K = 16 rows ascending, hi then lo)
+    float *w = reinterpret_cast<float *>(lds + L.w);
+    const float l_last = lam[Q - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        if (i < nseg && j < Qp)
+            w[j] = fexp2(l_last - lv[i]) * dv[i];
+    }
+    const float dec = fexp2(l_last);
+    constexpr int NT = NPT * (N / 32);
+    constexpr int TPP = NT < 4 ? NT : 4;            // tiles per pass
+    constexpr int XP16 = P / 32, BP16 = N / 32;     // 16-byte pieces per lane, 16 rows
+    float *st = a.cache_state + hoff;
+    uint16_t *stbf = static_cast<uint16_t *>(a.cache_state_bf) + hoff;
+    for (int pass = 0; pass < NT / TPP; ++pass) {
+        f32x16 S[TPP];
+#pragma unroll
+        for (int i = 0; i < TPP; ++i) {
+            const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
+            const int p = 32 * pt + c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 32 * nt + 8 * q + 4 * gl;
+                const float4 v = *reinterpret_cast<const float4 *>(st + (int64_t)p * N + n);
+                S[i][4 * q + 0] = v.x;
+                S[i][4 * q + 1] = v.y;
+                S[i][4 * q + 2] = v.z;
+                S[i][4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                S[i][r] = S[i][r] * dec;
+        }
+        for (int ks = 0; ks < Qp / 16; ++ks) {
+            // rows 16 ks .. +15 of the chunk: buffer below k, the token at k,
+            // zeros past the chunk
+#pragma unroll
+            for (int i = 0; i < XP16; ++i) {
+                const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+                const int row = 16 * ks + r;
+                const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
+                *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
+                    keep_if(row <= k, *reinterpret_cast<const uint4 *>(src + 8 * q));
+            }
+#pragma unroll
+            for (int i = 0; i < BP16; ++i) {
+                const int e = lane + 64 * i, r = e / (N / 8), q = e % (N / 8);
+                const int row = 16 * ks + r;
+                const uint16_t *src = row < k ? bB + ((int64_t)row * G + g) * N : Bin;
+                *reinterpret_cast<uint4 *>(lds + L.B + (r * L.BS + 8 * q) * 2) =
+                    keep_if(row <= k, *reinterpret_cast<const uint4 *>(src + 8 * q));
+            }
+            const int r0 = 16 * ks + 8 * gl;
+            const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
+            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            bf16x8 bhi[NPT], blo[NPT];
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt)
+                split_wx(lds_tr8(lds, L.X, L.XS, 8 * gl, 8 * gl + 4,
+                                 32 * pt + 16 * ((lane >> 4) & 1)),
+                         ws, bhi[pt], blo[pt]);
+#pragma unroll
+            for (int i = 0; i < TPP; ++i) {
+                const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
+                const bf16x8 aop = as_bf16x8(
+                    lds_tr8(lds, L.B, L.BS, 8 * gl, 8 * gl + 4, 32 * nt + 16 * ((lane >> 4) & 1)));
+                state_step(aop, bhi[pt], blo[pt], S[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TPP; ++i) {
+            const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
+            const int p = 32 * pt + c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 32 * nt + 8 * q + 4 * gl;
+                *reinterpret_cast<float4 *>(st + (int64_t)p * N + n) =
+                    make_float4(S[i][4 * q], S[i][4 * q + 1], S[i][4 * q + 2], S[i][4 * q + 3]);
+                *reinterpret_cast<uint2 *>(stbf + state_bf_index(p, n, P)) = make_uint2(
+                    bf16_bits(S[i][4 * q]) | ((uint32_t)bf16_bits(S[i][4 * q + 1]) << 16),
+                    bf16_bits(S[i][4 * q + 2]) | ((uint32_t)bf16_bits(S[i][4 * q + 3]) << 16));
+            }
+        }
+    }
+}
+
+template <int P, int N, class DT>
+__global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_mfma(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds_all[];
+    const int H = a.d.H, Q = a.d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int HQ = (H + kDecodeWaves - 1) / kDecodeWaves;
+    // the workgroups of one slot run on one XCD (they share its B rows)
+    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
+    const int b = wid / HQ;
+    const int wave = threadIdx.x >> 6;
+    const int h = (wid % HQ) * kDecodeWaves + wave;
+    const DLayout L(Qp, P, N);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0 || slot >= a.num_slots)
         return;
     const int k = a.buf_len[slot];
     if (k < 0 || k >= Q)
         return;
-    const bool commit = k + 1 == Q;
-    float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
-
-    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
-    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
-
-    MView<DT> v;
-    v.x = static_cast<const uint16_t *>(a.x);
-    v.B = static_cast<const uint16_t *>(a.B);
-    v.C = static_cast<const uint16_t *>(a.C);
-    v.dt = static_cast<const TD *>(a.dt);
-    v.bx = bx; v.bB = bB; v.bdt = bdt;
-    v.h = h; v.g = g; v.H = H; v.G = G;
-    v.tok_base = b;
-    v.nb = k;
-    v.n_valid = k + 1;
-
-    const int tau = k >> 5;
-    const int rows = commit ? Qp : 32 * (tau + 1);
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    // S_bf from the fp32 boundary state
-    for (int e = tid; e < PN / 4; e += kBlock) {
-        const int p = (4 * e) / N, n = (4 * e) % N;
-        const float4 sv = reinterpret_cast<const float4 *>(st)[e];
-        const uint32_t lo = bf16_bits(sv.x) | ((uint32_t)bf16_bits(sv.y) << 16);
-        const uint32_t hi = bf16_bits(sv.z) | ((uint32_t)bf16_bits(sv.w) << 16);
-        *reinterpret_cast<uint2 *>(lds + L.S + (p * L.SS + n) * 2) = make_uint2(lo, hi);
-    }
-    stage_chunk<P, N, DT>(v, rows, a.A[h] * kLog2e, bias, d.softplus, commit, lds, L);
+    if (h < H)
+        decode_head<P, N, DT>(a, b, slot, h, k, lds_all + wave * L.bytes, L);
+    // (with one wave per workgroup the barrier below is a no-op)
+    // Every wave of this workgroup has read buf_len (and used it) by now; the
+    // slot's last workgroup to arrive advances it. The counter needs only
+    // atomicity, no ordering: no workgroup reads what the last one writes
+    // during this launch, and the launch boundary publishes the writes. (An
+    // acquire/release atomic here would write back and invalidate the L2 in
+    // every workgroup.)
     __syncthreads();
-
-    // one wave per 32-column p-tile of the output row
-    if (wave < P / 32) {
-        bf16x8 cf[N / 16];
-        load_cfrag<N, DT>(v, tau, k, cf);
-        f32x16 acc[P / 32];
-        const float D_h = a.D ? a.D[h] : 0.0f;
-        uint16_t *y = static_cast<uint16_t *>(a.y);
-        if (wave == 0) {
-            tblock_output<P, N, 0, 1>(tau, cf, lds, L, acc);
-            emit_tblock<P, 0, 1>(v, tau, k, k + 1, D_h, lds, L, acc, y);
-        } else if (P / 32 > 1 && wave == 1) {
-            tblock_output<P, N, (P / 32 > 1 ? 1 : 0), (P / 32 > 1 ? 2 : 1)>(tau, cf, lds, L, acc);
-            emit_tblock<P, (P / 32 > 1 ? 1 : 0), (P / 32 > 1 ? 2 : 1)>(v, tau, k, k + 1, D_h, lds,
-                                                                          L, acc, y);
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(a.arrivals + slot, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == HQ - 1) {
+            __hip_atomic_store(a.arrivals + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.buf_len[slot] = k + 1 == Q ? 0 : k + 1;
+            if (k + 1 == Q)
+                a.boundary_pos[slot] += Q;
         }
-    }
-
-    // append the new token at buffer position k (reads above used LDS or
-    // positions < k of the buffer)
-    const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
-    for (int p = tid; p < P; p += kBlock)
-        bx[((int64_t)k * H + h) * P + p] = xin[p];
-    if (tid == 0)
-        bdt[(int64_t)k * H + h] = static_cast<const TD *>(a.dt)[(int64_t)b * H + h];
-    if (h % hpg == 0) {
-        const uint16_t *bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
-        for (int n = tid; n < N; n += kBlock)
-            bB[((int64_t)k * G + g) * N + n] = bin[n];
-        if (a.buf_C) {
-            uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
-            const uint16_t *cin = static_cast<const uint16_t *>(a.C) + ((int64_t)b * G + g) * N;
-            for (int n = tid; n < N; n += kBlock)
-                bC[((int64_t)k * G + g) * N + n] = cin[n];
-        }
-    }
-    if (commit) {
-        constexpr int NW = kBlock / 64;
-        f32x16 S[StateTiles<P, N, NW>::per_wave];
-        state_io<P, N, NW, true>(st, S);
-        chunk_state_update<P, N, NW>(Qp, Q, lds, L, S);
-        __syncthreads();  // every wave has read the old state
-        state_io<P, N, NW, false>(st, S);
     }
 }
 
@@ -833,11 +1098,12 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
 template <int P, int N, class DT>
 hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
-    const MLayout L(Qp, P, N);
-    hipError_t e = set_lds(k_decode_mfma<P, N, DT>, L.bytes);
+    const size_t bytes = (size_t)DLayout(Qp, P, N).bytes * kDecodeWaves;
+    hipError_t e = set_lds(k_decode_mfma<P, N, DT>, bytes);
     if (e != hipSuccess)
         return e;
-    k_decode_mfma<P, N, DT><<<dim3(a.d.H * a.batch), dim3(kBlock), L.bytes, stream>>>(a);
+    const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
+    k_decode_mfma<P, N, DT><<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -870,14 +1136,7 @@ bool mfma_supported(const Dims &d) {
 hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream) { SSD_PN_SWITCH(scan_pn, a, stream) }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
-    hipError_t e;
-    {
-        auto run = [&]() -> hipError_t { SSD_PN_SWITCH(decode_pn, a, stream) };
-        e = run();
-    }
-    if (e != hipSuccess)
-        return e;
-    return launch_decode_advance(a, stream);
+    SSD_PN_SWITCH(decode_pn, a, stream)
 }
 
 }  // namespace ssd

@@ -238,11 +238,16 @@ __device__ void state_load(float *S, const float *src, int P, int N) {
     __syncthreads();
 }
 
-__device__ void state_store(float *dst, const float *S, int P, int N) {
+// fp32 state out of LDS; with dst_bf, also its bf16 copy (nearest even)
+__device__ void state_store(float *dst, const float *S, int P, int N,
+                            uint16_t *dst_bf = nullptr) {
     const int N1 = N + 1;
     for (int e = threadIdx.x; e < P * N; e += kBlock) {
         const int p = e / N, n = e % N;
-        dst[e] = S[p * N1 + n];
+        const float v = S[p * N1 + n];
+        dst[e] = v;
+        if (dst_bf)
+            dst_bf[state_bf_index(p, n, P)] = bf16_rne(v);
     }
 }
 
@@ -293,12 +298,15 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
     float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
                                               : nullptr);
+    uint16_t *bnd_bf = a.replay ? static_cast<uint16_t *>(a.cache_state_bf) +
+                                      ((int64_t)slot * H + h) * PN
+                                : nullptr;
     const bool write_bnd = bnd && (!a.replay || nfull > 0);
     T *y = static_cast<T *>(a.y);
 
     for (int c = 0; c < nchunks; ++c) {
         if (c == nfull && write_bnd)
-            state_store(bnd, lds + L.S, P, N);
+            state_store(bnd, lds + L.S, P, N, bnd_bf);
         v.nb = (c == 0) ? nbuf : 0;
         v.n_valid = min(Q, total - c * Q);
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
             chunk_state_update(v, lds, L);
     }
     if (nfull == nchunks && write_bnd)
-        state_store(bnd, lds + L.S, P, N);
+        state_store(bnd, lds + L.S, P, N, bnd_bf);
     if (!a.replay && a.final_state)
         state_store(a.final_state + ((int64_t)s * H + h) * PN, lds + L.S, P, N);
 }
@@ -377,7 +385,8 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
     }
     if (k + 1 == Q) {
         chunk_state_update(v, lds, L);
-        state_store(st, lds + L.S, P, N);
+        state_store(st, lds + L.S, P, N,
+                    static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN);
     }
 }
 
@@ -403,19 +412,40 @@ __global__ void k_decode_advance(int batch, const int32_t *slot_idx, int32_t *bu
 }
 
 // Trailing partial chunk -> slot buffers; buf_len / boundary_pos update;
-// optional boundary-state copy. One workgroup per sequence.
+// optional boundary-state copy. Workgroup (s, 0) handles sequence s's buffer
+// and metadata; workgroup (s, 1 + h) copies head h of its boundary state
+// (and writes the bf16 copy) when state_src is given.
 template <class IO, class DT>
 __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     using T = typename IO::T;
     using TD = typename DT::T;
     const Dims d = a.d;
-    const int s = blockIdx.x, tid = threadIdx.x;
+    const int s = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
     const int H = d.H, G = d.G, P = d.P, N = d.N, Q = d.Q;
     const int slot = a.slot_idx ? a.slot_idx[s] : s;
     const int64_t t0 = a.cu[s];
     const int len = a.cu[s + 1] - a.cu[s];
     if ((!a.fresh && len == 0) || slot < 0 || slot >= a.num_slots)
         return;
+    if (part > 0) {
+        if (!a.state_src)
+            return;
+        const int h = part - 1;
+        const int64_t PN = (int64_t)P * N;
+        const float4 *src =
+            reinterpret_cast<const float4 *>(a.state_src + ((int64_t)s * H + h) * PN);
+        float4 *dst = reinterpret_cast<float4 *>(a.cache_state + ((int64_t)slot * H + h) * PN);
+        uint16_t *dbf = static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN;
+        for (int64_t e = tid; e < PN / 4; e += kBlock) {
+            const float4 v = src[e];
+            dst[e] = v;
+            const int p = (int)((4 * e) / N), n = (int)((4 * e) % N);
+            *reinterpret_cast<uint2 *>(dbf + state_bf_index(p, n, P)) =
+                make_uint2(bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
+                           bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
+        }
+        return;
+    }
     const int nbuf = a.fresh ? 0 : a.buf_len[slot];
     if (nbuf < 0 || nbuf >= Q)
         return;
@@ -445,17 +475,25 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
         for (int64_t e = tid; e < ntok * GN; e += kBlock)
             bC[dst0 * GN + e] = C[(t0 + src0) * GN + e];
     }
-    if (a.state_src) {
-        const int64_t HPN = HP * N;
-        const float *src = a.state_src + (int64_t)s * HPN;
-        float *dst = a.cache_state + (int64_t)slot * HPN;
-        for (int64_t e = tid; e < HPN; e += kBlock)
-            dst[e] = src[e];
-    }
     __syncthreads();
     if (tid == 0) {
         a.buf_len[slot] = nfull == 0 ? total : tail;
         a.boundary_pos[slot] = (a.fresh ? 0 : a.boundary_pos[slot]) + (int64_t)nfull * Q;
+    }
+}
+
+// bf16 copy of the whole cache state (one workgroup per slot and head).
+__global__ __launch_bounds__(kBlock) void k_refresh_state_bf(const float *state, uint16_t *state_bf,
+                                                             int P, int N) {
+    const int64_t PN = (int64_t)P * N;
+    const float4 *src = reinterpret_cast<const float4 *>(state + blockIdx.x * PN);
+    uint16_t *dst = state_bf + blockIdx.x * PN;
+    for (int64_t e = threadIdx.x; e < PN / 4; e += kBlock) {
+        const float4 v = src[e];
+        const int p = (int)((4 * e) / N), n = (int)((4 * e) % N);
+        *reinterpret_cast<uint2 *>(dst + state_bf_index(p, n, P)) =
+            make_uint2(bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
+                       bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
     }
 }
 
@@ -550,7 +588,7 @@ hipError_t decode_impl(const DecodeArgs &a, hipStream_t stream) {
 
 template <class IO, class DT>
 hipError_t commit_impl(const CommitArgs &a, hipStream_t stream) {
-    k_commit<IO, DT><<<dim3(a.S), dim3(kBlock), 0, stream>>>(a);
+    k_commit<IO, DT><<<dim3(a.S, a.state_src ? 1 + a.d.H : 1), dim3(kBlock), 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -583,5 +621,13 @@ hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return dispatch<DecodeF>(a, stream); }
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream) { return dispatch<CommitF>(a, stream); }
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream) { return dispatch<SsuF>(a, stream); }
+hipError_t launch_refresh_state_bf(const float *state, void *state_bf, int64_t heads, int P, int N,
+                                   hipStream_t stream) {
+    if (heads <= 0)
+        return hipSuccess;
+    k_refresh_state_bf<<<dim3((unsigned)heads), dim3(kBlock), 0, stream>>>(
+        state, static_cast<uint16_t *>(state_bf), P, N);
+    return hipGetLastError();
+}
 
 }  // namespace ssd

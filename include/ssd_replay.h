@@ -19,7 +19,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless their name ends in _host. Arrays are
- *    row-major and contiguous with the layouts given below.
+ *    row-major and contiguous with the layouts given below. x, B, C, y, every
+ *    state array and the x/B/C buffers must be 16-byte aligned (the kernels
+ *    move them in 16-byte pieces); other arrays need their natural alignment.
  *  - T = packed token count, S = number of sequences, Q = chunk_size.
  *    x, y: [T,H,P]; dt: [T,H] (raw dt); B, C: [T,G,N]; A, D, dt_bias: [H]
  *    fp32; states: [.,H,P,N] fp32; cu_seqlens: [S+1] int32, cu[0] = 0,
@@ -55,7 +57,8 @@ typedef enum {
     SSD_ERR_CHUNK_MISMATCH = -5,  /* [RFC] section 4: one chunk size for prefill and decode */
     SSD_ERR_WORKSPACE = -6,       /* workspace missing or too small */
     SSD_ERR_UNSUPPORTED = -7,     /* P, N or chunk_size outside the built set */
-    SSD_ERR_HIP = -8              /* a HIP launch or runtime call failed */
+    SSD_ERR_HIP = -8,             /* a HIP launch or runtime call failed */
+    SSD_ERR_ALIGN = -9            /* a token, state or buffer array is not 16-byte aligned */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -76,6 +79,16 @@ typedef struct {
  * representation"): the fp32 state at the last multiple of the chunk size
  * plus a token-major buffer of the inputs received since then.
  *   state         [num_slots,H,P,N] fp32   boundary state
+ *   state_bf      [num_slots,H,N/16,P,16]  the boundary state rounded to bf16
+ *                 bf16                     (nearest even), element (p, n) of a
+ *                                          head at (n/16)*16P + 16p + n%16: the
+ *                                          operand of the state read-out, which
+ *                                          rounds the state to bf16 in prefill
+ *                                          too. Written by the library whenever
+ *                                          it writes state; decode reads it
+ *                                          instead of the fp32 state (half the
+ *                                          bytes). A caller that writes state
+ *                                          itself calls ssd_replay_cache_refresh.
  *   buf_x         [num_slots,Q,H,P] io     buffered x
  *   buf_dt        [num_slots,Q,H]   dt     buffered raw dt ([RFC] section 3:
  *                                          raw dt, not softplus(dt + bias))
@@ -84,28 +97,40 @@ typedef struct {
  *   buf_len       [num_slots] int32        tokens buffered, in [0, Q)
  *   boundary_pos  [num_slots] int64        sequence position of the boundary,
  *                                          a multiple of Q
+ *   arrivals      [num_slots] int32        decode bookkeeping: the workgroups
+ *                                          of a slot count themselves in and
+ *                                          the last one advances buf_len; zero
+ *                                          between calls
  * A fresh slot is all zeros. The struct itself is a host object; the
  * pointers in it are device pointers. */
 typedef struct {
     float *state;
+    void *state_bf;
     void *buf_x;
     void *buf_dt;
     void *buf_B;
     void *buf_C;
     int32_t *buf_len;
     int64_t *boundary_pos;
+    int32_t *arrivals;
     int32_t num_slots;
     int32_t chunk_size;
     int32_t state_dtype;
 } ssd_replay_cache;
 
+/* Rebuild the bf16 state copy (state_bf) of every slot from the fp32 state,
+ * for a caller that wrote cache->state itself. */
+int ssd_replay_cache_refresh(const ssd_shape *shape, const ssd_replay_cache *cache,
+                             hipStream_t stream);
+
 /* Human-readable name of a status code. Never NULL. */
 const char *ssd_status_string(int status);
 
 /* Bytes of device memory one exact-replay cache of num_slots slots needs
- * (state + buffers + metadata), with or without the C buffer; 0 for a bad
- * shape. [RFC] section 4 sizes the buffer at about 1.16 MiB and the fp32
- * state at 1 MiB per layer and sequence for H=32, G=1, P=64, N=128, Q=256. */
+ * (state, its bf16 copy, buffers and metadata), with or without the C
+ * buffer; 0 for a bad shape. [RFC] section 4 sizes the buffer at about
+ * 1.16 MiB and the fp32 state at 1 MiB per layer and sequence for H=32, G=1,
+ * P=64, N=128, Q=256; the bf16 copy adds 0.5 MiB. */
 size_t ssd_replay_cache_bytes(const ssd_shape *shape, int32_t num_slots,
                               int32_t with_C);
 

@@ -106,3 +106,11 @@ def split_lengths(T: int, step: int):
         out.append(min(step, T - t))
         t += step
     return out
+
+
+def cache_consistent(cache) -> bool:
+    """The cache's bf16 state copy is the fp32 state rounded to nearest even
+    (torch's float32 -> bfloat16 conversion), and the decode bookkeeping
+    counters are back to zero."""
+    return (same_bits(cache.state_bf_rowmajor(), cache.state.to(torch.bfloat16))
+            and int(cache.arrivals.abs().sum()) == 0)

@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     want = {"ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
-            "ssd_replay_decode", "ssm_state_update"}
+            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -51,7 +51,8 @@ def test_cache_bytes_match_printed_memory():
     sh = erd.Shape(32, 1, 64, 128, 256, "bf16", "f32")
     total = erd.ssd_replay_cache_bytes(sh, 1, with_C=True)
     state = 32 * 64 * 128 * 4
-    buf = total - state - 4 - 8
+    state_bf = 32 * 64 * 128 * 2      # bf16 copy of the state (read-out operand)
+    buf = total - state - state_bf - 4 - 4 - 8
     assert state / 2 ** 20 == g["fp32_state_mib_per_layer_per_seq"]["value"]
     assert round(buf / 2 ** 20, 2) == g["buffer_mib_per_layer_per_seq"]["value"]
     assert erd.ssd_replay_cache_bytes(sh, 27, with_C=True) == 27 * total
@@ -100,11 +101,14 @@ def test_prefill_rejects_bad_seqlens_and_nulls():
     assert prefill(sh, A=None) == -1
     assert prefill(sh, cu_dev=None) == -1
     assert prefill(shape(), cu=(0,), T=0) == 0        # nothing to do, no launch
+    assert prefill(sh, x=ctypes.c_void_p(0x1002)) == -9   # misaligned x
+    assert prefill(sh, y=ctypes.c_void_p(0x1008)) == -9
 
 
 def cache(sh_c, **kw):
-    base = dict(state=0x1000, buf_x=0x1000, buf_dt=0x1000, buf_B=0x1000, buf_C=None,
-                buf_len=0x1000, boundary_pos=0x1000, num_slots=4, chunk_size=16, state_dtype=0)
+    base = dict(state=0x1000, state_bf=0x1000, buf_x=0x1000, buf_dt=0x1000, buf_B=0x1000,
+                buf_C=None, buf_len=0x1000, boundary_pos=0x1000, arrivals=0x1000, num_slots=4,
+                chunk_size=16, state_dtype=0)
     base.update(kw)
     return _lib.ssd_replay_cache(**base)
 
@@ -120,6 +124,14 @@ def test_replay_fails_closed():
     assert decode(sh, cache(sh, state_dtype=1)) == -4        # non-fp32 state
     assert decode(sh, cache(sh, chunk_size=32)) == -5        # chunk mismatch
     assert decode(sh, cache(sh, buf_B=None)) == -1
+    assert decode(sh, cache(sh, state_bf=None)) == -1
+    assert decode(sh, cache(sh, arrivals=None)) == -1
+    assert decode(sh, cache(sh, state_bf=0x1008)) == -9      # misaligned
+    lib = _lib.load()
+    assert lib.ssd_replay_cache_refresh(ctypes.byref(sh), ctypes.byref(cache(sh, state=None)),
+                                        None) == -1
+    assert lib.ssd_replay_cache_refresh(ctypes.byref(sh), ctypes.byref(cache(sh, chunk_size=32)),
+                                        None) == -5
     assert decode(sh, cache(sh, num_slots=0)) == -2
     assert decode(sh, cache(sh), batch=5) == -2              # more rows than slots
     assert decode(shape(state_dtype=1), cache(sh)) == -4

@@ -10,8 +10,8 @@ import torch
 
 import exact_replay_decode_amd as erd
 from exact_replay_decode_amd import synth
-from gpu_cases import (DEV, headwise_max_rel, make_problem, mean_rel_err, same_bits,
-                       y_headwise_max_rel)
+from gpu_cases import (DEV, cache_consistent, headwise_max_rel, make_problem, mean_rel_err,
+                       same_bits, y_headwise_max_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_c0_decode_every_token():
     cache = erd.ReplayCache(pr.shape, 1, DEV, with_C=True)
     yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
     assert same_bits(yd, y)
-    assert same_bits(cache.state[0], bnd[0])
+    assert same_bits(cache.state[0], bnd[0]) and cache_consistent(cache)
     assert int(cache.buf_len[0]) == 0 and int(cache.boundary_pos[0]) == 64
     ref = pr.oracle()
     assert y_headwise_max_rel(yd, ref.y, pr.cu) <= F32_Y_REL
@@ -72,7 +72,7 @@ def test_c1_decode_2048_steps_bitwise(c1):
     cache = erd.ReplayCache(pr.shape, 1, DEV, with_C=True)
     yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
     assert same_bits(yd, y)
-    assert same_bits(cache.state[0], bnd[0])
+    assert same_bits(cache.state[0], bnd[0]) and cache_consistent(cache)
     # the buffer holds the last chunk's tokens, C included
     assert int(cache.buf_len[0]) == 0 and int(cache.boundary_pos[0]) == 2048
     assert same_bits(cache.buf_x[0], x[1792:]) and same_bits(cache.buf_C[0], C[1792:])
@@ -88,6 +88,7 @@ def test_c1_commit_boundary_then_decode(c1):
     cache = erd.ReplayCache(pr.shape, 1, DEV)
     erd.ssd_commit_boundary(pr.shape, cache, [0, 600], x[:600], dt[:600], B[:600], C[:600], b6)
     assert int(cache.buf_len[0]) == 88 and int(cache.boundary_pos[0]) == 512
+    assert cache_consistent(cache)
     yd = decode_tokens(pr.shape, cache, x[600:900], dt[600:900], B[600:900], C[600:900],
                        pr.A, pr.D, pr.bias)
     assert same_bits(torch.cat([y6, yd]), y[:900])
@@ -126,6 +127,45 @@ def test_c1_ssu_differs_in_bits_but_matches_oracle(c1):
     print(f"SSU vs SSD bit-identical elements: {100 * frac_equal:.1f} %")
     ref = pr.oracle()
     assert mean_rel_err(ys, ref.y[:512]) <= BF16_MEAN_REL
+
+
+# ---- grouped heads (C2's shape) and head counts that are not a multiple of
+# the heads per decode workgroup ---------------------------------------------
+
+@pytest.mark.parametrize("H,G,P,N,Q,io", [(64, 8, 64, 128, 256, "bf16"),
+                                           (6, 2, 32, 64, 32, "bf16"),
+                                           (5, 5, 64, 32, 16, "bf16"),
+                                           (3, 1, 32, 128, 64, "bf16")])
+def test_decode_grouped_and_ragged_heads(H, G, P, N, Q, io):
+    lengths = [600, 300, 900, 248] if H == 64 else [300, 77, 129]
+    pr = make_problem(lengths, H=H, G=G, P=P, N=N, Q=Q, io=io, seed=11)
+    x, dt, B, C = pr.dev(None)
+    y, _, bnd = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias)
+    cu = pr.cu
+    S = len(lengths)
+    # replay-prefill a prefix of each sequence, then decode the rest in
+    # batched steps (finished sequences drop out of the batch)
+    pre = np.array([L // 3 + 5 for L in lengths])
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    cache = erd.ReplayCache(pr.shape, S, DEV)
+    y_pre = erd.ssd_replay_prefill(pr.shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip],
+                                   B[ip], C[ip], pr.A, pr.D, pr.bias)
+    assert same_bits(y_pre, y[ip])
+    yd = torch.empty_like(y)
+    for k in range(max(lengths) - int(pre.min())):
+        live = [s for s in range(S) if pre[s] + k < lengths[s]]
+        if not live:
+            break
+        it = torch.tensor([int(cu[s] + pre[s] + k) for s in live], device=DEV)
+        sl = torch.tensor(live, dtype=torch.int32, device=DEV)
+        yd[it] = erd.ssd_replay_decode(pr.shape, cache, x[it], dt[it], B[it], C[it], pr.A,
+                                       pr.D, pr.bias, slot_idx=sl)
+    idec = torch.from_numpy(np.concatenate([np.arange(cu[s] + pre[s], cu[s + 1])
+                                            for s in range(S)])).to(DEV)
+    assert same_bits(yd[idec], y[idec])
+    assert same_bits(cache.state, bnd) and cache_consistent(cache)
+    assert np.array_equal(cache.buf_len.cpu().numpy(), np.array(lengths) % Q)
 
 
 # ---- C3: batched decode, B = 256 ------------------------------------------
@@ -174,7 +214,7 @@ def test_c3_batched_replay_decode_bitwise(Q):
     assert np.all(bp % Q == 0)
     assert np.array_equal(bp, (lengths // Q) * Q)
     assert np.array_equal(cache.buf_len.cpu().numpy(), lengths % Q)
-    assert same_bits(cache.state, bnd)
+    assert same_bits(cache.state, bnd) and cache_consistent(cache)
     # oracle parity on sampled sequences (decode rows and boundary state)
     from oracle import scan
     for s in (0, 131, 255):
@@ -258,7 +298,7 @@ def test_c4_layer_stack():
                            pr.bias)
         rows = (yd.view(torch.int16) != y[600:].view(torch.int16)).flatten(1).any(1)
         assert same_bits(y0, y[:600]) and int(rows.sum()) == 0, layer
-        assert same_bits(cache.state[0], bnd[0])
+        assert same_bits(cache.state[0], bnd[0]) and cache_consistent(cache)
         # chunked prefill at most 100 tokens per call
         c2 = erd.ReplayCache(pr.shape, 1, DEV)
         parts = []
@@ -270,3 +310,22 @@ def test_c4_layer_stack():
         if layer == 0:
             ref = pr.oracle()
             assert mean_rel_err(yd, ref.y[600:]) <= BF16_MEAN_REL
+
+
+def test_cache_refresh_after_direct_state_write():
+    """A caller that writes the fp32 state itself rebuilds the bf16 copy with
+    ssd_replay_cache_refresh; decode then continues from that state exactly
+    as a prefill resumed from it (init_state) does."""
+    pr = make_problem([300], H=8, G=2, P=64, N=64, Q=64, seed=21)
+    x, dt, B, C = pr.dev(None)
+    st0 = torch.randn((1, 8, 64, 64), generator=torch.Generator(device=DEV).manual_seed(5),
+                      device=DEV)
+    y, _, _ = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias,
+                                     init_state=st0)
+    cache = erd.ReplayCache(pr.shape, 1, DEV)
+    cache.state.copy_(st0)
+    assert not cache_consistent(cache)
+    cache.refresh()
+    assert cache_consistent(cache)
+    yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
+    assert same_bits(yd, y) and cache_consistent(cache)
