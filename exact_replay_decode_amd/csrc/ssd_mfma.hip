@@ -494,6 +494,15 @@ __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
                      : DT::ld(v.dt, v.token(jd) * v.H + v.h);
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maximum, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &u) {
     return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
 }
@@ -735,28 +744,33 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Exact-replay decode. One single-wave workgroup per (slot, head). The wave computes the one output row k = buf_len of
-// the t-block that holds it, with the prefill's operands and MFMA order:
+// Exact-replay decode. A workgroup of kDecodeWaves waves serves that many
+// heads of one slot, one wave per head. Each wave computes the single output
+// row k = buf_len of the t-block holding it, with the prefill's operands and
+// MFMA order:
 //   - the read-out operand S_bf comes from the cache's bf16 state copy, the
-//     bf16 rounding the prefill applies to the same fp32 state;
+//     rounding the prefill applies to the same fp32 state;
 //   - C . B^T and the weights are built for column k % 32 only (the other
-//     columns of C are zero, their weights are selected to zero): an MFMA
+//     columns of C are zero and their weights are selected to zero): an MFMA
 //     output element depends only on its own row and column;
-//   - the buffer's B rows are A operands read straight from global memory;
-//     the X rows of each s-block pass through a small per-wave LDS tile for
-//     the transposed read; rows after k are zero;
+//   - when the workgroup's heads share a B/C group, each wave computes C . B^T
+//     for a quarter of the s-blocks and hands column k % 32 over in LDS;
+//   - the X rows of each s-block pass through a small per-wave LDS tile for
+//     the transposed read (rows after k are zero), loaded one block ahead;
 //   - the in-chunk scan is the prefill's block scan, one 64-row segment at a
 //     time (wave_scan_segments).
 // When the token fills the chunk the wave also runs the chunk-state update
-// of its head (per 16-row K step, staged through the same LDS tile) and
-// writes the new fp32 state and its bf16 copy. The last workgroup of a slot
-// to finish advances buf_len / boundary_pos (arrivals counter).
-constexpr int kDecodeWaves = 1;
+// of its head (per 16-row K step, staged through LDS) and writes the new
+// fp32 state and its bf16 copy. The last workgroup of a slot to finish
+// advances buf_len / boundary_pos (arrivals counter).
+constexpr int kDecodeWaves = 4;
 
-// Per-wave LDS of the decode kernel, in bytes.
+// Per-wave LDS of the decode kernel, in bytes. The x region holds the
+// padded 32-row x tile during the s-block loop and the padded 16-row x and B
+// tiles of the state update afterwards.
 struct DLayout {
     int XS, BS;
-    int lam, u, beta, w, X, B, bytes;
+    int lam, u, beta, w, gc, X, B, bytes;
     __host__ __device__ DLayout(int Qp, int P, int N) {
         XS = P + kPad;
         BS = N + kPad;
@@ -765,15 +779,28 @@ struct DLayout {
         u = o;    o += Qp * 4;
         beta = o; o += Qp * 4;
         w = o;    o += Qp * 4;
-        X = o;    o += 32 * XS * 2;   // 32 rows of x (16 in the state update)
-        B = o;    o += 16 * BS * 2;   // 16 rows of B (state update)
+        gc = o;   o += (kMaxQ / 32) * 32 * 4;   // C.B^T column k % 32 per s-block
+        X = o;
+        B = X + 16 * XS * 2;
+        const int tile = 32 * XS * 2, stage = 16 * XS * 2 + 16 * BS * 2;
+        o += stage > tile ? stage : tile;
         bytes = (o + 15) & ~15;
     }
 };
 
+// Registers a decode wave carries from the first phase to the second.
+template <int P, class DT>
+struct DecodeCarry {
+    f32x16 acc[P / 32];          // read-out, scaled: the Y^T accumulators
+    float lam_k;
+};
+
+// Phase 1: the wave's loads, the read-out, the append of the token, the
+// in-chunk scan and the C.B^T columns of the s-blocks this wave owns.
 template <int P, int N, class DT>
-__device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot, int h, int k,
-                                            char *lds, const DLayout &L) {
+__device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slot, int h, int k,
+                                             int wave, bool gshare, char *lds, const DLayout &L,
+                                             DecodeCarry<P, DT> &cy) {
     using TD = typename DT::T;
     constexpr int NPT = P / 32, NK = N / 16;
     const Dims d = a.d;
@@ -785,23 +812,21 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
     const bool commit = k + 1 == Q;
     const bool col = c == (k & 31);   // lanes of output column k % 32
     const int64_t PN = (int64_t)P * N;
-    const int64_t hoff = ((int64_t)slot * H + h) * PN;
-    const uint16_t *sbf = static_cast<const uint16_t *>(a.cache_state_bf) + hoff;
+    const uint16_t *sbf = static_cast<const uint16_t *>(a.cache_state_bf) +
+                          ((int64_t)slot * H + h) * PN;
     const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
     const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
     const uint16_t *Cin = static_cast<const uint16_t *>(a.C) + ((int64_t)b * G + g) * N;
     const TD *dtin = static_cast<const TD *>(a.dt) + (int64_t)b * H + h;
-    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
-    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
-    float *lam = reinterpret_cast<float *>(lds + L.lam);
-    float *uu = reinterpret_cast<float *>(lds + L.u);
-    float *bt = reinterpret_cast<float *>(lds + L.beta);
+    const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    const TD *bdt = static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+    // s-blocks whose C.B^T column this wave computes
+    const int sg0 = gshare ? wave : 0, sgs = gshare ? kDecodeWaves : 1;
 
-    // Every load that does not depend on earlier results is issued first:
-    // the token (for y and the append), raw dt of rows 0..k, C_k, S_bf.
-    const int nseg_max = commit ? (Qp + 63) >> 6 : ((32 * (tau + 1)) + 63) >> 6;
-    TD rawdt[4];
+    // every load that does not depend on earlier results goes out first
+    const float A2 = a.A[h] * kLog2e;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    TD rawdt[4];   // raw dt of rows lane + 64 i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
@@ -822,21 +847,56 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
         for (int kk = 0; kk < NK; ++kk)
             cf[kk] = __builtin_bit_cast(bf16x8, keep_if(col, raw[kk]));
     }
-    // read-out C . S_bf (operand (pt, kk) is 1 KiB contiguous in the copy)
-    f32x16 acc[NPT];
+    auto load_brows = [&](int sg, uint4 (&br)[NK]) {
+        const int s = 32 * sg + c;
+        const uint16_t *brow = s < k ? bB + ((int64_t)s * G + g) * N : Bin;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            br[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
+    };
+    // read-out C . S_bf (operand (pt, kk) is 1 KiB contiguous in the copy);
+    // all operand loads are in flight before the first MFMA waits on one
+    bf16x8 sa[NPT][NK];
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
-        acc[pt] = readout_raw<N>(
-            [&](int kk) {
-                return *reinterpret_cast<const bf16x8 *>(sbf + ((int64_t)kk * P + 32 * pt + c) * 16 +
-                                                         8 * gl);
-            },
-            cf);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            sa[pt][kk] = *reinterpret_cast<const bf16x8 *>(
+                sbf + ((int64_t)kk * P + 32 * pt + c) * 16 + 8 * gl);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+        cy.acc[pt] = readout_raw<N>([&](int kk) { return sa[pt][kk]; }, cf);
+
+    // append the token at buffer position k now: this step reads only
+    // positions < k of the buffer (the token itself comes from the input)
+    {
+        uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+        uint16_t *bBw = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+        TD *bdtw = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+        if (lane < P / 8)
+            *reinterpret_cast<uint4 *>(bx + ((int64_t)k * H + h) * P + 8 * lane) = xtok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == k)
+                bdtw[(int64_t)k * H + h] = rawdt[i];
+        if (h % (H / G) == 0 && lane < N / 8) {
+            *reinterpret_cast<uint4 *>(bBw + ((int64_t)k * G + g) * N + 8 * lane) = btok;
+            if (a.buf_C) {
+                uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
+                *reinterpret_cast<uint4 *>(bC + ((int64_t)k * G + g) * N + 8 * lane) =
+                    *reinterpret_cast<const uint4 *>(Cin + 8 * lane);
+            }
+        }
+    }
+
+    // B rows of the first owned s-block (in flight during the scan)
+    uint4 braw[NK];
+    if (sg0 <= tau)
+        load_brows(sg0, braw);
 
     // delta and the in-chunk cumulative sum (log2 units) over rows j = lane + 64 i
-    const float A2 = a.A[h] * kLog2e;
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const int nseg = nseg_max;
+    const int nseg = commit ? (Qp + 63) >> 6 : (32 * (tau + 1) + 63) >> 6;
     float dv[4], lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -850,6 +910,10 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
         lv[i] = aa;
     }
     wave_scan_segments(lv, nseg);
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *bt = reinterpret_cast<float *>(lds + L.beta);
+    float *dl = reinterpret_cast<float *>(lds + L.w);   // delta, for the state update
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
@@ -860,38 +924,93 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
             lam[j] = l;
             uu[j] = u;
             bt[j] = fexp2(lend - u);
+            if (commit)
+                dl[j] = dv[i];
         }
     }
-    const float lam_k = lam[k];
-    const float el_k = fexp2(lam_k);
+    cy.lam_k = lam[k];
+    const float el_k = fexp2(cy.lam_k);
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
-        acc[pt] = readout_scale(acc[pt], el_k);
+        cy.acc[pt] = readout_scale(cy.acc[pt], el_k);
 
-    // s-blocks 0..tau: G^T, weights of column k % 32, M.X
-    constexpr int XPL = P / 16;  // 16-byte pieces of a 32-row x block per lane
-    for (int sg = 0; sg <= tau; ++sg) {
-        const int s = 32 * sg + c;
-        const uint16_t *brow = s < k ? bB + ((int64_t)s * G + g) * N : Bin;
-        uint4 braw[NK];
+    // C.B^T of the owned s-blocks; column k % 32 to LDS
+    float *gcol = reinterpret_cast<float *>(lds + L.gc);
+    for (int sg = sg0; sg <= tau; sg += sgs) {
+        const bool more = sg + sgs <= tau;
+        const bool srow = 32 * sg + c <= k;   // rows after k are zero
+        const f32x16 gt = gram_block<N>(
+            [&](int kk) { return __builtin_bit_cast(bf16x8, keep_if(srow, braw[kk])); }, cf);
+        if (col) {
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-            braw[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
-        uint4 xraw[XPL];
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4 *>(gcol + 32 * sg + 8 * q + 4 * gl) =
+                    make_float4(gt[4 * q], gt[4 * q + 1], gt[4 * q + 2], gt[4 * q + 3]);
+        }
+        if (more)
+            load_brows(sg + sgs, braw);
+    }
+}
+
+// Phase 2: weights and M.X over the s-blocks, the output row and (when the
+// chunk fills) the chunk-state update.
+template <int P, int N, class DT>
+__device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot, int h, int k,
+                                            int wave, bool gshare, char *lds_all, const DLayout &L,
+                                            DecodeCarry<P, DT> &cy) {
+    constexpr int NPT = P / 32;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int g = h / (H / G);
+    const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
+    const int tau = k >> 5;
+    const bool commit = k + 1 == Q;
+    const bool col = c == (k & 31);
+    char *lds = lds_all + wave * L.bytes;
+    const int64_t hoff = ((int64_t)slot * H + h) * (int64_t)P * N;
+    const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
+    const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
+    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    const float *lam = reinterpret_cast<const float *>(lds + L.lam);
+    const float *uu = reinterpret_cast<const float *>(lds + L.u);
+    const float *bt = reinterpret_cast<const float *>(lds + L.beta);
+
+    // x tile of each s-block: 32 rows x P through registers into the padded
+    // LDS tile, the next two blocks' rows in flight during this block's work
+    constexpr int XPL = P / 16;  // 16-byte pieces of a tile per lane
+    auto load_x = [&](int sg, uint4 (&xr)[XPL]) {
 #pragma unroll
         for (int i = 0; i < XPL; ++i) {
             const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
             const int row = 32 * sg + r;
             const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
-            xraw[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+            xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
         }
-        const f32x16 gt = gram_block<N>(
-            [&](int kk) { return __builtin_bit_cast(bf16x8, keep_if(s <= k, braw[kk])); }, cf);
+    };
+    uint4 xa[XPL], xb[XPL];
+    load_x(0, xa);
+    if (tau >= 1)
+        load_x(1, xb);
+    for (int sg = 0; sg <= tau; ++sg) {
+        // C.B^T column of this s-block, back in the MFMA output layout
+        const int owner = gshare ? sg % kDecodeWaves : wave;
+        const float *gcol = reinterpret_cast<const float *>(lds_all + owner * L.bytes + L.gc);
+        f32x16 gt;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(gcol + 32 * sg + 8 * q + 4 * gl);
+            gt[4 * q] = v.x;
+            gt[4 * q + 1] = v.y;
+            gt[4 * q + 2] = v.z;
+            gt[4 * q + 3] = v.w;
+        }
         uint32_t mb[8];
         if (sg == tau)
-            m_diag(gt, lam_k, uu, 32 * sg, k, mb);
+            m_diag(gt, cy.lam_k, uu, 32 * sg, k, mb);
         else
-            m_off(gt, fexp2(lam_k - lam[32 * sg + 31]), bt, 32 * sg, mb);
+            m_off(gt, fexp2(cy.lam_k - lam[32 * sg + 31]), bt, 32 * sg, mb);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             mb[q] = col ? mb[q] : 0u;
@@ -899,9 +1018,16 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
         for (int i = 0; i < XPL; ++i) {
             const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
             *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
-                keep_if(32 * sg + r <= k, xraw[i]);
+                keep_if(32 * sg + r <= k, xa[i]);   // rows after k are zero
         }
-        mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc);
+        if (sg + 1 <= tau) {
+#pragma unroll
+            for (int i = 0; i < XPL; ++i)
+                xa[i] = xb[i];
+        }
+        if (sg + 2 <= tau)
+            load_x(sg + 2, xb);
+        mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, cy.acc);
     }
 
     // y row k: fmaf(D, x, Y^T) -> bf16, -0 -> +0 (lanes of column k % 32);
@@ -915,13 +1041,13 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = 32 * pt + 8 * q + 4 * gl;
-                const uint2 xr = *reinterpret_cast<const uint2 *>(xk + 2 * p);
-                const float xs[4] = {bf16_float(xr.x & 0xffff), bf16_float(xr.x >> 16),
-                                     bf16_float(xr.y & 0xffff), bf16_float(xr.y >> 16)};
+                const uint2 xv = *reinterpret_cast<const uint2 *>(xk + 2 * p);
+                const float xs[4] = {bf16_float(xv.x & 0xffff), bf16_float(xv.x >> 16),
+                                     bf16_float(xv.y & 0xffff), bf16_float(xv.y >> 16)};
                 uint16_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float yv = fmaf(D_h, xs[e], acc[pt][4 * q + e]);
+                    float yv = fmaf(D_h, xs[e], cy.acc[pt][4 * q + e]);
                     yv = yv + 0.0f;
                     o[e] = bf16_bits(yv);
                 }
@@ -930,41 +1056,44 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
             }
         }
     }
-
-    // append the token at buffer position k (this step reads positions < k)
-    if (lane < P / 8)
-        *reinterpret_cast<uint4 *>(bx + ((int64_t)k * H + h) * P + 8 * lane) = xtok;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == k)
-            bdt[(int64_t)k * H + h] = rawdt[i];
-    if (h % (H / G) == 0 && lane < N / 8) {
-        *reinterpret_cast<uint4 *>(bB + ((int64_t)k * G + g) * N + 8 * lane) = btok;
-        if (a.buf_C) {
-            uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
-            *reinterpret_cast<uint4 *>(bC + ((int64_t)k * G + g) * N + 8 * lane) =
-                *reinterpret_cast<const uint4 *>(Cin + 8 * lane);
-        }
-    }
     if (!commit)
         return;
 
     // chunk-state update S <- 2^(l_last) S + sum_s B_s (w_s x_s), as in the
-    // prefill (tiles of 32 x 32, K = 16 rows ascending, hi then lo)
-    float *w = reinterpret_cast<float *>(lds + L.w);
+    // prefill (tiles of 32 x 32, K = 16 rows ascending, hi then lo); each
+    // pass keeps TPP tiles in registers, the next 16 rows in flight
+    float *w = reinterpret_cast<float *>(lds + L.w);   // holds delta on entry
     const float l_last = lam[Q - 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
-        if (i < nseg && j < Qp)
-            w[j] = fexp2(l_last - lv[i]) * dv[i];
+        if (j < Qp)
+            w[j] = fexp2(l_last - lam[j]) * w[j];
     }
     const float dec = fexp2(l_last);
     constexpr int NT = NPT * (N / 32);
-    constexpr int TPP = NT < 4 ? NT : 4;            // tiles per pass
+    constexpr int TPP = NT < 2 ? NT : 2;            // tiles per pass
     constexpr int XP16 = P / 32, BP16 = N / 32;     // 16-byte pieces per lane, 16 rows
+    const int nks = Qp / 16;
     float *st = a.cache_state + hoff;
     uint16_t *stbf = static_cast<uint16_t *>(a.cache_state_bf) + hoff;
+    auto load_stage = [&](int ks, uint4 (&xs)[XP16], uint4 (&bs)[BP16]) {
+#pragma unroll
+        for (int i = 0; i < XP16; ++i) {
+            const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+            const int row = 16 * ks + r;
+            const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
+            xs[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+#pragma unroll
+        for (int i = 0; i < BP16; ++i) {
+            const int e = lane + 64 * i, r = e / (N / 8), q = e % (N / 8);
+            const int row = 16 * ks + r;
+            const uint16_t *src = row < k ? bB + ((int64_t)row * G + g) * N : Bin;
+            bs[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+        }
+    };
+#pragma unroll 1
     for (int pass = 0; pass < NT / TPP; ++pass) {
         f32x16 S[TPP];
 #pragma unroll
@@ -980,29 +1109,31 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
                 S[i][4 * q + 2] = v.z;
                 S[i][4 * q + 3] = v.w;
             }
+        }
+        uint4 xs[XP16], bs[BP16];
+        load_stage(0, xs, bs);
+#pragma unroll
+        for (int i = 0; i < TPP; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 S[i][r] = S[i][r] * dec;
-        }
-        for (int ks = 0; ks < Qp / 16; ++ks) {
+        for (int ks = 0; ks < nks; ++ks) {
             // rows 16 ks .. +15 of the chunk: buffer below k, the token at k,
             // zeros past the chunk
 #pragma unroll
             for (int i = 0; i < XP16; ++i) {
                 const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
-                const int row = 16 * ks + r;
-                const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
                 *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
-                    keep_if(row <= k, *reinterpret_cast<const uint4 *>(src + 8 * q));
+                    keep_if(16 * ks + r <= k, xs[i]);
             }
 #pragma unroll
             for (int i = 0; i < BP16; ++i) {
                 const int e = lane + 64 * i, r = e / (N / 8), q = e % (N / 8);
-                const int row = 16 * ks + r;
-                const uint16_t *src = row < k ? bB + ((int64_t)row * G + g) * N : Bin;
                 *reinterpret_cast<uint4 *>(lds + L.B + (r * L.BS + 8 * q) * 2) =
-                    keep_if(row <= k, *reinterpret_cast<const uint4 *>(src + 8 * q));
+                    keep_if(16 * ks + r <= k, bs[i]);
             }
+            if (ks + 1 < nks)
+                load_stage(ks + 1, xs, bs);
             const int r0 = 16 * ks + 8 * gl;
             const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
             const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
@@ -1039,15 +1170,16 @@ __device__ __forceinline__ void decode_head(const DecodeArgs &a, int b, int slot
 }
 
 template <int P, int N, class DT>
-__global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void k_decode_mfma(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds_all[];
-    const int H = a.d.H, Q = a.d.Q;
+    const int H = a.d.H, G = a.d.G, Q = a.d.Q;
     const int Qp = Q < 32 ? 32 : Q;
     const int HQ = (H + kDecodeWaves - 1) / kDecodeWaves;
     // the workgroups of one slot run on one XCD (they share its B rows)
     const int wid = xcd_local_index(blockIdx.x, gridDim.x);
     const int b = wid / HQ;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int h = (wid % HQ) * kDecodeWaves + wave;
     const DLayout L(Qp, P, N);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
@@ -1056,9 +1188,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_mfma(DecodeArgs a)
     const int k = a.buf_len[slot];
     if (k < 0 || k >= Q)
         return;
+    // the workgroup's heads share one B/C group: C.B^T is split between them
+    const bool gshare = (H / G) % kDecodeWaves == 0;
+    DecodeCarry<P, DT> cy;
     if (h < H)
-        decode_head<P, N, DT>(a, b, slot, h, k, lds_all + wave * L.bytes, L);
-    // (with one wave per workgroup the barrier below is a no-op)
+        decode_front<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all + wave * L.bytes, L, cy);
+    __syncthreads();  // C.B^T columns of every wave are in LDS
+    if (h < H)
+        decode_back<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all, L, cy);
     // Every wave of this workgroup has read buf_len (and used it) by now; the
     // slot's last workgroup to arrive advances it. The counter needs only
     // atomicity, no ordering: no workgroup reads what the last one writes
@@ -1076,6 +1213,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_mfma(DecodeArgs a)
                 a.boundary_pos[slot] += Q;
         }
     }
+    (void)G;
 }
 
 template <class K>
