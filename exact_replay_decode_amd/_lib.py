@@ -37,7 +37,7 @@ class ssd_replay_cache(ctypes.Structure):
                 ("buf_x", ctypes.c_void_p), ("buf_dt", ctypes.c_void_p),
                 ("buf_B", ctypes.c_void_p), ("buf_C", ctypes.c_void_p),
                 ("buf_len", ctypes.c_void_p), ("boundary_pos", ctypes.c_void_p),
-                ("arrivals", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+                ("work", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 

@@ -112,7 +112,7 @@ class ReplayCache:
         self.buf_len = mk((num_slots,), dtype=torch.int32, device=self.device)
         self.boundary_pos = mk((num_slots,), dtype=torch.int64, device=self.device)
         # decode bookkeeping, zero between calls (always allocated zeroed)
-        self.arrivals = torch.zeros((num_slots,), dtype=torch.int32, device=self.device)
+        self.work = torch.zeros((2 * num_slots + 34,), dtype=torch.int32, device=self.device)
 
     def struct(self) -> _lib.ssd_replay_cache:
         sd = _lib.SSD_F32 if self.state.dtype == torch.float32 else _lib.SSD_BF16
@@ -120,7 +120,7 @@ class ReplayCache:
             self.state.data_ptr(), self.state_bf.data_ptr(), self.buf_x.data_ptr(),
             self.buf_dt.data_ptr(), self.buf_B.data_ptr(),
             None if self.buf_C is None else self.buf_C.data_ptr(),
-            self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.arrivals.data_ptr(),
+            self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.work.data_ptr(),
             self.num_slots, self.shape.chunk_size, sd)
 
     def state_bf_rowmajor(self) -> torch.Tensor:
@@ -137,7 +137,7 @@ class ReplayCache:
 
     def tensors(self):
         return [t for t in (self.state, self.state_bf, self.buf_x, self.buf_dt, self.buf_B,
-                            self.buf_C, self.buf_len, self.boundary_pos, self.arrivals)
+                            self.buf_C, self.buf_len, self.boundary_pos, self.work)
                 if t is not None]
 
     def clone(self) -> "ReplayCache":

@@ -76,7 +76,7 @@ int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
     if (c->chunk_size != sh->chunk_size)
         return SSD_ERR_CHUNK_MISMATCH;
     if (!c->state || !c->state_bf || !c->buf_x || !c->buf_dt || !c->buf_B || !c->buf_len ||
-        !c->boundary_pos || !c->arrivals)
+        !c->boundary_pos || !c->work)
         return SSD_ERR_NULL;
     if (c->num_slots <= 0)
         return SSD_ERR_SHAPE;
@@ -125,8 +125,8 @@ size_t ssd_replay_cache_bytes(const ssd_shape *sh, int32_t num_slots, int32_t wi
     const size_t per_tok = (size_t)d.H * d.P * io + (size_t)d.H * dtb +
                            (with_C ? 2 : 1) * (size_t)d.G * d.N * io;
     const size_t per_slot =
-        state + (size_t)d.Q * per_tok + 2 * sizeof(int32_t) + sizeof(int64_t);
-    return per_slot * (size_t)num_slots;
+        state + (size_t)d.Q * per_tok + 3 * sizeof(int32_t) + sizeof(int64_t);
+    return per_slot * (size_t)num_slots + 34 * sizeof(int32_t);
 }
 
 int ssd_replay_cache_refresh(const ssd_shape *sh, const ssd_replay_cache *cache,
@@ -313,7 +313,7 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
-    a.arrivals = cache->arrivals;
+    a.work = cache->work;
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
 }

@@ -68,7 +68,8 @@ struct DecodeArgs {
     void *buf_x, *buf_dt, *buf_B, *buf_C;
     int32_t *buf_len;
     int64_t *boundary_pos;
-    int32_t *arrivals;        // [slots], zero between calls
+    int32_t *work;            // [2*slots+34]: arrival counters [slots], commit-list
+                              // count and done counters [34], commit list [slots]
 };
 
 struct SsuArgs {

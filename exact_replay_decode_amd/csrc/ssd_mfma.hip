@@ -507,8 +507,39 @@ __device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &u) {
     return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
 }
 
-// LDS copy of the register-staged chunk plus delta / lam / u / exp(lam) /
-// state weights; the arithmetic is that of stage_chunk.
+// Per-row quantities of a chunk, computed by the whole workgroup (one row per
+// thread; rows past n_valid have delta 0): lam (in-chunk cumulative sum of
+// delta A, log2 units), u = lam - log2(delta), 2^lam, beta = 2^(c - u) with c
+// the lam at the end of the row's 32-row block, and, with `weights`, the
+// state weights w = 2^(lam_last - lam) delta.
+__device__ __forceinline__ void chunk_scalars(float dt_raw, int n_valid, float A2_h, float bias,
+                                              int softplus, bool weights, char *lds,
+                                              const MLayout &L) {
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *el = reinterpret_cast<float *>(lds + L.el);
+    float *w = reinterpret_cast<float *>(lds + L.w);
+    const int j = threadIdx.x;
+    float d = 0.0f, a = 0.0f;
+    if (j < n_valid) {
+        d = delta_of(dt_raw, bias, softplus);
+        a = d * A2_h;
+    }
+    const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
+    if (j < kMaxQ) {
+        lam[j] = l;
+        uu[j] = l - flog2(d);
+        el[j] = fexp2(l);
+    }
+    __syncthreads();
+    if (j < kMaxQ) {
+        reinterpret_cast<float *>(lds + L.beta)[j] = fexp2(lam[j | 31] - uu[j]);
+        if (weights)
+            w[j] = fexp2(lam[n_valid - 1] - l) * d;
+    }
+}
+
+// LDS copy of the register-staged chunk, then chunk_scalars.
 template <int P, int N, int NT>
 __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, int rows,
                                                  int n_valid, float A2_h, float bias,
@@ -531,27 +562,42 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
             *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) =
                 full ? r.b[i] : keep_if(j < n_valid, r.b[i]);
     }
-    float *lam = reinterpret_cast<float *>(lds + L.lam);
-    float *uu = reinterpret_cast<float *>(lds + L.u);
-    float *el = reinterpret_cast<float *>(lds + L.el);
-    float *w = reinterpret_cast<float *>(lds + L.w);
-    const int j = tid;
-    float d = 0.0f, a = 0.0f;
-    if (j < n_valid) {
-        d = delta_of(r.dt, bias, softplus);
-        a = d * A2_h;
-    }  // (a lane past the chunk loaded row 0's dt; it is not used)
-    const float l = block_scan_inclusive(a, reinterpret_cast<float *>(lds + L.tot));
-    if (j < kMaxQ) {
-        lam[j] = l;
-        uu[j] = l - flog2(d);
-        el[j] = fexp2(l);
-    }
-    __syncthreads();
-    if (j < kMaxQ) {
-        reinterpret_cast<float *>(lds + L.beta)[j] = fexp2(lam[j | 31] - uu[j]);
-        if (weights)
-            w[j] = fexp2(lam[n_valid - 1] - l) * d;
+    // (a thread past the chunk loaded row 0's dt; chunk_scalars ignores it)
+    chunk_scalars(r.dt, n_valid, A2_h, bias, softplus, weights, lds, L);
+}
+
+// Rows [0, rows) of the chunk's x (CX 16-byte pieces per row) and B (CB
+// pieces per row) from global rows (strides in elements) into the padded LDS
+// tiles; rows past n_valid are zero. Both streams share one index space so
+// that eight pieces per thread are in flight at a time.
+template <int CX, int CB>
+__device__ __forceinline__ void stage_rows(const uint16_t *xs, int64_t xstride,
+                                           const uint16_t *bs, int64_t bstride, int rows,
+                                           int n_valid, char *xdst, int XS, char *bdst, int BS) {
+    const int nthr = blockDim.x, tid = threadIdx.x;
+    const int nx = rows * CX, total = nx + rows * CB;
+    for (int e0 = 0; e0 < total; e0 += 8 * nthr) {
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e0 + tid + i * nthr;
+            const bool isx = e < nx;
+            const int f = isx ? e : e - nx, C = isx ? CX : CB;
+            const int j = f / C, q = f % C;
+            const int jj = (e < total && j < n_valid) ? j : 0;
+            v[i] = isx ? *reinterpret_cast<const uint4 *>(xs + jj * xstride + 8 * q)
+                       : *reinterpret_cast<const uint4 *>(bs + jj * bstride + 8 * q);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e0 + tid + i * nthr;
+            const bool isx = e < nx;
+            const int f = isx ? e : e - nx, C = isx ? CX : CB;
+            const int j = f / C, q = f % C;
+            if (e < total)
+                *reinterpret_cast<uint4 *>((isx ? xdst : bdst) + (j * (isx ? XS : BS) + 8 * q) * 2) =
+                    keep_if(j < n_valid, v[i]);
+        }
     }
 }
 
@@ -759,32 +805,35 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
 //     the transposed read (rows after k are zero), loaded one block ahead;
 //   - the in-chunk scan is the prefill's block scan, one 64-row segment at a
 //     time (wave_scan_segments).
-// When the token fills the chunk the wave also runs the chunk-state update
-// of its head (per 16-row K step, staged through LDS) and writes the new
-// fp32 state and its bf16 copy. The last workgroup of a slot to finish
-// advances buf_len / boundary_pos (arrivals counter).
+// The last workgroup of a slot to arrive advances buf_len / boundary_pos
+// (per-slot arrival counter); when the token filled the chunk it also puts
+// the slot on a list, and a second kernel (k_decode_commit) runs the
+// chunk-state update of those slots with the prefill's own chunk routines.
 constexpr int kDecodeWaves = 4;
 
-// Per-wave LDS of the decode kernel, in bytes. The x region holds the
-// padded 32-row x tile during the s-block loop and the padded 16-row x and B
-// tiles of the state update afterwards.
+// Workgroups of the chunk-commit kernel (each handles one head of a full
+// chunk at a time; when no chunk filled they return at once).
+constexpr int kCommitGroups = 1024;
+// The work array after the per-slot arrival counters: [0] number of slots
+// on the commit list, [1] finished groups, [2, 2 + kDoneGroups) finished
+// workgroups per group, then the list itself.
+constexpr int kDoneGroups = 32;
+constexpr int kListHead = 2 + kDoneGroups;
+
+// Per-wave LDS of the decode kernel, in bytes.
 struct DLayout {
-    int XS, BS;
-    int lam, u, beta, w, gc, X, B, bytes;
+    int XS;
+    int lam, u, beta, gc, X, bytes;
     __host__ __device__ DLayout(int Qp, int P, int N) {
         XS = P + kPad;
-        BS = N + kPad;
         int o = 0;
         lam = o;  o += Qp * 4;
         u = o;    o += Qp * 4;
         beta = o; o += Qp * 4;
-        w = o;    o += Qp * 4;
         gc = o;   o += (kMaxQ / 32) * 32 * 4;   // C.B^T column k % 32 per s-block
-        X = o;
-        B = X + 16 * XS * 2;
-        const int tile = 32 * XS * 2, stage = 16 * XS * 2 + 16 * BS * 2;
-        o += stage > tile ? stage : tile;
+        X = o;    o += 32 * XS * 2;              // padded 32-row x tile
         bytes = (o + 15) & ~15;
+        (void)N;
     }
 };
 
@@ -793,7 +842,24 @@ template <int P, class DT>
 struct DecodeCarry {
     f32x16 acc[P / 32];          // read-out, scaled: the Y^T accumulators
     float lam_k;
+    uint4 xa[P / 16], xb[P / 16];   // x tiles of s-blocks 0 and 1 (in flight)
 };
+
+// Rows 32 sg .. +31 of the head's x (buffer below k, the token at k; rows
+// after k are loaded from the token and zeroed when stored), as 16-byte
+// pieces lane + 64 i of the row-major tile.
+template <int P>
+__device__ __forceinline__ void load_x_tile(const uint16_t *bx, const uint16_t *xin, int H, int h,
+                                            int k, int sg, uint4 (&xr)[P / 16]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < P / 16; ++i) {
+        const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+        const int row = 32 * sg + r;
+        const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
+        xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+    }
+}
 
 // Phase 1: the wave's loads, the read-out, the append of the token, the
 // in-chunk scan and the C.B^T columns of the s-blocks this wave owns.
@@ -809,7 +875,6 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     const int g = h / (H / G);
     const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
     const int tau = k >> 5;
-    const bool commit = k + 1 == Q;
     const bool col = c == (k & 31);   // lanes of output column k % 32
     const int64_t PN = (int64_t)P * N;
     const uint16_t *sbf = static_cast<const uint16_t *>(a.cache_state_bf) +
@@ -890,13 +955,20 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
         }
     }
 
-    // B rows of the first owned s-block (in flight during the scan)
+    // B rows of the first owned s-block and the first two x tiles (in flight
+    // during the scan)
     uint4 braw[NK];
     if (sg0 <= tau)
         load_brows(sg0, braw);
+    {
+        const uint16_t *bxr = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+        load_x_tile<P>(bxr, xin, H, h, k, 0, cy.xa);
+        if (tau >= 1)
+            load_x_tile<P>(bxr, xin, H, h, k, 1, cy.xb);
+    }
 
     // delta and the in-chunk cumulative sum (log2 units) over rows j = lane + 64 i
-    const int nseg = commit ? (Qp + 63) >> 6 : (32 * (tau + 1) + 63) >> 6;
+    const int nseg = (32 * (tau + 1) + 63) >> 6;
     float dv[4], lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -913,7 +985,6 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     float *lam = reinterpret_cast<float *>(lds + L.lam);
     float *uu = reinterpret_cast<float *>(lds + L.u);
     float *bt = reinterpret_cast<float *>(lds + L.beta);
-    float *dl = reinterpret_cast<float *>(lds + L.w);   // delta, for the state update
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
@@ -924,8 +995,6 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
             lam[j] = l;
             uu[j] = u;
             bt[j] = fexp2(lend - u);
-            if (commit)
-                dl[j] = dv[i];
         }
     }
     cy.lam_k = lam[k];
@@ -952,47 +1021,30 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     }
 }
 
-// Phase 2: weights and M.X over the s-blocks, the output row and (when the
-// chunk fills) the chunk-state update.
+// Phase 2: weights and M.X over the s-blocks, and the output row.
 template <int P, int N, class DT>
 __device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot, int h, int k,
                                             int wave, bool gshare, char *lds_all, const DLayout &L,
                                             DecodeCarry<P, DT> &cy) {
     constexpr int NPT = P / 32;
     const Dims d = a.d;
-    const int H = d.H, G = d.G, Q = d.Q;
-    const int Qp = Q < 32 ? 32 : Q;
-    const int g = h / (H / G);
+    const int H = d.H, Q = d.Q;
     const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
     const int tau = k >> 5;
-    const bool commit = k + 1 == Q;
     const bool col = c == (k & 31);
     char *lds = lds_all + wave * L.bytes;
-    const int64_t hoff = ((int64_t)slot * H + h) * (int64_t)P * N;
     const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
-    const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
-    uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-    uint16_t *bB = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+    const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
     const float *uu = reinterpret_cast<const float *>(lds + L.u);
     const float *bt = reinterpret_cast<const float *>(lds + L.beta);
 
     // x tile of each s-block: 32 rows x P through registers into the padded
     // LDS tile, the next two blocks' rows in flight during this block's work
+    // (tiles 0 and 1 were issued in phase 1)
     constexpr int XPL = P / 16;  // 16-byte pieces of a tile per lane
-    auto load_x = [&](int sg, uint4 (&xr)[XPL]) {
-#pragma unroll
-        for (int i = 0; i < XPL; ++i) {
-            const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
-            const int row = 32 * sg + r;
-            const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
-            xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
-    };
-    uint4 xa[XPL], xb[XPL];
-    load_x(0, xa);
-    if (tau >= 1)
-        load_x(1, xb);
+    uint4 (&xa)[XPL] = cy.xa;
+    uint4 (&xb)[XPL] = cy.xb;
     for (int sg = 0; sg <= tau; ++sg) {
         // C.B^T column of this s-block, back in the MFMA output layout
         const int owner = gshare ? sg % kDecodeWaves : wave;
@@ -1026,7 +1078,7 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot
                 xa[i] = xb[i];
         }
         if (sg + 2 <= tau)
-            load_x(sg + 2, xb);
+            load_x_tile<P>(bx, xin, H, h, k, sg + 2, xb);
         mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, cy.acc);
     }
 
@@ -1053,117 +1105,6 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot
                 }
                 *reinterpret_cast<uint2 *>(yrow + p) =
                     make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
-            }
-        }
-    }
-    if (!commit)
-        return;
-
-    // chunk-state update S <- 2^(l_last) S + sum_s B_s (w_s x_s), as in the
-    // prefill (tiles of 32 x 32, K = 16 rows ascending, hi then lo); each
-    // pass keeps TPP tiles in registers, the next 16 rows in flight
-    float *w = reinterpret_cast<float *>(lds + L.w);   // holds delta on entry
-    const float l_last = lam[Q - 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = lane + 64 * i;
-        if (j < Qp)
-            w[j] = fexp2(l_last - lam[j]) * w[j];
-    }
-    const float dec = fexp2(l_last);
-    constexpr int NT = NPT * (N / 32);
-    constexpr int TPP = NT < 2 ? NT : 2;            // tiles per pass
-    constexpr int XP16 = P / 32, BP16 = N / 32;     // 16-byte pieces per lane, 16 rows
-    const int nks = Qp / 16;
-    float *st = a.cache_state + hoff;
-    uint16_t *stbf = static_cast<uint16_t *>(a.cache_state_bf) + hoff;
-    auto load_stage = [&](int ks, uint4 (&xs)[XP16], uint4 (&bs)[BP16]) {
-#pragma unroll
-        for (int i = 0; i < XP16; ++i) {
-            const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
-            const int row = 16 * ks + r;
-            const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
-            xs[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
-#pragma unroll
-        for (int i = 0; i < BP16; ++i) {
-            const int e = lane + 64 * i, r = e / (N / 8), q = e % (N / 8);
-            const int row = 16 * ks + r;
-            const uint16_t *src = row < k ? bB + ((int64_t)row * G + g) * N : Bin;
-            bs[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
-        }
-    };
-#pragma unroll 1
-    for (int pass = 0; pass < NT / TPP; ++pass) {
-        f32x16 S[TPP];
-#pragma unroll
-        for (int i = 0; i < TPP; ++i) {
-            const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
-            const int p = 32 * pt + c;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = 32 * nt + 8 * q + 4 * gl;
-                const float4 v = *reinterpret_cast<const float4 *>(st + (int64_t)p * N + n);
-                S[i][4 * q + 0] = v.x;
-                S[i][4 * q + 1] = v.y;
-                S[i][4 * q + 2] = v.z;
-                S[i][4 * q + 3] = v.w;
-            }
-        }
-        uint4 xs[XP16], bs[BP16];
-        load_stage(0, xs, bs);
-#pragma unroll
-        for (int i = 0; i < TPP; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                S[i][r] = S[i][r] * dec;
-        for (int ks = 0; ks < nks; ++ks) {
-            // rows 16 ks .. +15 of the chunk: buffer below k, the token at k,
-            // zeros past the chunk
-#pragma unroll
-            for (int i = 0; i < XP16; ++i) {
-                const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
-                *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
-                    keep_if(16 * ks + r <= k, xs[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < BP16; ++i) {
-                const int e = lane + 64 * i, r = e / (N / 8), q = e % (N / 8);
-                *reinterpret_cast<uint4 *>(lds + L.B + (r * L.BS + 8 * q) * 2) =
-                    keep_if(16 * ks + r <= k, bs[i]);
-            }
-            if (ks + 1 < nks)
-                load_stage(ks + 1, xs, bs);
-            const int r0 = 16 * ks + 8 * gl;
-            const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
-            const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
-            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            bf16x8 bhi[NPT], blo[NPT];
-#pragma unroll
-            for (int pt = 0; pt < NPT; ++pt)
-                split_wx(lds_tr8(lds, L.X, L.XS, 8 * gl, 8 * gl + 4,
-                                 32 * pt + 16 * ((lane >> 4) & 1)),
-                         ws, bhi[pt], blo[pt]);
-#pragma unroll
-            for (int i = 0; i < TPP; ++i) {
-                const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
-                const bf16x8 aop = as_bf16x8(
-                    lds_tr8(lds, L.B, L.BS, 8 * gl, 8 * gl + 4, 32 * nt + 16 * ((lane >> 4) & 1)));
-                state_step(aop, bhi[pt], blo[pt], S[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < TPP; ++i) {
-            const int ti = pass * TPP + i, pt = ti % NPT, nt = ti / NPT;
-            const int p = 32 * pt + c;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = 32 * nt + 8 * q + 4 * gl;
-                *reinterpret_cast<float4 *>(st + (int64_t)p * N + n) =
-                    make_float4(S[i][4 * q], S[i][4 * q + 1], S[i][4 * q + 2], S[i][4 * q + 3]);
-                *reinterpret_cast<uint2 *>(stbf + state_bf_index(p, n, P)) = make_uint2(
-                    bf16_bits(S[i][4 * q]) | ((uint32_t)bf16_bits(S[i][4 * q + 1]) << 16),
-                    bf16_bits(S[i][4 * q + 2]) | ((uint32_t)bf16_bits(S[i][4 * q + 3]) << 16));
             }
         }
     }
@@ -1194,26 +1135,115 @@ void k_decode_mfma(DecodeArgs a) {
     if (h < H)
         decode_front<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all + wave * L.bytes, L, cy);
     __syncthreads();  // C.B^T columns of every wave are in LDS
-    if (h < H)
-        decode_back<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all, L, cy);
-    // Every wave of this workgroup has read buf_len (and used it) by now; the
-    // slot's last workgroup to arrive advances it. The counter needs only
-    // atomicity, no ordering: no workgroup reads what the last one writes
-    // during this launch, and the launch boundary publishes the writes. (An
+    // Every wave of this workgroup has read buf_len (and used it) by now, so
+    // the workgroup counts itself in; the slot's last workgroup to arrive
+    // advances buf_len when it is done. The counter needs only atomicity, no
+    // ordering: no workgroup reads what the last one writes during this
+    // launch, and the launch boundary publishes the writes. (An
     // acquire/release atomic here would write back and invalidate the L2 in
     // every workgroup.)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(a.arrivals + slot, 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == HQ - 1) {
-            __hip_atomic_store(a.arrivals + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a.buf_len[slot] = k + 1 == Q ? 0 : k + 1;
-            if (k + 1 == Q)
-                a.boundary_pos[slot] += Q;
+    int prev = 0;
+    if (threadIdx.x == 0)
+        prev = __hip_atomic_fetch_add(a.work + slot, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    if (h < H)
+        decode_back<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all, L, cy);
+    if (threadIdx.x == 0 && prev == HQ - 1) {
+        __hip_atomic_store(a.work + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.buf_len[slot] = k + 1 == Q ? 0 : k + 1;
+        if (k + 1 == Q) {
+            // the chunk is full: its state update runs in k_decode_commit
+            a.boundary_pos[slot] += Q;
+            int32_t *list = a.work + a.num_slots;
+            const int at = __hip_atomic_fetch_add(list, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+            list[kListHead + at] = slot;
         }
     }
     (void)G;
+}
+
+// Chunk-state update of the slots whose chunk the decode step filled (the
+// list k_decode_commit finds in the cache's work array): one head of one
+// slot per workgroup at a time, with the prefill's chunk arithmetic (the
+// per-row quantities of chunk_scalars, chunk_state_update on 32 x 32 tiles),
+// on the chunk's Q tokens, all in the slot buffer now. Writes the new fp32
+// boundary state and its bf16 copy. The last workgroup to finish empties the
+// list.
+constexpr int kCommitWaves = 4;
+
+template <int P, int N, class DT>
+__global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    using TD = typename DT::T;
+    constexpr int NW = kCommitWaves;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const MLayout L(Qp, P, N);
+    int32_t *list = a.work + a.num_slots;   // count, done counters, slots
+    const int raw = list[0];
+    if (raw == 0)
+        return;
+    // (a count outside [0, num_slots] means the work array was not zeroed:
+    // nothing is processed and the counters are cleared)
+    const int count = raw > 0 && raw <= a.num_slots ? raw : 0;
+    if (count == 0) {
+        if (blockIdx.x == 0 && threadIdx.x < kListHead)
+            list[threadIdx.x] = 0;
+        return;
+    }
+    const int64_t PN = (int64_t)P * N;
+    for (int e = blockIdx.x; e < count * H; e += gridDim.x) {
+        const int slot = list[kListHead + e / H], h = e % H, g = h / (H / G);
+        if (slot < 0 || slot >= a.num_slots)
+            continue;
+        const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+        const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
+        const TD *bdt = static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+        float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
+        f32x16 S[StateTiles<P, N, NW>::per_wave];
+        state_io<P, N, NW, true>(st, S);
+        const float dt_raw = DT::ld(bdt, (int64_t)(threadIdx.x < Q ? threadIdx.x : 0) * H + h);
+        __syncthreads();  // the previous entry's LDS reads are done
+        stage_rows<P / 8, N / 8>(bx + h * P, (int64_t)H * P, bB + g * N, (int64_t)G * N, Qp, Q,
+                                 lds + L.X, L.XS, lds + L.B, L.BS);
+        chunk_scalars(dt_raw, Q, a.A[h] * kLog2e, a.dt_bias ? a.dt_bias[h] : 0.0f, d.softplus,
+                      true, lds, L);
+        __syncthreads();
+        chunk_state_update<P, N, NW>(Qp, Q, lds, L, S);
+        state_io<P, N, NW, false>(st, S);
+        state_to_lds<P, N, NW>(lds, L, S);
+        __syncthreads();
+        state_bf_from_lds<P, N>(static_cast<uint16_t *>(a.cache_state_bf) +
+                                    ((int64_t)slot * H + h) * PN,
+                                lds, L);
+    }
+    // The workgroups that had entries ([0, W)) count themselves out, in 32
+    // groups (blockIdx % 32) and then once per group, so that no counter
+    // takes many atomics; the last one empties the list. Workgroups past W
+    // touch nothing (a late one may find the list already empty).
+    const int W = count * H < (int)gridDim.x ? count * H : (int)gridDim.x;
+    if (blockIdx.x >= W)
+        return;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int grp = blockIdx.x % kDoneGroups;
+        const int members = (W - grp + kDoneGroups - 1) / kDoneGroups;
+        int32_t *sub = list + 2 + grp;
+        if (__hip_atomic_fetch_add(sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            members - 1) {
+            __hip_atomic_store(sub, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int groups = W < kDoneGroups ? W : kDoneGroups;
+            if (__hip_atomic_fetch_add(list + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                groups - 1) {
+                for (int i = 0; i < count; ++i)
+                    list[kListHead + i] = 0;
+                __hip_atomic_store(list + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(list, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 template <class K>
@@ -1242,6 +1272,12 @@ hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
         return e;
     const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
     k_decode_mfma<P, N, DT><<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const MLayout LC(Qp, P, N);
+    if ((e = set_lds(k_decode_commit<P, N, DT>, LC.bytes)) != hipSuccess)
+        return e;
+    k_decode_commit<P, N, DT><<<dim3(kCommitGroups), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -97,10 +97,13 @@ typedef struct {
  *   buf_len       [num_slots] int32        tokens buffered, in [0, Q)
  *   boundary_pos  [num_slots] int64        sequence position of the boundary,
  *                                          a multiple of Q
- *   arrivals      [num_slots] int32        decode bookkeeping: the workgroups
- *                                          of a slot count themselves in and
- *                                          the last one advances buf_len; zero
- *                                          between calls
+ *   work          [2*num_slots+34] int32   decode bookkeeping: per-slot
+ *                                          arrival counters (the last
+ *                                          workgroup of a slot advances
+ *                                          buf_len) and the list of slots whose
+ *                                          chunk filled in this step; zero
+ *                                          before first use, and every call
+ *                                          leaves it zero
  * A fresh slot is all zeros. The struct itself is a host object; the
  * pointers in it are device pointers. */
 typedef struct {
@@ -112,7 +115,7 @@ typedef struct {
     void *buf_C;
     int32_t *buf_len;
     int64_t *boundary_pos;
-    int32_t *arrivals;
+    int32_t *work;
     int32_t num_slots;
     int32_t chunk_size;
     int32_t state_dtype;

@@ -113,4 +113,4 @@ def cache_consistent(cache) -> bool:
     (torch's float32 -> bfloat16 conversion), and the decode bookkeeping
     counters are back to zero."""
     return (same_bits(cache.state_bf_rowmajor(), cache.state.to(torch.bfloat16))
-            and int(cache.arrivals.abs().sum()) == 0)
+            and int(cache.work.abs().sum()) == 0)

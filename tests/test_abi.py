@@ -52,10 +52,11 @@ def test_cache_bytes_match_printed_memory():
     total = erd.ssd_replay_cache_bytes(sh, 1, with_C=True)
     state = 32 * 64 * 128 * 4
     state_bf = 32 * 64 * 128 * 2      # bf16 copy of the state (read-out operand)
-    buf = total - state - state_bf - 4 - 4 - 8
+    buf = total - state - state_bf - 3 * 4 - 8 - 34 * 4
     assert state / 2 ** 20 == g["fp32_state_mib_per_layer_per_seq"]["value"]
     assert round(buf / 2 ** 20, 2) == g["buffer_mib_per_layer_per_seq"]["value"]
-    assert erd.ssd_replay_cache_bytes(sh, 27, with_C=True) == 27 * total
+    # per slot, plus two shared bookkeeping words
+    assert erd.ssd_replay_cache_bytes(sh, 27, with_C=True) == 27 * (total - 136) + 136
     # the scan never reads buffered C: without it the buffer shrinks by G*N*2*Q
     assert total - erd.ssd_replay_cache_bytes(sh, 1, with_C=False) == 256 * 128 * 2
 
@@ -107,7 +108,7 @@ def test_prefill_rejects_bad_seqlens_and_nulls():
 
 def cache(sh_c, **kw):
     base = dict(state=0x1000, state_bf=0x1000, buf_x=0x1000, buf_dt=0x1000, buf_B=0x1000,
-                buf_C=None, buf_len=0x1000, boundary_pos=0x1000, arrivals=0x1000, num_slots=4,
+                buf_C=None, buf_len=0x1000, boundary_pos=0x1000, work=0x1000, num_slots=4,
                 chunk_size=16, state_dtype=0)
     base.update(kw)
     return _lib.ssd_replay_cache(**base)
@@ -125,7 +126,7 @@ def test_replay_fails_closed():
     assert decode(sh, cache(sh, chunk_size=32)) == -5        # chunk mismatch
     assert decode(sh, cache(sh, buf_B=None)) == -1
     assert decode(sh, cache(sh, state_bf=None)) == -1
-    assert decode(sh, cache(sh, arrivals=None)) == -1
+    assert decode(sh, cache(sh, work=None)) == -1
     assert decode(sh, cache(sh, state_bf=0x1008)) == -9      # misaligned
     lib = _lib.load()
     assert lib.ssd_replay_cache_refresh(ctypes.byref(sh), ctypes.byref(cache(sh, state=None)),
