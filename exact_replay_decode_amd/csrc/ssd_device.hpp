@@ -86,17 +86,29 @@ __device__ __forceinline__ float state_weight(float lam_last, float lam_j, float
 
 // ---- prefix-consistent inclusive scan -------------------------------------
 // Lane t's result depends only on the values of lanes 0..t and on a fixed
-// combination tree: a Hillis-Steele scan inside each 64-lane wave, then the
-// totals of the earlier waves added in ascending order.
+// combination tree: a DPP scan inside each 64-lane wave, then the totals of
+// the earlier waves added in ascending order.
 
+// v from lane (DPP control CTRL) of the rows enabled in ROW_MASK; 0 where
+// the source lane is outside the row or the row is not enabled.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_from(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Within each 16-lane row: add the value 1, 2, 4, 8 lanes below (row_shr);
+// then rows 1 and 3 add lane 15 of the row below (row_bcast:15) and rows 2
+// and 3 add lane 31 (row_bcast:31). Lane t reads only lanes below t. (Adding
+// the 0 of a lane without a source leaves the value unchanged: the summands
+// are finite and never -0.)
 __device__ __forceinline__ float wave_scan_inclusive(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (lane >= off)
-            v = v + o;
-    }
+    v = v + dpp_from<0x111, 0xf>(v);
+    v = v + dpp_from<0x112, 0xf>(v);
+    v = v + dpp_from<0x114, 0xf>(v);
+    v = v + dpp_from<0x118, 0xf>(v);
+    v = v + dpp_from<0x142, 0xa>(v);
+    v = v + dpp_from<0x143, 0xc>(v);
     return v;
 }
 

@@ -437,40 +437,24 @@ struct MView {
 // Register-staged copy of a chunk's X / B rows and raw dt, loaded one chunk
 // ahead by the prefill workgroup (NT threads) so the global-load latency
 // overlaps the previous chunk's matrix work.
-template <int P, int N, int NT>
+template <int P, int N, int NT, class DT>
 struct ChunkRegs {
-    static constexpr int XC = P / 8, BC = N / 8;
+    static constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
     static constexpr int XPT = (kMaxQ * XC + NT - 1) / NT;
     static constexpr int BPT = (kMaxQ * BC + NT - 1) / NT;
     uint4 x[XPT], b[BPT];
-    float dt;
+    typename DT::T dt;   // raw (converted where it is used)
 };
 
+// One code path for every chunk shape, branch-free: each piece's source is
+// selected (buffer rows below nb, input tokens after; pieces past the chunk
+// read row 0 and are zeroed when stored), so the loads stay in flight until
+// their values are used.
 template <int P, int N, int NT, class DT>
 __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
-                                                ChunkRegs<P, N, NT> &r) {
-    using CR = ChunkRegs<P, N, NT>;
+                                                ChunkRegs<P, N, NT, DT> &r) {
+    using CR = ChunkRegs<P, N, NT, DT>;
     const int tid = threadIdx.x;
-    if (v.nb == 0 && v.n_valid == rows) {
-        // every row is an input token: fixed row stride, no clamping
-        const int64_t xs = (int64_t)(NT / CR::XC) * v.H * P;
-        const uint16_t *xp = v.x + (v.token(tid / CR::XC) * v.H + v.h) * P + 8 * (tid % CR::XC);
-#pragma unroll
-        for (int i = 0; i < CR::XPT; ++i)
-            if (tid + NT * i < rows * CR::XC)
-                r.x[i] = *reinterpret_cast<const uint4 *>(xp + i * xs);
-        const int64_t bs = (int64_t)(NT / CR::BC) * v.G * N;
-        const uint16_t *bp = v.B + (v.token(tid / CR::BC) * v.G + v.g) * N + 8 * (tid % CR::BC);
-#pragma unroll
-        for (int i = 0; i < CR::BPT; ++i)
-            if (tid + NT * i < rows * CR::BC)
-                r.b[i] = *reinterpret_cast<const uint4 *>(bp + i * bs);
-        r.dt = DT::ld(v.dt, v.token(tid < rows ? tid : 0) * v.H + v.h);
-        return;
-    }
-    // General chunk, branch-free: every lane loads a valid row (rows past
-    // the chunk read row 0) so the loads stay in flight together;
-    // store_chunk_regs zeroes the lanes that are not chunk rows.
 #pragma unroll
     for (int i = 0; i < CR::XPT; ++i) {
         const int e = tid + NT * i, q = e % CR::XC;
@@ -490,8 +474,7 @@ __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
         r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
     const int jd = tid < v.n_valid ? tid : 0;
-    r.dt = jd < v.nb ? DT::ld(v.bdt, (int64_t)jd * v.H + v.h)
-                     : DT::ld(v.dt, v.token(jd) * v.H + v.h);
+    r.dt = jd < v.nb ? v.bdt[(int64_t)jd * v.H + v.h] : v.dt[v.token(jd) * v.H + v.h];
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -540,12 +523,12 @@ __device__ __forceinline__ void chunk_scalars(float dt_raw, int n_valid, float A
 }
 
 // LDS copy of the register-staged chunk, then chunk_scalars.
-template <int P, int N, int NT>
-__device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, int rows,
+template <int P, int N, int NT, class DT>
+__device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT, DT> &r, int rows,
                                                  int n_valid, float A2_h, float bias,
                                                  int softplus, bool weights, char *lds,
                                                  const MLayout &L) {
-    using CR = ChunkRegs<P, N, NT>;
+    using CR = ChunkRegs<P, N, NT, DT>;
     const int tid = threadIdx.x;
     const bool full = n_valid == rows;
 #pragma unroll
@@ -563,7 +546,7 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT> &r, i
                 full ? r.b[i] : keep_if(j < n_valid, r.b[i]);
     }
     // (a thread past the chunk loaded row 0's dt; chunk_scalars ignores it)
-    chunk_scalars(r.dt, n_valid, A2_h, bias, softplus, weights, lds, L);
+    chunk_scalars(DT::val(r.dt), n_valid, A2_h, bias, softplus, weights, lds, L);
 }
 
 // Rows [0, rows) of the chunk's x (CX 16-byte pieces per row) and B (CB
@@ -602,7 +585,9 @@ __device__ __forceinline__ void stage_rows(const uint16_t *xs, int64_t xstride,
 }
 
 // C fragments of t-block tau: lane gets C[t][16k + 8g .. +7] for rows t that
-// produce output (t in [row_lo, n_valid)), zeros otherwise.
+// produce output (t in [row_lo, n_valid)), zeros otherwise. When every row
+// of the t-block is an output row the loaded values are used as they are,
+// so nothing waits for the loads before the first MFMA that reads them.
 template <int N, class DT>
 __device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_lo,
                                            bf16x8 (&cf)[N / 16]) {
@@ -610,15 +595,22 @@ __device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, t = 32 * tau + (lane & 31);
     const bool ok = t >= row_lo && t < v.n_valid && t >= v.nb;
+    const bool all = row_lo <= 32 * tau && 32 * tau + 32 <= v.n_valid && v.nb <= 32 * tau;
     const int tt = ok ? t : row_lo;
     const uint16_t *src = v.C + (v.token(tt) * v.G + v.g) * N;
     uint4 raw[N / 16];
 #pragma unroll
     for (int k = 0; k < N / 16; ++k)
         raw[k] = *reinterpret_cast<const uint4 *>(src + 16 * k + 8 * g);
+    if (all) {
 #pragma unroll
-    for (int k = 0; k < N / 16; ++k)
-        cf[k] = __builtin_bit_cast(bf16x8, keep_if(ok, raw[k]));
+        for (int k = 0; k < N / 16; ++k)
+            cf[k] = __builtin_bit_cast(bf16x8, raw[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k)
+            cf[k] = __builtin_bit_cast(bf16x8, keep_if(ok, raw[k]));
+    }
 }
 
 // y rows [row_lo, row_hi) of t-block tau: y = fmaf(D, x, acc), -0 -> +0.
@@ -704,6 +696,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
                                            : nullptr);
     f32x16 S[StateTiles<P, N, NW>::per_wave];
     state_io<P, N, NW, true>(init, S);
+    // the initial state is in registers before the chunk loop starts (so no
+    // wait inside the loop has to account for these loads)
+    wait_vmcnt<0>();
     state_to_lds<P, N, NW>(lds, L, S);
 
     MView<DT> v;
@@ -737,7 +732,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
     };
 
-    ChunkRegs<P, N, 64 * NW> regs;
+    ChunkRegs<P, N, 64 * NW, DT> regs;
     if (nchunks > 0) {
         set_chunk(0);
         load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
@@ -752,7 +747,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
         __syncthreads();  // previous chunk's LDS reads (and S_bf writes) are done
         if (mirror)  // S_bf in LDS is the bf16 copy of the state just stored
             state_bf_from_lds<P, N>(bnd_bf, lds, L);
-        store_chunk_regs<P, N, 64 * NW>(regs, Qp, n_valid, A2_h, bias, d.softplus, upd, lds, L);
+        store_chunk_regs<P, N, 64 * NW, DT>(regs, Qp, n_valid, A2_h, bias, d.softplus, upd, lds,
+                                            L);
         __syncthreads();
         const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, n_valid);
         const bool has_rows = tau >= 0 && lo < hi;
