@@ -255,7 +255,11 @@ template <int P, int N, int NW>
 struct StateTiles {
     static constexpr int NPT = P / 32, NNT = N / 32;
     static constexpr int total = NPT * NNT;
-    static constexpr bool paired = false;  // pairing raises register pressure past 256 VGPRs
+    // Pairing needs the n-tiles to pair up and half the waves to hold them
+    // (the other waves then own no tile). It is off: with two tiles per
+    // wave the prefill kernel spills registers, for no measured gain.
+    static constexpr bool kPairTiles = false;
+    static constexpr bool paired = kPairTiles && NNT % 2 == 0 && total / 2 <= NW;
     static constexpr int per_wave = paired ? 2 : (total + NW - 1) / NW;
     __device__ static __forceinline__ bool tile(int w, int i, int &pt, int &nt) {
         if (paired) {
