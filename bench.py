@@ -66,8 +66,8 @@ def replay_step_bytes(ks, Q, H, G, P, N, io=2, dtb=2, with_C=False):
     """Algorithmic bytes of one replay-decode step for buffer fills ks: the
     bf16 copy of the boundary state (the read-out operand), the buffered
     tokens' x, B and raw dt, the new token, its append and y; when the token
-    fills the chunk, the fp32 state is read and written and its bf16 copy
-    written."""
+    fills the chunk, the chunk-state update reads the fp32 state and the
+    chunk's tokens and writes the new state and its bf16 copy."""
     ks = np.asarray(ks, dtype=np.int64)
     state_bf = H * P * N * 2
     per_buf_tok = H * P * io + G * N * io + H * dtb          # x, B, raw dt re-read
@@ -75,8 +75,10 @@ def replay_step_bytes(ks, Q, H, G, P, N, io=2, dtb=2, with_C=False):
     append = H * P * io + H * dtb + G * N * io * (2 if with_C else 1)
     y = H * P * io
     commits = int(np.sum(ks + 1 == Q))
+    # a commit reads the fp32 state and the chunk's Q buffered tokens, and
+    # writes the new fp32 state and its bf16 copy
     return int(len(ks) * (state_bf + new_tok + append + y) + ks.sum() * per_buf_tok
-               + commits * H * P * N * (4 + 4 + 2))
+               + commits * (H * P * N * (4 + 4 + 2) + Q * per_buf_tok))
 
 
 def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):

@@ -31,6 +31,8 @@
 //
 // LDS tiles are row-major with 16 bytes of padding per row; operands that
 // contract over tokens are fetched transposed with ds_read_b64_tr_b16.
+#include <algorithm>
+
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 
@@ -811,9 +813,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
 // chunk-state update of those slots with the prefill's own chunk routines.
 constexpr int kDecodeWaves = 4;
 
-// Workgroups of the chunk-commit kernel (each handles one head of a full
-// chunk at a time; when no chunk filled they return at once).
-constexpr int kCommitGroups = 1024;
+// Workgroups of the chunk-commit kernel: as many as fit on the device at
+// once (compute units x workgroups per unit that the LDS allows, at most 4),
+// each handling one head of a full chunk at a time; when no chunk filled
+// they return at once, in one dispatch round.
+constexpr int kLdsBytesPerCu = 160 * 1024;
 // The work array after the per-slot arrival counters: [0] number of slots
 // on the commit list, [1] finished groups, [2, 2 + kDoneGroups) finished
 // workgroups per group, then the list itself.
@@ -1277,7 +1281,13 @@ hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
     const MLayout LC(Qp, P, N);
     if ((e = set_lds(k_decode_commit<P, N, DT>, LC.bytes)) != hipSuccess)
         return e;
-    k_decode_commit<P, N, DT><<<dim3(kCommitGroups), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return e;
+    const int per_cu = std::max(1, std::min(4, kLdsBytesPerCu / (int)LC.bytes));
+    k_decode_commit<P, N, DT>
+        <<<dim3(std::max(1, cus) * per_cu), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
     return hipGetLastError();
 }
 
