@@ -22,7 +22,8 @@ STATUS = {
 # every symbol include/ssd_replay.h declares
 EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
-           "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh")
+           "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
+           "ssd_replay_page_bytes")
 
 
 class ssd_shape(ctypes.Structure):
@@ -38,7 +39,9 @@ class ssd_replay_cache(ctypes.Structure):
                 ("buf_B", ctypes.c_void_p), ("buf_C", ctypes.c_void_p),
                 ("buf_len", ctypes.c_void_p), ("boundary_pos", ctypes.c_void_p),
                 ("work", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
-                ("chunk_size", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
+                ("chunk_size", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("buf_pages", ctypes.c_void_p), ("page_tokens", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -65,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.ssd_prefill_varlen.restype = ctypes.c_int
     lib.ssd_prefill_varlen.argtypes = [shp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_replay_page_bytes.restype = sz
+    lib.ssd_replay_page_bytes.argtypes = [shp, i32, i32]
     lib.ssd_replay_cache_refresh.restype = ctypes.c_int
     lib.ssd_replay_cache_refresh.argtypes = [shp, cp, vp]
     lib.ssd_commit_boundary.restype = ctypes.c_int

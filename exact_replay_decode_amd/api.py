@@ -91,24 +91,39 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, device):
 class ReplayCache:
     """Exact-replay cache for num_slots sequences: fp32 boundary state (and
     its bf16 copy, the read-out operand) plus the partial-chunk token buffers
-    (all zeros = every slot fresh)."""
+    (all zeros = every slot fresh).
+
+    With page_tokens, the buffers are pools of num_pages pages of page_tokens
+    rows, and `buf_pages` [num_slots, Q / page_tokens] (int32, -1 = no page)
+    says which page holds each slot's positions; the caller fills it."""
 
     def __init__(self, shape: Shape, num_slots: int, device="cuda", with_C: bool = False,
-                 state_dtype: torch.dtype = torch.float32, _empty: bool = False):
+                 state_dtype: torch.dtype = torch.float32, _empty: bool = False,
+                 page_tokens: int | None = None, num_pages: int | None = None):
         H, G, P, N, Q = shape.H, shape.G, shape.P, shape.N, shape.chunk_size
         self.shape = shape
         self.num_slots = num_slots
         self.device = torch.device(device)
+        self.page_tokens = page_tokens
+        self.num_pages = num_pages
         mk = torch.empty if _empty else torch.zeros
         self.state = mk((num_slots, H, P, N), dtype=state_dtype, device=self.device)
         # bf16 copy of the state in the read-out operand order [N/16, P, 16]
         self.state_bf = mk((num_slots, H, N // 16, P, 16), dtype=torch.bfloat16,
                            device=self.device)
-        self.buf_x = mk((num_slots, Q, H, P), dtype=shape.io, device=self.device)
-        self.buf_dt = mk((num_slots, Q, H), dtype=shape.dtt, device=self.device)
-        self.buf_B = mk((num_slots, Q, G, N), dtype=shape.io, device=self.device)
-        self.buf_C = (mk((num_slots, Q, G, N), dtype=shape.io, device=self.device)
-                      if with_C else None)
+        if page_tokens is None:
+            lead = (num_slots, Q)
+            self.buf_pages = None
+        else:
+            if not num_pages or Q % page_tokens:
+                raise ValueError("paged cache: need num_pages > 0 and page_tokens dividing Q")
+            lead = (num_pages, page_tokens)
+            self.buf_pages = torch.full((num_slots, Q // page_tokens), -1, dtype=torch.int32,
+                                        device=self.device)
+        self.buf_x = mk(lead + (H, P), dtype=shape.io, device=self.device)
+        self.buf_dt = mk(lead + (H,), dtype=shape.dtt, device=self.device)
+        self.buf_B = mk(lead + (G, N), dtype=shape.io, device=self.device)
+        self.buf_C = mk(lead + (G, N), dtype=shape.io, device=self.device) if with_C else None
         self.buf_len = mk((num_slots,), dtype=torch.int32, device=self.device)
         self.boundary_pos = mk((num_slots,), dtype=torch.int64, device=self.device)
         # decode bookkeeping, zero between calls (always allocated zeroed)
@@ -116,12 +131,38 @@ class ReplayCache:
 
     def struct(self) -> _lib.ssd_replay_cache:
         sd = _lib.SSD_F32 if self.state.dtype == torch.float32 else _lib.SSD_BF16
+        paged = self.buf_pages is not None
         return _lib.ssd_replay_cache(
             self.state.data_ptr(), self.state_bf.data_ptr(), self.buf_x.data_ptr(),
             self.buf_dt.data_ptr(), self.buf_B.data_ptr(),
             None if self.buf_C is None else self.buf_C.data_ptr(),
             self.buf_len.data_ptr(), self.boundary_pos.data_ptr(), self.work.data_ptr(),
-            self.num_slots, self.shape.chunk_size, sd)
+            self.num_slots, self.shape.chunk_size, sd,
+            self.buf_pages.data_ptr() if paged else None,
+            self.page_tokens if paged else 0, self.num_pages if paged else 0)
+
+    def buffers_by_slot(self):
+        """The buffers as [num_slots, Q, ...] (x, dt, B, C or None): for a paged
+        cache, position j of a slot read through its page table (zeros where
+        the entry is not a page)."""
+        bufs = (self.buf_x, self.buf_dt, self.buf_B, self.buf_C)
+        if self.buf_pages is None:
+            return bufs
+        pt, Q = self.page_tokens, self.shape.chunk_size
+        pos = torch.arange(Q, device=self.device)
+        pg = self.buf_pages.long()[:, pos // pt]                      # [slots, Q]
+        ok = (pg >= 0) & (pg < self.num_pages)
+        rows = torch.where(ok, pg * pt + pos % pt, torch.zeros_like(pg))
+        out = []
+        for t in bufs:
+            if t is None:
+                out.append(None)
+                continue
+            flat = t.reshape((-1,) + tuple(t.shape[2:]))
+            g = flat[rows.reshape(-1)].reshape(rows.shape + tuple(t.shape[2:]))
+            mask = ok.reshape(ok.shape + (1,) * (g.dim() - 2))
+            out.append(torch.where(mask, g, torch.zeros_like(g)))
+        return tuple(out)
 
     def state_bf_rowmajor(self) -> torch.Tensor:
         """The bf16 state copy as [num_slots, H, P, N]."""
@@ -137,12 +178,14 @@ class ReplayCache:
 
     def tensors(self):
         return [t for t in (self.state, self.state_bf, self.buf_x, self.buf_dt, self.buf_B,
-                            self.buf_C, self.buf_len, self.boundary_pos, self.work)
+                            self.buf_C, self.buf_len, self.boundary_pos, self.work,
+                            self.buf_pages)
                 if t is not None]
 
     def clone(self) -> "ReplayCache":
         c = ReplayCache(self.shape, self.num_slots, self.device, self.buf_C is not None,
-                        self.state.dtype, _empty=True)
+                        self.state.dtype, _empty=True, page_tokens=self.page_tokens,
+                        num_pages=self.num_pages)
         for dst, src in zip(c.tensors(), self.tensors()):
             dst.copy_(src)
         return c
@@ -155,6 +198,11 @@ class ReplayCache:
 def ssd_replay_cache_bytes(shape: Shape, num_slots: int, with_C: bool = True) -> int:
     c = shape.c()
     return int(_lib.load().ssd_replay_cache_bytes(ctypes.byref(c), num_slots, int(with_C)))
+
+
+def ssd_replay_page_bytes(shape: Shape, page_tokens: int, with_C: bool = True) -> int:
+    c = shape.c()
+    return int(_lib.load().ssd_replay_page_bytes(ctypes.byref(c), page_tokens, int(with_C)))
 
 
 def _slots(slot_idx, n, device):

@@ -80,9 +80,29 @@ int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
         return SSD_ERR_NULL;
     if (c->num_slots <= 0)
         return SSD_ERR_SHAPE;
+    if (c->buf_pages) {
+        const int pt = c->page_tokens;
+        if (pt < 16 || pt > c->chunk_size || (pt & (pt - 1)) != 0 || c->num_pages <= 0)
+            return SSD_ERR_SHAPE;
+    }
     if (!all_a16(c->state, c->state_bf, c->buf_x, c->buf_B, c->buf_C))
         return SSD_ERR_ALIGN;
     return SSD_OK;
+}
+
+// Buffer addressing of a checked cache.
+ssd::BufMap buf_map(const ssd_replay_cache *c) {
+    ssd::BufMap m = {};
+    if (c->buf_pages) {
+        m.pages = c->buf_pages;
+        int sh = 0;
+        while ((1 << sh) < c->page_tokens)
+            ++sh;
+        m.shift = sh;
+        m.npp = c->chunk_size >> sh;
+        m.num_pages = c->num_pages;
+    }
+    return m;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
@@ -127,6 +147,17 @@ size_t ssd_replay_cache_bytes(const ssd_shape *sh, int32_t num_slots, int32_t wi
     const size_t per_slot =
         state + (size_t)d.Q * per_tok + 3 * sizeof(int32_t) + sizeof(int64_t);
     return per_slot * (size_t)num_slots + 34 * sizeof(int32_t);
+}
+
+size_t ssd_replay_page_bytes(const ssd_shape *sh, int32_t page_tokens, int32_t with_C) {
+    Dims d;
+    if (check_shape(sh, &d) != SSD_OK || page_tokens < 16 || page_tokens > d.Q ||
+        (page_tokens & (page_tokens - 1)) != 0)
+        return 0;
+    const size_t io = dtype_bytes(sh->io_dtype), dtb = dtype_bytes(sh->dt_dtype);
+    const size_t per_tok = (size_t)d.H * d.P * io + (size_t)d.H * dtb +
+                           (with_C ? 2 : 1) * (size_t)d.G * d.N * io;
+    return per_tok * (size_t)page_tokens;
 }
 
 int ssd_replay_cache_refresh(const ssd_shape *sh, const ssd_replay_cache *cache,
@@ -221,6 +252,7 @@ int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t
     a.buf_B = cache->buf_B; a.buf_C = cache->buf_C;
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
+    a.bm = buf_map(cache);
     return hip_status(ssd::launch_commit(a, (hipStream_t)stream));
 }
 
@@ -259,6 +291,7 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
     a.cache_state_bf = cache->state_bf;
     a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
     a.buf_len = cache->buf_len;
+    a.bm = buf_map(cache);
     hipError_t e = launch_scan_any(a, (hipStream_t)stream);
     if (e != hipSuccess)
         return SSD_ERR_HIP;
@@ -277,6 +310,7 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
     c.buf_B = cache->buf_B; c.buf_C = cache->buf_C;
     c.buf_len = cache->buf_len;
     c.boundary_pos = cache->boundary_pos;
+    c.bm = a.bm;
     return hip_status(ssd::launch_commit(c, (hipStream_t)stream));
 }
 
@@ -314,6 +348,7 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
     a.work = cache->work;
+    a.bm = buf_map(cache);
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
 }

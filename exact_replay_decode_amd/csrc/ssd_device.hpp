@@ -56,6 +56,15 @@ __host__ __device__ __forceinline__ int64_t state_bf_index(int p, int n, int P) 
     return (int64_t)(n >> 4) * 16 * P + 16 * p + (n & 15);
 }
 
+// Buffer positions a replay prefill or commit of len new tokens touches in
+// a slot holding nbuf: it reads [0, nbuf) and writes the trailing partial
+// chunk.
+__host__ __device__ __forceinline__ int replay_npos(int nbuf, int len, int Q) {
+    const int total = nbuf + len;
+    const int tail = total % Q;
+    return total < Q ? total : (nbuf > tail ? nbuf : tail);
+}
+
 // ---- scalar functions that fix the rounding ------------------------------
 
 // delta = softplus(dt + bias) computed as log1p(exp(u)) for u <= 0 and

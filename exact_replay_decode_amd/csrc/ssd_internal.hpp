@@ -15,6 +15,16 @@ struct Dims {
     int32_t softplus;
 };
 
+// Where buffered position j of a slot lives in the buffer arrays: row
+// slot * Q + j (contiguous), or row page * page_tokens + j % page_tokens
+// with page = pages[slot * npp + j / page_tokens] (paged pool).
+struct BufMap {
+    const int32_t *pages;     // [slots, npp] or null = contiguous
+    int32_t shift;            // log2(page_tokens)
+    int32_t npp;              // pages per slot, Q / page_tokens
+    int32_t num_pages;        // pages in the pool
+};
+
 // One chunked-scan launch over S sequences, plain or replay.
 struct ScanArgs {
     Dims d;
@@ -35,6 +45,7 @@ struct ScanArgs {
     void *cache_state_bf;     // [slots,H,P,N] bf16 copy of cache_state
     const void *buf_x, *buf_dt, *buf_B;
     const int32_t *buf_len;   // [slots]
+    BufMap bm;
 };
 
 // Write the trailing partial chunk of each sequence into the slot buffers
@@ -53,6 +64,7 @@ struct CommitArgs {
     void *buf_x, *buf_dt, *buf_B, *buf_C;  // buf_C may be null
     int32_t *buf_len;
     int64_t *boundary_pos;
+    BufMap bm;
 };
 
 struct DecodeArgs {
@@ -70,6 +82,7 @@ struct DecodeArgs {
     int64_t *boundary_pos;
     int32_t *work;            // [2*slots+34]: arrival counters [slots], commit-list
                               // count and done counters [34], commit list [slots]
+    BufMap bm;
 };
 
 struct SsuArgs {

@@ -425,15 +425,52 @@ __device__ __forceinline__ void state_bf_from_lds(uint16_t *gbf, const char *lds
     }
 }
 
+// Buffer row of buffered position j of one slot, for one wave.
+// Contiguous buffers: row slot * Q + j. Paged buffers: lane i holds the
+// slot's page-table entry i (entries repeat across the wave) and a lookup
+// is one lane shuffle, so no lookup waits on memory; every lane of the wave
+// must take part in a lookup.
+template <bool PG>
+struct SlotRows;
+
+template <>
+struct SlotRows<false> {
+    int64_t base;
+    SlotRows() = default;
+    __device__ SlotRows(const BufMap &, int slot, int Q) : base((int64_t)slot * Q) {}
+    __device__ bool ok(const BufMap &, int) const { return true; }
+    __device__ int64_t operator()(int j) const { return base + j; }
+};
+
+template <>
+struct SlotRows<true> {
+    int ent, shift;
+    SlotRows() = default;
+    __device__ SlotRows(const BufMap &m, int slot, int) : shift(m.shift) {
+        ent = m.pages[(int64_t)slot * m.npp + ((threadIdx.x & 63) & (m.npp - 1))];
+    }
+    // the entries of positions [0, npos) are pages of the pool (same answer
+    // in every lane)
+    __device__ bool ok(const BufMap &m, int npos) const {
+        const int n = (npos + (1 << shift) - 1) >> shift;
+        const bool bad = (threadIdx.x & 63) < n && (ent < 0 || ent >= m.num_pages);
+        return __ballot(bad) == 0;
+    }
+    __device__ int64_t operator()(int j) const {
+        return ((int64_t)__shfl(ent, j >> shift, 64) << shift) + (j & ((1 << shift) - 1));
+    }
+};
+
 // Chunk positions: [0, nb) from the slot buffer, [nb, n_valid) from the
 // packed input starting at token tok_base; later rows are zero.
-template <class DT>
+template <class DT, bool PG = false>
 struct MView {
     using TD = typename DT::T;
     const uint16_t *x, *B, *C;
     const TD *dt;
-    const uint16_t *bx, *bB;
+    const uint16_t *bx, *bB;   // buffer arrays (whole pool), rows through `rows`
     const TD *bdt;
+    SlotRows<PG> rows;
     int64_t tok_base;
     int nb, n_valid;
     int h, g, H, G;
@@ -456,8 +493,8 @@ struct ChunkRegs {
 // selected (buffer rows below nb, input tokens after; pieces past the chunk
 // read row 0 and are zeroed when stored), so the loads stay in flight until
 // their values are used.
-template <int P, int N, int NT, class DT>
-__device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
+template <int P, int N, int NT, class DT, bool PG>
+__device__ __forceinline__ void load_chunk_regs(const MView<DT, PG> &v, int rows,
                                                 ChunkRegs<P, N, NT, DT> &r) {
     using CR = ChunkRegs<P, N, NT, DT>;
     const int tid = threadIdx.x;
@@ -466,7 +503,8 @@ __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
         const int e = tid + NT * i, q = e % CR::XC;
         int j = e / CR::XC;
         j = (e < rows * CR::XC && j < v.n_valid) ? j : 0;
-        const uint16_t *src = j < v.nb ? v.bx + ((int64_t)j * v.H + v.h) * P
+        const int64_t br = v.rows(j);
+        const uint16_t *src = j < v.nb ? v.bx + (br * v.H + v.h) * P
                                        : v.x + (v.token(j) * v.H + v.h) * P;
         r.x[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
@@ -475,12 +513,14 @@ __device__ __forceinline__ void load_chunk_regs(const MView<DT> &v, int rows,
         const int e = tid + NT * i, q = e % CR::BC;
         int j = e / CR::BC;
         j = (e < rows * CR::BC && j < v.n_valid) ? j : 0;
-        const uint16_t *src = j < v.nb ? v.bB + ((int64_t)j * v.G + v.g) * N
+        const int64_t br = v.rows(j);
+        const uint16_t *src = j < v.nb ? v.bB + (br * v.G + v.g) * N
                                        : v.B + (v.token(j) * v.G + v.g) * N;
         r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
     const int jd = tid < v.n_valid ? tid : 0;
-    r.dt = jd < v.nb ? v.bdt[(int64_t)jd * v.H + v.h] : v.dt[v.token(jd) * v.H + v.h];
+    const int64_t brd = v.rows(jd);
+    r.dt = jd < v.nb ? v.bdt[brd * v.H + v.h] : v.dt[v.token(jd) * v.H + v.h];
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -556,11 +596,12 @@ __device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT, DT> &
 }
 
 // Rows [0, rows) of the chunk's x (CX 16-byte pieces per row) and B (CB
-// pieces per row) from global rows (strides in elements) into the padded LDS
-// tiles; rows past n_valid are zero. Both streams share one index space so
-// that eight pieces per thread are in flight at a time.
-template <int CX, int CB>
-__device__ __forceinline__ void stage_rows(const uint16_t *xs, int64_t xstride,
+// pieces per row) into the padded LDS tiles; chunk row j is global row
+// rmap(j) of xs / bs (strides in elements); rows past n_valid are zero.
+// Both streams share one index space so that eight pieces per thread are in
+// flight at a time.
+template <int CX, int CB, class RM>
+__device__ __forceinline__ void stage_rows(const RM &rmap, const uint16_t *xs, int64_t xstride,
                                            const uint16_t *bs, int64_t bstride, int rows,
                                            int n_valid, char *xdst, int XS, char *bdst, int BS) {
     const int nthr = blockDim.x, tid = threadIdx.x;
@@ -574,8 +615,9 @@ __device__ __forceinline__ void stage_rows(const uint16_t *xs, int64_t xstride,
             const int f = isx ? e : e - nx, C = isx ? CX : CB;
             const int j = f / C, q = f % C;
             const int jj = (e < total && j < n_valid) ? j : 0;
-            v[i] = isx ? *reinterpret_cast<const uint4 *>(xs + jj * xstride + 8 * q)
-                       : *reinterpret_cast<const uint4 *>(bs + jj * bstride + 8 * q);
+            const int64_t gr = rmap(jj);
+            v[i] = isx ? *reinterpret_cast<const uint4 *>(xs + gr * xstride + 8 * q)
+                       : *reinterpret_cast<const uint4 *>(bs + gr * bstride + 8 * q);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -594,8 +636,8 @@ __device__ __forceinline__ void stage_rows(const uint16_t *xs, int64_t xstride,
 // produce output (t in [row_lo, n_valid)), zeros otherwise. When every row
 // of the t-block is an output row the loaded values are used as they are,
 // so nothing waits for the loads before the first MFMA that reads them.
-template <int N, class DT>
-__device__ __forceinline__ void load_cfrag(const MView<DT> &v, int tau, int row_lo,
+template <int N, class DT, bool PG>
+__device__ __forceinline__ void load_cfrag(const MView<DT, PG> &v, int tau, int row_lo,
                                            bf16x8 (&cf)[N / 16]) {
     // rows outside [row_lo, n_valid) load row row_lo and are zeroed after
     const int lane = threadIdx.x & 63;
@@ -672,7 +714,7 @@ __device__ __forceinline__ int wave_tblock(int nT, int wave) {
     return wave < nT ? wave : -1;
 }
 
-template <int P, int N, class DT>
+template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using TD = typename DT::T;
@@ -695,6 +737,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     const int nbuf = a.replay ? a.buf_len[slot] : 0;
     if (nbuf < 0 || nbuf >= Q)
         return;
+    const SlotRows<PG> rows(a.bm, slot, Q);
+    if (!rows.ok(a.bm, replay_npos(nbuf, len, Q)))
+        return;
 
     float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                            : (a.init_state ? const_cast<float *>(a.init_state) +
@@ -707,14 +752,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     wait_vmcnt<0>();
     state_to_lds<P, N, NW>(lds, L, S);
 
-    MView<DT> v;
+    MView<DT, PG> v;
     v.x = static_cast<const uint16_t *>(a.x);
     v.B = static_cast<const uint16_t *>(a.B);
     v.C = static_cast<const uint16_t *>(a.C);
     v.dt = static_cast<const TD *>(a.dt);
-    v.bx = a.replay ? static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P : nullptr;
-    v.bB = a.replay ? static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N : nullptr;
-    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H : nullptr;
+    v.bx = a.replay ? static_cast<const uint16_t *>(a.buf_x) : nullptr;
+    v.bB = a.replay ? static_cast<const uint16_t *>(a.buf_B) : nullptr;
+    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) : nullptr;
+    v.rows = rows;
     v.h = h; v.g = g; v.H = H; v.G = G;
 
     const float A2_h = a.A[h] * kLog2e;
@@ -762,7 +808,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
         if (has_rows)
             load_cfrag<N, DT>(v, tau, lo, cf);
         // next chunk's inputs: in flight during this chunk's matrix work
-        const MView<DT> vc = v;
+        const MView<DT, PG> vc = v;
         if (c + 1 < nchunks) {
             set_chunk(c + 1);
             load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
@@ -852,25 +898,27 @@ struct DecodeCarry {
 // Rows 32 sg .. +31 of the head's x (buffer below k, the token at k; rows
 // after k are loaded from the token and zeroed when stored), as 16-byte
 // pieces lane + 64 i of the row-major tile.
-template <int P>
-__device__ __forceinline__ void load_x_tile(const uint16_t *bx, const uint16_t *xin, int H, int h,
-                                            int k, int sg, uint4 (&xr)[P / 16]) {
+template <int P, bool PG>
+__device__ __forceinline__ void load_x_tile(const uint16_t *bx, const SlotRows<PG> &rows,
+                                            const uint16_t *xin, int H, int h, int k, int sg,
+                                            uint4 (&xr)[P / 16]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < P / 16; ++i) {
         const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
         const int row = 32 * sg + r;
-        const uint16_t *src = row < k ? bx + ((int64_t)row * H + h) * P : xin;
+        const int64_t br = rows(row);
+        const uint16_t *src = row < k ? bx + (br * H + h) * P : xin;
         xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
     }
 }
 
 // Phase 1: the wave's loads, the read-out, the append of the token, the
 // in-chunk scan and the C.B^T columns of the s-blocks this wave owns.
-template <int P, int N, class DT>
-__device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slot, int h, int k,
-                                             int wave, bool gshare, char *lds, const DLayout &L,
-                                             DecodeCarry<P, DT> &cy) {
+template <int P, int N, class DT, bool PG>
+__device__ __forceinline__ void decode_front(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
+                                             int slot, int h, int k, int wave, bool gshare,
+                                             char *lds, const DLayout &L, DecodeCarry<P, DT> &cy) {
     using TD = typename DT::T;
     constexpr int NPT = P / 32, NK = N / 16;
     const Dims d = a.d;
@@ -887,8 +935,9 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
     const uint16_t *Cin = static_cast<const uint16_t *>(a.C) + ((int64_t)b * G + g) * N;
     const TD *dtin = static_cast<const TD *>(a.dt) + (int64_t)b * H + h;
-    const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
-    const TD *bdt = static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+    // buffer arrays (whole pool); position j is row rows(j)
+    const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
+    const TD *bdt = static_cast<const TD *>(a.buf_dt);
     // s-blocks whose C.B^T column this wave computes
     const int sg0 = gshare ? wave : 0, sgs = gshare ? kDecodeWaves : 1;
 
@@ -899,7 +948,8 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
-        rawdt[i] = j < k ? bdt[(int64_t)j * H + h] : dtin[0];
+        const int64_t br = rows(j);
+        rawdt[i] = j < k ? bdt[br * H + h] : dtin[0];
     }
     uint4 xtok = make_uint4(0, 0, 0, 0), btok = make_uint4(0, 0, 0, 0);
     if (lane < P / 8)
@@ -918,7 +968,8 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     }
     auto load_brows = [&](int sg, uint4 (&br)[NK]) {
         const int s = 32 * sg + c;
-        const uint16_t *brow = s < k ? bB + ((int64_t)s * G + g) * N : Bin;
+        const int64_t rs = rows(s);
+        const uint16_t *brow = s < k ? bB + (rs * G + g) * N : Bin;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
             br[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
@@ -940,20 +991,21 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     // append the token at buffer position k now: this step reads only
     // positions < k of the buffer (the token itself comes from the input)
     {
-        uint16_t *bx = static_cast<uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-        uint16_t *bBw = static_cast<uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
-        TD *bdtw = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+        const int64_t rk = rows(k);
+        uint16_t *bx = static_cast<uint16_t *>(a.buf_x);
+        uint16_t *bBw = static_cast<uint16_t *>(a.buf_B);
+        TD *bdtw = static_cast<TD *>(a.buf_dt);
         if (lane < P / 8)
-            *reinterpret_cast<uint4 *>(bx + ((int64_t)k * H + h) * P + 8 * lane) = xtok;
+            *reinterpret_cast<uint4 *>(bx + (rk * H + h) * P + 8 * lane) = xtok;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (lane + 64 * i == k)
-                bdtw[(int64_t)k * H + h] = rawdt[i];
+                bdtw[rk * H + h] = rawdt[i];
         if (h % (H / G) == 0 && lane < N / 8) {
-            *reinterpret_cast<uint4 *>(bBw + ((int64_t)k * G + g) * N + 8 * lane) = btok;
+            *reinterpret_cast<uint4 *>(bBw + (rk * G + g) * N + 8 * lane) = btok;
             if (a.buf_C) {
-                uint16_t *bC = static_cast<uint16_t *>(a.buf_C) + (int64_t)slot * Q * G * N;
-                *reinterpret_cast<uint4 *>(bC + ((int64_t)k * G + g) * N + 8 * lane) =
+                uint16_t *bC = static_cast<uint16_t *>(a.buf_C);
+                *reinterpret_cast<uint4 *>(bC + (rk * G + g) * N + 8 * lane) =
                     *reinterpret_cast<const uint4 *>(Cin + 8 * lane);
             }
         }
@@ -965,10 +1017,10 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
     if (sg0 <= tau)
         load_brows(sg0, braw);
     {
-        const uint16_t *bxr = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-        load_x_tile<P>(bxr, xin, H, h, k, 0, cy.xa);
+        const uint16_t *bxr = static_cast<const uint16_t *>(a.buf_x);
+        load_x_tile<P>(bxr, rows, xin, H, h, k, 0, cy.xa);
         if (tau >= 1)
-            load_x_tile<P>(bxr, xin, H, h, k, 1, cy.xb);
+            load_x_tile<P>(bxr, rows, xin, H, h, k, 1, cy.xb);
     }
 
     // delta and the in-chunk cumulative sum (log2 units) over rows j = lane + 64 i
@@ -1026,19 +1078,19 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, int b, int slo
 }
 
 // Phase 2: weights and M.X over the s-blocks, and the output row.
-template <int P, int N, class DT>
-__device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot, int h, int k,
-                                            int wave, bool gshare, char *lds_all, const DLayout &L,
-                                            DecodeCarry<P, DT> &cy) {
+template <int P, int N, class DT, bool PG>
+__device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
+                                            int h, int k, int wave, bool gshare, char *lds_all,
+                                            const DLayout &L, DecodeCarry<P, DT> &cy) {
     constexpr int NPT = P / 32;
     const Dims d = a.d;
-    const int H = d.H, Q = d.Q;
+    const int H = d.H;
     const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
     const int tau = k >> 5;
     const bool col = c == (k & 31);
     char *lds = lds_all + wave * L.bytes;
     const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
-    const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
+    const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pool
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
     const float *uu = reinterpret_cast<const float *>(lds + L.u);
     const float *bt = reinterpret_cast<const float *>(lds + L.beta);
@@ -1082,7 +1134,7 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot
                 xa[i] = xb[i];
         }
         if (sg + 2 <= tau)
-            load_x_tile<P>(bx, xin, H, h, k, sg + 2, xb);
+            load_x_tile<P>(bx, rows, xin, H, h, k, sg + 2, xb);
         mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, cy.acc);
     }
 
@@ -1114,7 +1166,7 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, int b, int slot
     }
 }
 
-template <int P, int N, class DT>
+template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_decode_mfma(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds_all[];
@@ -1133,11 +1185,16 @@ void k_decode_mfma(DecodeArgs a) {
     const int k = a.buf_len[slot];
     if (k < 0 || k >= Q)
         return;
+    // positions 0..k of the buffer are read or written
+    const SlotRows<PG> rows(a.bm, slot, Q);
+    if (!rows.ok(a.bm, k + 1))
+        return;
     // the workgroup's heads share one B/C group: C.B^T is split between them
     const bool gshare = (H / G) % kDecodeWaves == 0;
     DecodeCarry<P, DT> cy;
     if (h < H)
-        decode_front<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all + wave * L.bytes, L, cy);
+        decode_front<P, N, DT>(a, rows, b, slot, h, k, wave, gshare, lds_all + wave * L.bytes, L,
+                               cy);
     __syncthreads();  // C.B^T columns of every wave are in LDS
     // Every wave of this workgroup has read buf_len (and used it) by now, so
     // the workgroup counts itself in; the slot's last workgroup to arrive
@@ -1151,7 +1208,7 @@ void k_decode_mfma(DecodeArgs a) {
         prev = __hip_atomic_fetch_add(a.work + slot, 1, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
     if (h < H)
-        decode_back<P, N, DT>(a, b, slot, h, k, wave, gshare, lds_all, L, cy);
+        decode_back<P, N, DT>(a, rows, b, h, k, wave, gshare, lds_all, L, cy);
     if (threadIdx.x == 0 && prev == HQ - 1) {
         __hip_atomic_store(a.work + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         a.buf_len[slot] = k + 1 == Q ? 0 : k + 1;
@@ -1176,7 +1233,7 @@ void k_decode_mfma(DecodeArgs a) {
 // list.
 constexpr int kCommitWaves = 4;
 
-template <int P, int N, class DT>
+template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using TD = typename DT::T;
@@ -1202,16 +1259,21 @@ __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs 
         const int slot = list[kListHead + e / H], h = e % H, g = h / (H / G);
         if (slot < 0 || slot >= a.num_slots)
             continue;
-        const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x) + (int64_t)slot * Q * H * P;
-        const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B) + (int64_t)slot * Q * G * N;
-        const TD *bdt = static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+        // (the decode step checked the same entries before listing the slot)
+        const SlotRows<PG> rows(a.bm, slot, Q);
+        if (!rows.ok(a.bm, Q))
+            continue;
+        const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pool
+        const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
+        const TD *bdt = static_cast<const TD *>(a.buf_dt);
         float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
         f32x16 S[StateTiles<P, N, NW>::per_wave];
         state_io<P, N, NW, true>(st, S);
-        const float dt_raw = DT::ld(bdt, (int64_t)(threadIdx.x < Q ? threadIdx.x : 0) * H + h);
+        const int64_t rd = rows(threadIdx.x < Q ? threadIdx.x : 0);
+        const float dt_raw = DT::ld(bdt, rd * H + h);
         __syncthreads();  // the previous entry's LDS reads are done
-        stage_rows<P / 8, N / 8>(bx + h * P, (int64_t)H * P, bB + g * N, (int64_t)G * N, Qp, Q,
-                                 lds + L.X, L.XS, lds + L.B, L.BS);
+        stage_rows<P / 8, N / 8>(rows, bx + h * P, (int64_t)H * P, bB + g * N, (int64_t)G * N, Qp,
+                                 Q, lds + L.X, L.XS, lds + L.B, L.BS);
         chunk_scalars(dt_raw, Q, a.A[h] * kLog2e, a.dt_bias ? a.dt_bias[h] : 0.0f, d.softplus,
                       true, lds, L);
         __syncthreads();
@@ -1256,39 +1318,53 @@ hipError_t set_lds(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int P, int N, class DT>
+template <int P, int N, class DT, bool PG>
 hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
     const MLayout L(Qp, P, N);
-    hipError_t e = set_lds(k_scan_mfma<P, N, DT>, L.bytes);
+    hipError_t e = set_lds(k_scan_mfma<P, N, DT, PG>, L.bytes);
     if (e != hipSuccess)
         return e;
-    k_scan_mfma<P, N, DT><<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
+    k_scan_mfma<P, N, DT, PG>
+        <<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int P, int N, class DT>
+hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
+    return a.replay && a.bm.pages ? scan_mfma<P, N, DT, true>(a, stream)
+                                  : scan_mfma<P, N, DT, false>(a, stream);
+}
+
+template <int P, int N, class DT, bool PG>
 hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
     const size_t bytes = (size_t)DLayout(Qp, P, N).bytes * kDecodeWaves;
-    hipError_t e = set_lds(k_decode_mfma<P, N, DT>, bytes);
+    hipError_t e = set_lds(k_decode_mfma<P, N, DT, PG>, bytes);
     if (e != hipSuccess)
         return e;
     const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
-    k_decode_mfma<P, N, DT><<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+    k_decode_mfma<P, N, DT, PG>
+        <<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const MLayout LC(Qp, P, N);
-    if ((e = set_lds(k_decode_commit<P, N, DT>, LC.bytes)) != hipSuccess)
+    if ((e = set_lds(k_decode_commit<P, N, DT, PG>, LC.bytes)) != hipSuccess)
         return e;
     int dev = 0, cus = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
         (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return e;
     const int per_cu = std::max(1, std::min(4, kLdsBytesPerCu / (int)LC.bytes));
-    k_decode_commit<P, N, DT>
+    k_decode_commit<P, N, DT, PG>
         <<<dim3(std::max(1, cus) * per_cu), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
     return hipGetLastError();
+}
+
+template <int P, int N, class DT>
+hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+    return a.bm.pages ? decode_mfma<P, N, DT, true>(a, stream)
+                      : decode_mfma<P, N, DT, false>(a, stream);
 }
 
 template <int P, int N>

@@ -48,6 +48,29 @@ struct LdsLayout {
     }
 };
 
+// Buffer row of buffered position j of a slot: slot * Q + j, or through the
+// slot's page-table entry when the buffers are paged.
+__device__ __forceinline__ int64_t buf_row(const BufMap &m, int slot, int Q, int j) {
+    if (!m.pages)
+        return (int64_t)slot * Q + j;
+    return ((int64_t)m.pages[(int64_t)slot * m.npp + (j >> m.shift)] << m.shift) +
+           (j & ((1 << m.shift) - 1));
+}
+
+// Whether the page-table entries of the slot's positions [0, npos) are pages
+// of the pool (always true for contiguous buffers).
+__device__ bool buf_pages_ok(const BufMap &m, int slot, int npos) {
+    if (!m.pages)
+        return true;
+    const int n = (npos + (1 << m.shift) - 1) >> m.shift;
+    for (int i = 0; i < n; ++i) {
+        const int pg = m.pages[(int64_t)slot * m.npp + i];
+        if (pg < 0 || pg >= m.num_pages)
+            return false;
+    }
+    return true;
+}
+
 // Where chunk position j of the current chunk lives: positions [0, nb) in
 // the slot buffer, positions [nb, n_valid) in the packed input starting at
 // token tok_base. Positions >= n_valid do not exist.
@@ -57,22 +80,25 @@ struct ChunkView {
     using TD = typename DT::T;
     const T *x, *B, *C;
     const TD *dt;
-    const T *bx, *bB;
+    const T *bx, *bB;      // buffer arrays (whole pool)
     const TD *bdt;
+    BufMap bm;
+    int slot, Q;
     int64_t tok_base;
     int nb, n_valid;
     int h, g, H, G, P, N;
 
+    __device__ int64_t brw(int j) const { return buf_row(bm, slot, Q, j); }
     __device__ const T *xrow(int j) const {
-        return j < nb ? bx + ((int64_t)j * H + h) * P
+        return j < nb ? bx + (brw(j) * H + h) * P
                       : x + ((tok_base + (j - nb)) * H + h) * P;
     }
     __device__ float dtv(int j) const {
-        return j < nb ? DT::ld(bdt, (int64_t)j * H + h)
+        return j < nb ? DT::ld(bdt, brw(j) * H + h)
                       : DT::ld(dt, (tok_base + (j - nb)) * H + h);
     }
     __device__ const T *brow(int j) const {
-        return j < nb ? bB + ((int64_t)j * G + g) * N
+        return j < nb ? bB + (brw(j) * G + g) * N
                       : B + ((tok_base + (j - nb)) * G + g) * N;
     }
     // C is only read for rows whose output is produced (never buffered rows)
@@ -273,6 +299,8 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
     const int nbuf = a.replay ? a.buf_len[slot] : 0;
     if (nbuf < 0 || nbuf >= Q)  // corrupt slot metadata: leave the slot alone
         return;
+    if (a.replay && !buf_pages_ok(a.bm, slot, replay_npos(nbuf, len, Q)))
+        return;
 
     const float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                                  : (a.init_state ? a.init_state + ((int64_t)s * H + h) * PN
@@ -284,9 +312,10 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
     v.B = static_cast<const T *>(a.B);
     v.C = static_cast<const T *>(a.C);
     v.dt = static_cast<const TD *>(a.dt);
-    v.bx = a.replay ? static_cast<const T *>(a.buf_x) + (int64_t)slot * Q * H * P : nullptr;
-    v.bB = a.replay ? static_cast<const T *>(a.buf_B) + (int64_t)slot * Q * G * N : nullptr;
-    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) + (int64_t)slot * Q * H : nullptr;
+    v.bx = static_cast<const T *>(a.buf_x);
+    v.bB = static_cast<const T *>(a.buf_B);
+    v.bdt = static_cast<const TD *>(a.buf_dt);
+    v.bm = a.bm; v.slot = slot; v.Q = Q;
     v.h = h; v.g = g; v.H = H; v.G = G; v.P = P; v.N = N;
 
     const float A_h = a.A[h];
@@ -340,14 +369,15 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
     if (slot < 0 || slot >= a.num_slots)
         return;
     const int k = a.buf_len[slot];
-    if (k < 0 || k >= Q)
+    if (k < 0 || k >= Q || !buf_pages_ok(a.bm, slot, k + 1))
         return;
     float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
     state_load(lds + L.S, st, P, N);
 
-    T *bx = static_cast<T *>(a.buf_x) + (int64_t)slot * Q * H * P;
-    T *bB = static_cast<T *>(a.buf_B) + (int64_t)slot * Q * G * N;
-    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
+    T *bx = static_cast<T *>(a.buf_x);   // buffer arrays (whole pool)
+    T *bB = static_cast<T *>(a.buf_B);
+    TD *bdt = static_cast<TD *>(a.buf_dt);
+    const int64_t rk = buf_row(a.bm, slot, Q, k);   // buffer row of position k
 
     ChunkView<IO, DT> v;
     v.x = static_cast<const T *>(a.x);
@@ -355,6 +385,7 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
     v.C = static_cast<const T *>(a.C);
     v.dt = static_cast<const TD *>(a.dt);
     v.bx = bx; v.bB = bB; v.bdt = bdt;
+    v.bm = a.bm; v.slot = slot; v.Q = Q;
     v.h = h; v.g = g; v.H = H; v.G = G; v.P = P; v.N = N;
     v.tok_base = b;
     v.nb = k;
@@ -369,18 +400,18 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
     const int tid = threadIdx.x;
     const T *xin = static_cast<const T *>(a.x) + ((int64_t)b * H + h) * P;
     for (int p = tid; p < P; p += kBlock)
-        bx[((int64_t)k * H + h) * P + p] = xin[p];
+        bx[(rk * H + h) * P + p] = xin[p];
     if (tid == 0)
-        bdt[(int64_t)k * H + h] = static_cast<const TD *>(a.dt)[(int64_t)b * H + h];
+        bdt[rk * H + h] = static_cast<const TD *>(a.dt)[(int64_t)b * H + h];
     if (h % hpg == 0) {
         const T *bin = static_cast<const T *>(a.B) + ((int64_t)b * G + g) * N;
         for (int n = tid; n < N; n += kBlock)
-            bB[((int64_t)k * G + g) * N + n] = bin[n];
+            bB[(rk * G + g) * N + n] = bin[n];
         if (a.buf_C) {
-            T *bC = static_cast<T *>(a.buf_C) + (int64_t)slot * Q * G * N;
+            T *bC = static_cast<T *>(a.buf_C);
             const T *cin = static_cast<const T *>(a.C) + ((int64_t)b * G + g) * N;
             for (int n = tid; n < N; n += kBlock)
-                bC[((int64_t)k * G + g) * N + n] = cin[n];
+                bC[(rk * G + g) * N + n] = cin[n];
         }
     }
     if (k + 1 == Q) {
@@ -392,8 +423,9 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
 
 // buf_len / boundary_pos advance after a decode step (separate launch: every
 // head's workgroup of a slot reads buf_len first).
+// Slots the decode kernel skipped (a missing page) are not advanced.
 __global__ void k_decode_advance(int batch, const int32_t *slot_idx, int32_t *buf_len,
-                                 int64_t *boundary_pos, int Q, int num_slots) {
+                                 int64_t *boundary_pos, int Q, int num_slots, BufMap bm) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= batch)
         return;
@@ -401,7 +433,7 @@ __global__ void k_decode_advance(int batch, const int32_t *slot_idx, int32_t *bu
     if (slot < 0 || slot >= num_slots)
         return;
     const int k = buf_len[slot];
-    if (k < 0 || k >= Q)
+    if (k < 0 || k >= Q || !buf_pages_ok(bm, slot, k + 1))
         return;
     if (k + 1 == Q) {
         buf_len[slot] = 0;
@@ -428,7 +460,9 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     if ((!a.fresh && len == 0) || slot < 0 || slot >= a.num_slots)
         return;
     if (part > 0) {
-        if (!a.state_src)
+        // (state_src comes with fresh slots only: buf_len is not read here,
+        // workgroup (s, 0) writes it)
+        if (!a.state_src || !buf_pages_ok(a.bm, slot, replay_npos(0, len, Q)))
             return;
         const int h = part - 1;
         const int64_t PN = (int64_t)P * N;
@@ -447,7 +481,7 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
         return;
     }
     const int nbuf = a.fresh ? 0 : a.buf_len[slot];
-    if (nbuf < 0 || nbuf >= Q)
+    if (nbuf < 0 || nbuf >= Q || !buf_pages_ok(a.bm, slot, replay_npos(nbuf, len, Q)))
         return;
     const int total = nbuf + len;
     const int nfull = total / Q, tail = total % Q;
@@ -460,20 +494,27 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     const T *B = static_cast<const T *>(a.B);
     const T *C = static_cast<const T *>(a.C);
     const TD *dt = static_cast<const TD *>(a.dt);
-    T *bx = static_cast<T *>(a.buf_x) + (int64_t)slot * Q * H * P;
-    T *bB = static_cast<T *>(a.buf_B) + (int64_t)slot * Q * G * N;
-    TD *bdt = static_cast<TD *>(a.buf_dt) + (int64_t)slot * Q * H;
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
-    for (int64_t e = tid; e < ntok * HP; e += kBlock)
-        bx[dst0 * HP + e] = x[(t0 + src0) * HP + e];
-    for (int64_t e = tid; e < (int64_t)ntok * H; e += kBlock)
-        bdt[(int64_t)dst0 * H + e] = dt[(t0 + src0) * H + e];
-    for (int64_t e = tid; e < ntok * GN; e += kBlock)
-        bB[dst0 * GN + e] = B[(t0 + src0) * GN + e];
-    if (a.buf_C) {
-        T *bC = static_cast<T *>(a.buf_C) + (int64_t)slot * Q * G * N;
-        for (int64_t e = tid; e < ntok * GN; e += kBlock)
-            bC[dst0 * GN + e] = C[(t0 + src0) * GN + e];
+    // token rows in 16-byte pieces (a row of x or B is a multiple of 32
+    // bytes), each to the buffer row of its position
+    auto copy_rows = [&](void *dst, const void *src, int64_t row_elems) {
+        const int64_t per = row_elems * (int64_t)sizeof(T) / 16;
+        for (int64_t e = tid; e < ntok * per; e += kBlock) {
+            const int r = (int)(e / per);
+            const int64_t q = e % per;
+            const int64_t row = buf_row(a.bm, slot, Q, dst0 + r);
+            reinterpret_cast<uint4 *>(dst)[row * per + q] =
+                reinterpret_cast<const uint4 *>(src)[(t0 + src0 + r) * per + q];
+        }
+    };
+    copy_rows(a.buf_x, x, HP);
+    copy_rows(a.buf_B, B, GN);
+    if (a.buf_C)
+        copy_rows(a.buf_C, C, GN);
+    TD *bdt = static_cast<TD *>(a.buf_dt);
+    for (int64_t e = tid; e < (int64_t)ntok * H; e += kBlock) {
+        const int r = (int)(e / H);
+        bdt[buf_row(a.bm, slot, Q, dst0 + r) * H + e % H] = dt[(t0 + src0) * H + e];
     }
     __syncthreads();
     if (tid == 0) {
@@ -615,7 +656,7 @@ template <class IO, class DT> struct SsuF { static hipError_t run(const SsuArgs 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream) { return dispatch<ScanF>(a, stream); }
 hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream) {
     k_decode_advance<<<dim3((a.batch + 255) / 256), dim3(256), 0, stream>>>(
-        a.batch, a.slot_idx, a.buf_len, a.boundary_pos, a.d.Q, a.num_slots);
+        a.batch, a.slot_idx, a.buf_len, a.boundary_pos, a.d.Q, a.num_slots, a.bm);
     return hipGetLastError();
 }
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return dispatch<DecodeF>(a, stream); }

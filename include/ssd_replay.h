@@ -105,7 +105,25 @@ typedef struct {
  *                                          before first use, and every call
  *                                          leaves it zero
  * A fresh slot is all zeros. The struct itself is a host object; the
- * pointers in it are device pointers. */
+ * pointers in it are device pointers.
+ *
+ * Paged buffers ([RFC] section 6, implementation notes: the buffers live in
+ * the paged mamba cache, so slot and position are indexed separately). With
+ * buf_pages == NULL the buffers are contiguous per slot as above. Otherwise
+ * buf_x, buf_dt, buf_B and buf_C are pools of num_pages pages of page_tokens
+ * rows each ([num_pages,page_tokens,H,P] and so on), and buffered position
+ * j of a slot is row j % page_tokens of page buf_pages[slot][j / page_tokens]:
+ *   buf_pages     [num_slots,Q/page_tokens] int32, on the device
+ *   page_tokens   a power of two with 16 <= page_tokens <= Q
+ *   num_pages     pages in each pool (> 0)
+ * The state, its bf16 copy, buf_len and boundary_pos stay indexed by slot.
+ * Only the entries of the positions a call reads or writes need to be
+ * pages (positions 0..buf_len for a decode step; up to the larger of the
+ * buffered and the trailing tokens for a prefill or commit), so pages can
+ * be handed out as a slot's buffer grows and returned when its chunk
+ * completes. If such an entry is outside [0, num_pages), that sequence is
+ * skipped: nothing of its slot and none of its outputs are written. Entries
+ * in use must not share a page. */
 typedef struct {
     float *state;
     void *state_bf;
@@ -119,6 +137,9 @@ typedef struct {
     int32_t num_slots;
     int32_t chunk_size;
     int32_t state_dtype;
+    const int32_t *buf_pages;
+    int32_t page_tokens;
+    int32_t num_pages;
 } ssd_replay_cache;
 
 /* Rebuild the bf16 state copy (state_bf) of every slot from the fp32 state,
@@ -136,6 +157,11 @@ const char *ssd_status_string(int status);
  * P=64, N=128, Q=256; the bf16 copy adds 0.5 MiB. */
 size_t ssd_replay_cache_bytes(const ssd_shape *shape, int32_t num_slots,
                               int32_t with_C);
+
+/* Bytes of one buffer page of page_tokens rows (x, raw dt, B and, with
+ * with_C, C) for a paged cache; 0 for a bad shape or page size. */
+size_t ssd_replay_page_bytes(const ssd_shape *shape, int32_t page_tokens,
+                             int32_t with_C);
 
 /* Workspace bytes ssd_prefill_varlen needs (currently 0: the prefill kernel
  * carries the inter-chunk state on chip). */

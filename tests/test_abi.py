@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     want = {"ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
-            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh"}
+            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
+            "ssd_replay_page_bytes"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -150,6 +151,31 @@ def test_replay_fails_closed():
                                 FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == -4
     assert lib.ssm_state_update(ctypes.byref(sh), 3, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, None, None, FAKE, None) == -2
+
+
+def test_paged_cache_checks():
+    """Paged buffers: page_tokens a power of two in [16, Q], num_pages > 0."""
+    sh = shape(chunk_size=64)
+    ok = dict(chunk_size=64, buf_pages=0x2000, page_tokens=32, num_pages=8)
+    assert decode(sh, cache(sh, **ok), batch=0) == 0
+    for bad in (dict(page_tokens=8), dict(page_tokens=128), dict(page_tokens=48),
+                dict(page_tokens=0), dict(num_pages=0), dict(num_pages=-3)):
+        assert decode(sh, cache(sh, **{**ok, **bad}), batch=0) == -2, bad
+    # page_tokens and num_pages are ignored without a page table
+    assert decode(sh, cache(sh, chunk_size=64, page_tokens=3, num_pages=-1), batch=0) == 0
+
+
+def test_page_bytes():
+    sh = erd.Shape(32, 1, 64, 128, 256, "bf16", "f32")
+    per_tok = 32 * 64 * 2 + 32 * 4 + 2 * 128 * 2
+    assert erd.ssd_replay_page_bytes(sh, 64, with_C=True) == 64 * per_tok
+    assert erd.ssd_replay_page_bytes(sh, 16, with_C=False) == 16 * (per_tok - 128 * 2)
+    # a whole chunk of pages is the contiguous buffer of one slot
+    slot = erd.ssd_replay_cache_bytes(sh, 1, with_C=True) - 34 * 4
+    assert slot - erd.ssd_replay_page_bytes(sh, 256, with_C=True) == \
+        32 * 64 * 128 * 6 + 3 * 4 + 8
+    for bad in (8, 512, 48, 0):
+        assert erd.ssd_replay_page_bytes(sh, bad, with_C=True) == 0
 
 
 def test_python_binding_checks_extents():
