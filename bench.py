@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD prefill tokens/s + replay-decode steps/s at B=256; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+PAGE_TOKENS = 64             # rows per buffer page in the paged replay-decode leg
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
                   "ssd_internal.hpp"]
@@ -253,26 +254,35 @@ def main():
     cu_pre = synth.cu_seqlens(pre)
     cache256 = erd.ReplayCache(shape, S, dev)
     cache16 = erd.ReplayCache(shape16, S, dev)
+    # the same workload over paged buffers: pages of PAGE_TOKENS rows, every
+    # slot's pages scattered over the pool
+    npages = S * (Q // PAGE_TOKENS)
+    cachepg = erd.ReplayCache(shape, S, dev, page_tokens=PAGE_TOKENS, num_pages=npages)
+    perm = np.random.default_rng(0).permutation(npages).astype(np.int32)
+    cachepg.buf_pages.copy_(torch.from_numpy(perm.reshape(S, Q // PAGE_TOKENS)))
     erd.ssd_replay_prefill(shape, cache256, cu_pre, px, pdt, pB, pC, A, D, bias)
     erd.ssd_replay_prefill(shape16, cache16, cu_pre, px, pdt, pB, pC, A, D, bias)
+    erd.ssd_replay_prefill(shape, cachepg, cu_pre, px, pdt, pB, pC, A, D, bias)
     _, ssu_state, _ = erd.ssd_prefill_varlen(shape, cu_pre, px, pdt, A, pB, pC, D, bias,
                                              want_boundary=False)
     plan256 = erd.DecodePlan(shape, S, A, D, bias, cache=cache256)
     plan16 = erd.DecodePlan(shape16, S, A, D, bias, cache=cache16)
+    planpg = erd.DecodePlan(shape, S, A, D, bias, cache=cachepg)
     plan_ssu = erd.DecodePlan(shape, S, A, D, bias, state=ssu_state)
     plan256.check(dx[0], ddt[0], dB[0], dC[0], ydec)
     ks256 = (pre % Q).astype(np.int64)
     ks16 = (pre % 16).astype(np.int64)
+    kspg = ks256.copy()
 
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    bytes_decode256 = bytes_decode16 = 0
+    bytes_decode256 = bytes_decode16 = bytes_decodepg = 0
     decode_i = 0
 
     def step(record):
-        nonlocal decode_i, bytes_decode256, bytes_decode16, ks256, ks16
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
+        nonlocal decode_i, bytes_decode256, bytes_decode16, bytes_decodepg, ks256, ks16, kspg
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)] if record else None
         if record:
             ev[0].record(stream)
         erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
@@ -304,6 +314,14 @@ def main():
             ks16 = (ks16 + 1) % 16
         if record:
             ev[5].record(stream)
+        for r in range(R):
+            k = decode_i + r
+            planpg(dx[k], ddt[k], dB[k], dC[k], ydec)
+            if record:
+                bytes_decodepg += replay_step_bytes(kspg, Q, H, G, P, N)
+            kspg = (kspg + 1) % Q
+        if record:
+            ev[6].record(stream)
         decode_i += R
         return ev
 
@@ -324,7 +342,8 @@ def main():
     t_dec256 = span(2, 3)
     t_ssu = span(3, 4)
     t_dec16 = span(4, 5)
-    t_total = span(0, 5)
+    t_decpg = span(5, 6)
+    t_total = span(0, 6)
 
     pb = prefill_bytes(S * T, S, H, G, P, N)
     pf = prefill_flops(S * T, H, G, P, N, Q)
@@ -335,6 +354,7 @@ def main():
     dec_steps = K * R
     dec256_gbs = bytes_decode256 / t_dec256 / 1e9
     dec16_gbs = bytes_decode16 / t_dec16 / 1e9
+    decpg_gbs = bytes_decodepg / t_decpg / 1e9
     ssu_gbs = ssu_step_bytes(S, H, G, P, N) * dec_steps / t_ssu / 1e9
 
     out = {
@@ -354,8 +374,8 @@ def main():
         "config": {
             "workload": "prefill 256 seqs x 2048 tokens (H=32 G=1 P=64 N=128 chunk 256, "
                         "bf16 x/dt/B/C/y, fp32 state) + boundary commit + replay decode "
-                        "B=256 (chunk 256 and 16, 0..255 buffered tokens) + recurrent "
-                        "update B=256",
+                        "B=256 (chunk 256 and 16, 0..255 buffered tokens; chunk 256 also "
+                        "over paged buffers) + recurrent update B=256",
             "global_batch": S, "seq_len": T, "heads": H, "groups": G, "headdim": P,
             "dstate": N, "chunk_size": Q, "decode_steps_per_step": R,
         },
@@ -374,6 +394,10 @@ def main():
             "replay_q16_steps_per_s": dec_steps / t_dec16,
             "replay_q16_hbm_gbs": dec16_gbs,
             "replay_q16_frac": dec16_gbs / HBM_PEAK_GBS,
+            "replay_q256_paged_steps_per_s": dec_steps / t_decpg,
+            "replay_q256_paged_hbm_gbs": decpg_gbs,
+            "replay_q256_paged_frac": decpg_gbs / HBM_PEAK_GBS,
+            "page_tokens": PAGE_TOKENS,
             "ssu_steps_per_s": dec_steps / t_ssu,
             "ssu_hbm_gbs": ssu_gbs,
             "ssu_frac": ssu_gbs / HBM_PEAK_GBS,
