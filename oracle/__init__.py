@@ -8,5 +8,7 @@ library.
   the definition of what the scan computes.
 - ``closed_form.chunked_scan``: the chunk-by-chunk closed form in numpy, an
   independent formulation used to pin ``scan``.
+- ``conv1d``: the causal depthwise conv1d before the scan (prefill and decode
+  forms are one definition), in numpy.
 """
 from .oracle import scan, threads, ensure_built  # noqa: F401
