@@ -23,7 +23,7 @@ STATUS = {
 EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
-           "ssd_replay_page_bytes")
+           "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update")
 
 
 class ssd_shape(ctypes.Structure):
@@ -79,6 +79,12 @@ def load() -> ctypes.CDLL:
                                        vp, vp, vp, vp]
     lib.ssd_replay_decode.restype = ctypes.c_int
     lib.ssd_replay_decode.argtypes = [shp, cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_conv1d_varlen.restype = ctypes.c_int
+    lib.ssd_conv1d_varlen.argtypes = [shp, i32, i32, i32, i64, vp, vp, vp, i32, vp, vp, vp,
+                                      vp, vp, vp, vp, vp]
+    lib.ssd_conv1d_update.restype = ctypes.c_int
+    lib.ssd_conv1d_update.argtypes = [shp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                      vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [shp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib

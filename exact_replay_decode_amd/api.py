@@ -318,6 +318,74 @@ def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, 
     return y
 
 
+def conv_dim(shape: Shape) -> int:
+    """Channels of the conv before the scan: x | B | C."""
+    return shape.H * shape.P + 2 * shape.G * shape.N
+
+
+def _conv_outputs(shape: Shape, T: int, dev, out):
+    if out is None:
+        return (torch.empty((T, shape.H, shape.P), dtype=shape.io, device=dev),
+                torch.empty((T, shape.G, shape.N), dtype=shape.io, device=dev),
+                torch.empty((T, shape.G, shape.N), dtype=shape.io, device=dev))
+    x, B, C = out
+    return (_need(x, "x", (T, shape.H, shape.P), shape.io, dev),
+            _need(B, "B", (T, shape.G, shape.N), shape.io, dev),
+            _need(C, "C", (T, shape.G, shape.N), shape.io, dev))
+
+
+def ssd_conv1d_varlen(shape: Shape, cu_seqlens, xBC, weight, bias=None, conv_state=None,
+                      slot_idx=None, activation=True, out=None, cu_seqlens_host=None,
+                      stream=None):
+    """Causal depthwise conv1d (prefill form) over a varlen pack of xBC
+    [T, conv_dim]; conv_state [slots, conv_dim, W-1] is read and updated in
+    place (None: zero history). Returns (x, B, C), the scan's inputs."""
+    dev = xBC.device
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(xBC.shape[0])
+    cd = conv_dim(shape)
+    _need(xBC, "xBC", (T, cd), shape.io, dev)
+    W = int(weight.shape[1]) if weight.dim() == 2 else -1
+    _need(weight, "weight", (cd, W), torch.float32, dev)
+    _opt(bias, "bias", (cd,), torch.float32, dev)
+    ns = 0
+    if conv_state is not None:
+        ns = int(conv_state.shape[0])
+        _need(conv_state, "conv_state", (ns, cd, W - 1), shape.io, dev)
+    sl = _slots(slot_idx, S, dev)
+    x, B, C = _conv_outputs(shape, T, dev, out)
+    sh = shape.c()
+    rc = _lib.load().ssd_conv1d_varlen(
+        ctypes.byref(sh), W, int(bool(activation)), S, T, host.ctypes.data_as(ctypes.c_void_p),
+        _ptr(cu), _ptr(sl), ns, _ptr(xBC), _ptr(weight), _ptr(bias), _ptr(conv_state),
+        _ptr(x), _ptr(B), _ptr(C), _stream(stream))
+    _lib.check(rc, "ssd_conv1d_varlen")
+    return x, B, C
+
+
+def ssd_conv1d_update(shape: Shape, xBC, weight, conv_state, bias=None, slot_idx=None,
+                      activation=True, out=None, stream=None):
+    """Causal conv1d, decode form: one token per row of xBC [batch, conv_dim];
+    conv_state [slots, conv_dim, W-1] updated in place. Returns (x, B, C)."""
+    dev = xBC.device
+    nb = int(xBC.shape[0])
+    cd = conv_dim(shape)
+    _need(xBC, "xBC", (nb, cd), shape.io, dev)
+    W = int(weight.shape[1]) if weight.dim() == 2 else -1
+    _need(weight, "weight", (cd, W), torch.float32, dev)
+    _opt(bias, "bias", (cd,), torch.float32, dev)
+    ns = int(conv_state.shape[0])
+    _need(conv_state, "conv_state", (ns, cd, W - 1), shape.io, dev)
+    sl = _slots(slot_idx, nb, dev)
+    x, B, C = _conv_outputs(shape, nb, dev, out)
+    sh = shape.c()
+    rc = _lib.load().ssd_conv1d_update(
+        ctypes.byref(sh), W, int(bool(activation)), nb, _ptr(sl), ns, _ptr(xBC), _ptr(weight),
+        _ptr(bias), _ptr(conv_state), _ptr(x), _ptr(B), _ptr(C), _stream(stream))
+    _lib.check(rc, "ssd_conv1d_update")
+    return x, B, C
+
+
 def ssm_state_update(shape: Shape, state, x, dt, B, C, A, D=None, dt_bias=None, slot_idx=None,
                      y=None, stream=None):
     """One recurrent selective-state update for x.shape[0] sequences; state

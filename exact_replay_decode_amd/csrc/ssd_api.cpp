@@ -3,6 +3,7 @@
 // call launches nothing) and the translation into kernel argument blocks.
 #include "ssd_replay.h"
 
+#include <algorithm>
 #include <limits>
 
 #include "ssd_internal.hpp"
@@ -351,6 +352,75 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.bm = buf_map(cache);
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
+}
+
+int ssd_conv1d_varlen(const ssd_shape *sh, int32_t W, int32_t act, int32_t S, int64_t T,
+                      const int32_t *cu_host, const int32_t *cu, const int32_t *slot_idx,
+                      int32_t num_slots, const void *xBC, const float *weight, const float *bias,
+                      void *conv_state, void *x, void *B, void *C, hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if (W < 2 || W > 4)
+        return SSD_ERR_UNSUPPORTED;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (S > 65535 || (conv_state && (num_slots <= 0 || (!slot_idx && S > num_slots))))
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return SSD_OK;
+    if (!weight || (T > 0 && (!xBC || !x || !B || !C)))
+        return SSD_ERR_NULL;
+    if (!all_a16(xBC, conv_state, x, B, C))
+        return SSD_ERR_ALIGN;
+    int32_t maxlen = 0;
+    for (int32_t s = 0; s < S; ++s)
+        maxlen = std::max(maxlen, cu_host[s + 1] - cu_host[s]);
+    ssd::ConvArgs a = {};
+    a.d = d;
+    a.W = W;
+    a.act = act != 0;
+    a.S = S;
+    a.cu = cu;
+    a.maxlen = maxlen;
+    a.slot_idx = conv_state ? slot_idx : nullptr;
+    a.num_slots = conv_state ? num_slots : S;
+    a.xBC = xBC; a.weight = weight; a.bias = bias;
+    a.state = conv_state;
+    a.x = x; a.B = B; a.C = C;
+    return hip_status(ssd::launch_conv_fwd(a, (hipStream_t)stream));
+}
+
+int ssd_conv1d_update(const ssd_shape *sh, int32_t W, int32_t act, int32_t batch,
+                      const int32_t *slot_idx, int32_t num_slots, const void *xBC,
+                      const float *weight, const float *bias, void *conv_state, void *x, void *B,
+                      void *C, hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if (W < 2 || W > 4)
+        return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || batch > 65535 || num_slots < 0 || (!slot_idx && batch > num_slots))
+        return SSD_ERR_SHAPE;
+    if (batch == 0)
+        return SSD_OK;
+    if (!weight || !xBC || !conv_state || !x || !B || !C)
+        return SSD_ERR_NULL;
+    if (!all_a16(xBC, conv_state, x, B, C))
+        return SSD_ERR_ALIGN;
+    ssd::ConvArgs a = {};
+    a.d = d;
+    a.W = W;
+    a.act = act != 0;
+    a.S = batch;
+    a.slot_idx = slot_idx;
+    a.num_slots = num_slots;
+    a.xBC = xBC; a.weight = weight; a.bias = bias;
+    a.state = conv_state;
+    a.x = x; a.B = B; a.C = C;
+    return hip_status(ssd::launch_conv_update(a, (hipStream_t)stream));
 }
 
 int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,

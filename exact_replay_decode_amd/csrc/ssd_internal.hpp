@@ -85,6 +85,24 @@ struct DecodeArgs {
     BufMap bm;
 };
 
+// Causal depthwise conv1d before the scan: prefill (S sequences of a varlen
+// pack) or decode (S = batch rows of one token).
+struct ConvArgs {
+    Dims d;                   // H, G, P, N, io dtype (conv_dim = H*P + 2*G*N)
+    int32_t W;                // kernel width, 2..4
+    int32_t act;              // 1: SiLU after the conv
+    int32_t S;
+    const int32_t *cu;        // [S+1] (prefill)
+    int32_t maxlen;           // longest sequence (prefill)
+    const int32_t *slot_idx;  // [S] or null
+    int32_t num_slots;
+    const void *xBC;          // [T, conv_dim]
+    const float *weight;      // [conv_dim, W]
+    const float *bias;        // [conv_dim] or null
+    void *state;              // [slots, conv_dim, W-1] or null (prefill)
+    void *x, *B, *C;          // outputs [T,H,P], [T,G,N], [T,G,N]
+};
+
 struct SsuArgs {
     Dims d;
     int32_t batch;
@@ -103,6 +121,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 bool mfma_supported(const Dims &d);
 hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+// causal conv1d (ssd_conv.hip)
+hipError_t launch_conv_fwd(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_conv_update(const ConvArgs &a, hipStream_t stream);
 // shared by both engines
 hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);

@@ -155,3 +155,39 @@ def make_tokens_torch(T: int, H: int, G: int, P: int, N: int, seed: int, device,
     Bm = torch.randn((T, G, N), generator=g, device=device).to(tdt[io_dtype])
     Cm = torch.randn((T, G, N), generator=g, device=device).to(tdt[io_dtype])
     return x, dt, Bm, Cm
+
+
+@dataclasses.dataclass
+class ConvParams:
+    """Depthwise conv taps and bias of the conv before the scan, float32
+    holding bf16-representable values (bf16 model weights, promoted)."""
+    weight: np.ndarray   # [conv_dim, W]
+    bias: np.ndarray     # [conv_dim]
+
+
+def make_conv_params(conv_dim: int, W: int, seed: int) -> ConvParams:
+    """Taps and bias uniform in [-1/sqrt(W), 1/sqrt(W)] (fan-in init of a
+    depthwise conv with W taps), rounded to bf16."""
+    rng = np.random.default_rng([seed, W, 0xC0DE])
+    lim = 1.0 / np.sqrt(W)
+    w = widen(store(rng.uniform(-lim, lim, size=(conv_dim, W)), "bf16"), "bf16")
+    b = widen(store(rng.uniform(-lim, lim, size=conv_dim), "bf16"), "bf16")
+    return ConvParams(weight=w.astype(np.float32), bias=b.astype(np.float32))
+
+
+def make_xbc(T: int, conv_dim: int, seed: int, stream: int = 0,
+             io_dtype: str = "bf16") -> np.ndarray:
+    """Conv input xBC [T, conv_dim] ~ N(0, 1) in storage form; (seed, stream)
+    fixes the values."""
+    rng = np.random.default_rng([seed, stream, 0xBC])
+    return store(rng.standard_normal((T, conv_dim)), io_dtype)
+
+
+def make_xbc_torch(T: int, conv_dim: int, seed: int, device, io_dtype: str = "bf16"):
+    """Device-side draw of xBC ~ N(0, 1) for large workloads (float32 draw
+    by torch's generator, rounded to the storage dtype)."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 0xBC)
+    return torch.randn((T, conv_dim), generator=g, device=device).to(tdt[io_dtype])

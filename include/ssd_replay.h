@@ -249,6 +249,49 @@ int ssm_state_update(const ssd_shape *shape, int32_t batch, int32_t num_slots,
                      const void *C, const float *D, const float *dt_bias,
                      void *y, hipStream_t stream);
 
+/* Causal depthwise conv1d, the step before the scan ([RFC] section 2, item
+ * 6: its prefill form and its decode form give the same bits; bf16 operands
+ * are promoted to fp32 before the accumulation). The channels are the
+ * concatenated projection xBC = [x (H*P) | B (G*N) | C (G*N)], conv_dim =
+ * H*P + 2*G*N, and for channel c, kernel width W in {2,3,4}:
+ *   out_t[c] = act(bias[c] + sum_{i<W} weight[c][i] * in_{t-W+1+i}[c])
+ * in fp32, as an fmaf chain from the bias over i = 0..W-1, with act(v) =
+ * v / (1 + exp(-v)) (SiLU) when activation != 0, else the identity. Inputs
+ * before a sequence come from its conv state: the W-1 previous inputs,
+ * oldest first. Outputs go straight to the scan's inputs x [T,H,P],
+ * B [T,G,N], C [T,G,N] (io_dtype; bf16 rounds to nearest even).
+ *   xBC         [T, conv_dim]               io_dtype
+ *   weight      [conv_dim, W]               fp32
+ *   bias        [conv_dim] fp32 or NULL (zeros)
+ *   conv_state  [num_slots, conv_dim, W-1]  io_dtype, channel-major
+ * Both forms evaluate every output with the same device routine on the same
+ * W inputs, so decoding token by token reproduces the prefill's bits, and a
+ * prefill split at any point reproduces the unsplit one. Pointers are
+ * 16-byte aligned (SSD_ERR_ALIGN). shape->chunk_size and dt_dtype are not
+ * used (any valid value). */
+
+/* Prefill form over a varlen pack. Sequence s (tokens cu[s]..cu[s+1]-1)
+ * starts from conv_state[slot_idx[s]] (slot_idx NULL = s) and leaves there
+ * its last W-1 inputs (for a sequence shorter than W-1, the newer rows of
+ * the old state followed by its inputs). The state is read before it is
+ * written, so in-place use is the normal case; a fresh slot must be zero.
+ * conv_state NULL: zero history, nothing stored (slot_idx and num_slots
+ * ignored). Slots must be distinct. S <= 65535. */
+int ssd_conv1d_varlen(const ssd_shape *shape, int32_t width, int32_t activation,
+                      int32_t num_seqs, int64_t total_tokens,
+                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens,
+                      const int32_t *slot_idx, int32_t num_slots, const void *xBC,
+                      const float *weight, const float *bias, void *conv_state,
+                      void *x, void *B, void *C, hipStream_t stream);
+
+/* Decode form: one token per row b (xBC [batch, conv_dim]); slot =
+ * slot_idx[b] (NULL = b); conv_state[slot] is updated in place; outputs x
+ * [batch,H,P], B/C [batch,G,N]. Slots must be distinct. batch <= 65535. */
+int ssd_conv1d_update(const ssd_shape *shape, int32_t width, int32_t activation,
+                      int32_t batch, const int32_t *slot_idx, int32_t num_slots,
+                      const void *xBC, const float *weight, const float *bias,
+                      void *conv_state, void *x, void *B, void *C, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

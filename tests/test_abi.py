@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     want = {"ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
-            "ssd_replay_page_bytes"}
+            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -176,6 +176,41 @@ def test_page_bytes():
         32 * 64 * 128 * 6 + 3 * 4 + 8
     for bad in (8, 512, 48, 0):
         assert erd.ssd_replay_page_bytes(sh, bad, with_C=True) == 0
+
+
+def conv_prefill(sh, W=4, S=1, T=8, cu=None, state=None, num_slots=0, **over):
+    lib = _lib.load()
+    cu = np.asarray(cu if cu is not None else [0] + [T] * S, dtype=np.int32)
+    a = dict(xBC=FAKE, weight=FAKE, x=FAKE, B=FAKE, C=FAKE, cu_dev=FAKE)
+    a.update(over)
+    return lib.ssd_conv1d_varlen(ctypes.byref(sh), W, 1, len(cu) - 1, int(cu[-1]),
+                                 cu.ctypes.data_as(ctypes.c_void_p), a["cu_dev"], None,
+                                 num_slots, a["xBC"], a["weight"], None, state, a["x"],
+                                 a["B"], a["C"], None)
+
+
+def test_conv_checks():
+    sh = shape()
+    assert conv_prefill(sh, W=1) == -7 and conv_prefill(sh, W=5) == -7
+    assert conv_prefill(sh, weight=None) == -1
+    assert conv_prefill(sh, x=None) == -1
+    assert conv_prefill(sh, xBC=ctypes.c_void_p(0x1004)) == -9
+    assert conv_prefill(sh, state=ctypes.c_void_p(0x1008), num_slots=1) == -9
+    assert conv_prefill(sh, state=FAKE, num_slots=0) == -2     # state but no slots
+    assert conv_prefill(sh, cu=[0, 4, 2, 8]) == -2
+    assert conv_prefill(sh, cu=[0, 0]) == 0                    # empty sequence: nothing to do
+    assert conv_prefill(shape(state_dtype=1)) == -4
+    big = np.zeros(65537, dtype=np.int32)
+    assert conv_prefill(sh, cu=big) == -2                      # more than 65535 sequences
+    lib = _lib.load()
+    upd = lambda **k: lib.ssd_conv1d_update(  # noqa: E731
+        ctypes.byref(sh), k.get("W", 4), 1, k.get("batch", 2), None, k.get("ns", 4),
+        k.get("xBC", FAKE), FAKE, None, k.get("state", FAKE), FAKE, FAKE, FAKE, None)
+    assert upd(W=6) == -7
+    assert upd(state=None) == -1
+    assert upd(batch=5) == -2                                  # more rows than slots
+    assert upd(batch=0) == 0
+    assert upd(xBC=ctypes.c_void_p(0x1002)) == -9
 
 
 def test_python_binding_checks_extents():
