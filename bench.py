@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 PAGE_TOKENS = 64             # rows per buffer page in the paged replay-decode leg
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
-                  "ssd_internal.hpp"]
+                  "ssd_internal.hpp", "ssd_conv.hip"]
+CONV_W = 4                   # conv kernel width of the conv legs
 
 
 def kernel_source_sha() -> str:
@@ -80,6 +81,19 @@ def replay_step_bytes(ks, Q, H, G, P, N, io=2, dtb=2, with_C=False):
     # writes the new fp32 state and its bf16 copy
     return int(len(ks) * (state_bf + new_tok + append + y) + ks.sum() * per_buf_tok
                + commits * (H * P * N * (4 + 4 + 2) + Q * per_buf_tok))
+
+
+def conv_prefill_bytes(T, S, cd, W, io=2):
+    """Algorithmic bytes of one conv prefill launch: read xBC once, write
+    x | B | C once, read and write each sequence's conv state, read the taps
+    and bias."""
+    return 2 * T * cd * io + 2 * S * cd * (W - 1) * io + cd * (W + 1) * 4
+
+
+def conv_update_bytes(batch, cd, W, io=2):
+    """One conv decode step: the token's xBC in, x | B | C out, the conv
+    state read and written, the taps and bias."""
+    return batch * (2 * cd * io + 2 * cd * (W - 1) * io) + cd * (W + 1) * 4
 
 
 def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):
@@ -270,6 +284,23 @@ def main():
     planpg = erd.DecodePlan(shape, S, A, D, bias, cache=cachepg)
     plan_ssu = erd.DecodePlan(shape, S, A, D, bias, state=ssu_state)
     plan256.check(dx[0], ddt[0], dB[0], dC[0], ydec)
+
+    # conv before the scan (width CONV_W over x | B | C): prefill over the
+    # same 256 x 2048 pack, decode steps at B=256
+    cd = H * P + 2 * G * N
+    cparams = synth.make_conv_params(cd, CONV_W, 11)
+    cw = torch.from_numpy(cparams.weight).to(dev)
+    cbias = torch.from_numpy(cparams.bias).to(dev)
+    xbc = synth.make_xbc_torch(S * T, cd, 11, dev)
+    cstate = torch.zeros((S, cd, CONV_W - 1), dtype=torch.bfloat16, device=dev)
+    conv_out = (torch.empty_like(x), torch.empty_like(B), torch.empty_like(C))
+    dxbc = synth.make_xbc_torch(total_decode * S, cd, 12, dev).view(total_decode, S, cd)
+    ustate = torch.zeros((S, cd, CONV_W - 1), dtype=torch.bfloat16, device=dev)
+    uout = (torch.empty((S, H, P), dtype=torch.bfloat16, device=dev),
+            torch.empty((S, G, N), dtype=torch.bfloat16, device=dev),
+            torch.empty((S, G, N), dtype=torch.bfloat16, device=dev))
+    conv_plan = erd.ConvUpdatePlan(shape, S, cw, ustate, cbias)
+    conv_plan.check(dxbc[0], *uout)
     ks256 = (pre % Q).astype(np.int64)
     ks16 = (pre % 16).astype(np.int64)
     kspg = ks256.copy()
@@ -282,7 +313,7 @@ def main():
 
     def step(record):
         nonlocal decode_i, bytes_decode256, bytes_decode16, bytes_decodepg, ks256, ks16, kspg
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)] if record else None
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(9)] if record else None
         if record:
             ev[0].record(stream)
         erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
@@ -322,6 +353,14 @@ def main():
             kspg = (kspg + 1) % Q
         if record:
             ev[6].record(stream)
+        erd.ssd_conv1d_varlen(shape, cu, xbc, cw, cbias, conv_state=cstate, out=conv_out,
+                              cu_seqlens_host=cu_host)
+        if record:
+            ev[7].record(stream)
+        for r in range(R):
+            conv_plan(dxbc[decode_i + r], *uout)
+        if record:
+            ev[8].record(stream)
         decode_i += R
         return ev
 
@@ -343,7 +382,9 @@ def main():
     t_ssu = span(3, 4)
     t_dec16 = span(4, 5)
     t_decpg = span(5, 6)
-    t_total = span(0, 6)
+    t_conv = span(6, 7)
+    t_convu = span(7, 8)
+    t_total = span(0, 8)
 
     pb = prefill_bytes(S * T, S, H, G, P, N)
     pf = prefill_flops(S * T, H, G, P, N, Q)
@@ -355,6 +396,8 @@ def main():
     dec256_gbs = bytes_decode256 / t_dec256 / 1e9
     dec16_gbs = bytes_decode16 / t_dec16 / 1e9
     decpg_gbs = bytes_decodepg / t_decpg / 1e9
+    conv_gbs = conv_prefill_bytes(S * T, S, cd, CONV_W) * K / t_conv / 1e9
+    convu_gbs = conv_update_bytes(S, cd, CONV_W) * dec_steps / t_convu / 1e9
     ssu_gbs = ssu_step_bytes(S, H, G, P, N) * dec_steps / t_ssu / 1e9
 
     out = {
@@ -375,7 +418,8 @@ def main():
             "workload": "prefill 256 seqs x 2048 tokens (H=32 G=1 P=64 N=128 chunk 256, "
                         "bf16 x/dt/B/C/y, fp32 state) + boundary commit + replay decode "
                         "B=256 (chunk 256 and 16, 0..255 buffered tokens; chunk 256 also "
-                        "over paged buffers) + recurrent update B=256",
+                        "over paged buffers) + recurrent update B=256 + causal conv1d "
+                        "(width 4 over x|B|C) prefill on the same pack and decode at B=256",
             "global_batch": S, "seq_len": T, "heads": H, "groups": G, "headdim": P,
             "dstate": N, "chunk_size": Q, "decode_steps_per_step": R,
         },
@@ -402,6 +446,16 @@ def main():
             "ssu_hbm_gbs": ssu_gbs,
             "ssu_frac": ssu_gbs / HBM_PEAK_GBS,
             "batch": S,
+        },
+        "conv": {
+            "width": CONV_W, "conv_dim": cd,
+            "prefill_ms": 1e3 * t_conv / K,
+            "prefill_tokens_per_s": S * T * K / t_conv,
+            "prefill_hbm_gbs": conv_gbs,
+            "prefill_frac": conv_gbs / HBM_PEAK_GBS,
+            "update_steps_per_s": dec_steps / t_convu,
+            "update_hbm_gbs": convu_gbs,
+            "update_frac": convu_gbs / HBM_PEAK_GBS,
         },
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,

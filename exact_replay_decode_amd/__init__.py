@@ -4,7 +4,7 @@ The compute lives in libssd_replay.so (hand-written HIP, C ABI in
 include/ssd_replay.h); this package is its torch binding plus the seeded
 synthetic input generator (synth).
 """
-from .api import (Shape, ReplayCache, DecodePlan, ssd_prefill_varlen, ssd_commit_boundary,  # noqa: F401
+from .api import (Shape, ReplayCache, DecodePlan, ConvUpdatePlan, ssd_prefill_varlen, ssd_commit_boundary,  # noqa: F401
                   ssd_replay_prefill, ssd_replay_decode, ssm_state_update,
                   ssd_replay_cache_bytes, ssd_replay_page_bytes, ssd_conv1d_varlen,
                   ssd_conv1d_update, conv_dim, to_device, to_f64)

@@ -484,3 +484,42 @@ class DecodePlan:
                 self._b, y.data_ptr(), self._st)
         if rc != 0:
             _lib.check(rc, "DecodePlan")
+
+
+class ConvUpdatePlan:
+    """Pre-marshalled ssd_conv1d_update calls for a hot loop: each call only
+    passes the step's xBC [batch, conv_dim] and the x/B/C outputs."""
+
+    def __init__(self, shape: Shape, batch: int, weight, conv_state, bias=None, slot_idx=None,
+                 activation=True, stream=None):
+        dev = conv_state.device
+        cd = conv_dim(shape)
+        self.W = int(weight.shape[1])
+        _need(weight, "weight", (cd, self.W), torch.float32, dev)
+        _opt(bias, "bias", (cd,), torch.float32, dev)
+        self.ns = int(conv_state.shape[0])
+        _need(conv_state, "conv_state", (self.ns, cd, self.W - 1), shape.io, dev)
+        if slot_idx is None and batch > self.ns:
+            raise ValueError("batch exceeds conv state slots")
+        self.shape, self.batch, self.device = shape, batch, dev
+        self._keep = (weight, conv_state, bias, slot_idx)
+        self._sh = shape.c()
+        self._lib = _lib.load()
+        self._st = _stream(stream)
+        self._sl = _ptr(_slots(slot_idx, batch, dev))
+        self._w, self._b, self._cs = _ptr(weight), _ptr(bias), _ptr(conv_state)
+        self._act = int(bool(activation))
+
+    def check(self, xBC, x, B, C):
+        sh, dev, nb = self.shape, self.device, self.batch
+        _need(xBC, "xBC", (nb, conv_dim(sh)), sh.io, dev)
+        _conv_outputs(sh, nb, dev, (x, B, C))
+
+    def __call__(self, xBC, x, B, C):
+        """Launch one step; tensors must already satisfy check()."""
+        rc = self._lib.ssd_conv1d_update(
+            ctypes.byref(self._sh), self.W, self._act, self.batch, self._sl, self.ns,
+            xBC.data_ptr(), self._w, self._b, self._cs, x.data_ptr(), B.data_ptr(),
+            C.data_ptr(), self._st)
+        if rc != 0:
+            _lib.check(rc, "ConvUpdatePlan")
