@@ -23,7 +23,8 @@ STATUS = {
 EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
-           "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update")
+           "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
+           "ssd_replay_verify", "ssd_replay_accept")
 
 
 class ssd_shape(ctypes.Structure):
@@ -77,6 +78,12 @@ def load() -> ctypes.CDLL:
     lib.ssd_replay_prefill.restype = ctypes.c_int
     lib.ssd_replay_prefill.argtypes = [shp, cp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, vp]
+    lib.ssd_replay_verify.restype = ctypes.c_int
+    lib.ssd_replay_verify.argtypes = [shp, cp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp]
+    lib.ssd_replay_accept.restype = ctypes.c_int
+    lib.ssd_replay_accept.argtypes = [shp, cp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp]
     lib.ssd_replay_decode.restype = ctypes.c_int
     lib.ssd_replay_decode.argtypes = [shp, cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_conv1d_varlen.restype = ctypes.c_int

@@ -294,6 +294,57 @@ def ssd_replay_prefill(shape: Shape, cache: ReplayCache, cu_seqlens, x, dt, B, C
     return y
 
 
+def ssd_replay_verify(shape: Shape, cache: ReplayCache, cu_seqlens, x, dt, B, C, A, D=None,
+                      dt_bias=None, slot_idx=None, y=None, cu_seqlens_host=None, stream=None):
+    """Speculative verification: outputs of every draft token, replayed after
+    each slot's committed tokens; the cache is not changed. Returns y."""
+    dev = cache.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, S, dev)
+    y = torch.empty((T, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (T, H, P), shape.io, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_replay_verify(
+        ctypes.byref(sh), ctypes.byref(cs), S, T, host.ctypes.data_as(ctypes.c_void_p),
+        _ptr(cu), _ptr(sl), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+        _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssd_replay_verify")
+    return y
+
+
+def ssd_replay_accept(shape: Shape, cache: ReplayCache, cu_seqlens, accepted, x, dt, B, C, A,
+                      dt_bias=None, slot_idx=None, cu_seqlens_host=None, stream=None):
+    """Commit the first accepted[s] drafts of each sequence (accepted: int32
+    device tensor [S]); the drafts are the ones given to the verification."""
+    dev = cache.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    _need(accepted, "accepted", (S,), torch.int32, dev)
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, S, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_replay_accept(
+        ctypes.byref(sh), ctypes.byref(cs), S, T, host.ctypes.data_as(ctypes.c_void_p),
+        _ptr(cu), _ptr(sl), _ptr(accepted), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A),
+        _ptr(dt_bias), _stream(stream))
+    _lib.check(rc, "ssd_replay_accept")
+
+
 def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, dt_bias=None,
                       slot_idx=None, y=None, stream=None):
     """One exact-replay decode step for x.shape[0] sequences."""

@@ -119,6 +119,83 @@ size_t dtype_bytes(int dt) { return dt == SSD_BF16 ? 2 : 4; }
 
 }  // namespace
 
+namespace {
+
+// Replay-mode scan shared by prefill (mode 0), speculative verification
+// (mode 1: outputs only) and acceptance (mode 2: chunk states and buffer
+// append of the first take[s] tokens, no outputs).
+int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, int64_t T,
+                const int32_t *cu_host, const int32_t *cu, const int32_t *slot_idx,
+                const void *x, const void *dt, const void *B, const void *C, const float *A,
+                const float *D, const float *dt_bias, void *y, int mode, const int32_t *take,
+                hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_cache(sh, cache)) != SSD_OK)
+        return st;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (!slot_idx && S > cache->num_slots)
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return SSD_OK;
+    if (!A || (mode == 2 && !take))
+        return SSD_ERR_NULL;
+    if (T > 0 && (!x || !dt || !B))
+        return SSD_ERR_NULL;
+    if (T > 0 && mode != 2 && (!C || !y))
+        return SSD_ERR_NULL;
+    if (T > 0 && mode == 2 && cache->buf_C && !C)
+        return SSD_ERR_NULL;
+    if (!all_a16(x, B, C, y))
+        return SSD_ERR_ALIGN;
+    ssd::ScanArgs a = {};
+    a.d = d;
+    a.S = S;
+    a.cu = cu;
+    a.slot_idx = slot_idx;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = mode == 2 ? nullptr : y;
+    a.replay = 1;
+    a.num_slots = cache->num_slots;
+    a.cache_state = cache->state;
+    a.cache_state_bf = cache->state_bf;
+    a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
+    a.buf_len = cache->buf_len;
+    a.bm = buf_map(cache);
+    a.dry = mode == 1;
+    a.no_y = mode == 2;
+    a.take = mode == 2 ? take : nullptr;
+    hipError_t e = launch_scan_any(a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return SSD_ERR_HIP;
+    if (mode == 1)
+        return SSD_OK;
+    ssd::CommitArgs c = {};
+    c.d = d;
+    c.S = S;
+    c.cu = cu;
+    c.slot_idx = slot_idx;
+    c.x = x; c.dt = dt; c.B = B; c.C = C;
+    c.fresh = 0;
+    c.num_slots = cache->num_slots;
+    c.state_src = nullptr;
+    c.cache_state = cache->state;
+    c.cache_state_bf = cache->state_bf;
+    c.buf_x = cache->buf_x; c.buf_dt = cache->buf_dt;
+    c.buf_B = cache->buf_B; c.buf_C = cache->buf_C;
+    c.buf_len = cache->buf_len;
+    c.boundary_pos = cache->boundary_pos;
+    c.bm = a.bm;
+    c.take = a.take;
+    return hip_status(ssd::launch_commit(c, (hipStream_t)stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *ssd_status_string(int status) {
@@ -262,57 +339,25 @@ int ssd_replay_prefill(const ssd_shape *sh, const ssd_replay_cache *cache, int32
                        const void *x, const void *dt, const void *B, const void *C,
                        const float *A, const float *D, const float *dt_bias, void *y,
                        hipStream_t stream) {
-    Dims d;
-    int st = check_shape(sh, &d);
-    if (st != SSD_OK)
-        return st;
-    if ((st = check_cache(sh, cache)) != SSD_OK)
-        return st;
-    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
-        return st;
-    if (!slot_idx && S > cache->num_slots)
-        return SSD_ERR_SHAPE;
-    if (S == 0)
-        return SSD_OK;
-    if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
-        return SSD_ERR_NULL;
-    if (!all_a16(x, B, C, y))
-        return SSD_ERR_ALIGN;
-    ssd::ScanArgs a = {};
-    a.d = d;
-    a.S = S;
-    a.cu = cu;
-    a.slot_idx = slot_idx;
-    a.x = x; a.dt = dt; a.B = B; a.C = C;
-    a.A = A; a.D = D; a.dt_bias = dt_bias;
-    a.y = y;
-    a.replay = 1;
-    a.num_slots = cache->num_slots;
-    a.cache_state = cache->state;
-    a.cache_state_bf = cache->state_bf;
-    a.buf_x = cache->buf_x; a.buf_dt = cache->buf_dt; a.buf_B = cache->buf_B;
-    a.buf_len = cache->buf_len;
-    a.bm = buf_map(cache);
-    hipError_t e = launch_scan_any(a, (hipStream_t)stream);
-    if (e != hipSuccess)
-        return SSD_ERR_HIP;
-    ssd::CommitArgs c = {};
-    c.d = d;
-    c.S = S;
-    c.cu = cu;
-    c.slot_idx = slot_idx;
-    c.x = x; c.dt = dt; c.B = B; c.C = C;
-    c.fresh = 0;
-    c.num_slots = cache->num_slots;
-    c.state_src = nullptr;
-    c.cache_state = cache->state;
-    c.cache_state_bf = cache->state_bf;
-    c.buf_x = cache->buf_x; c.buf_dt = cache->buf_dt;
-    c.buf_B = cache->buf_B; c.buf_C = cache->buf_C;
-    c.buf_len = cache->buf_len;
-    c.boundary_pos = cache->boundary_pos;
-    c.bm = a.bm;
-    return hip_status(ssd::launch_commit(c, (hipStream_t)stream));
+    return replay_scan(sh, cache, S, T, cu_host, cu, slot_idx, x, dt, B, C, A, D, dt_bias, y, 0,
+                       nullptr, stream);
+}
+
+int ssd_replay_verify(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, int64_t T,
+                      const int32_t *cu_host, const int32_t *cu, const int32_t *slot_idx,
+                      const void *x, const void *dt, const void *B, const void *C,
+                      const float *A, const float *D, const float *dt_bias, void *y,
+                      hipStream_t stream) {
+    return replay_scan(sh, cache, S, T, cu_host, cu, slot_idx, x, dt, B, C, A, D, dt_bias, y, 1,
+                       nullptr, stream);
+}
+
+int ssd_replay_accept(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, int64_t T,
+                      const int32_t *cu_host, const int32_t *cu, const int32_t *slot_idx,
+                      const int32_t *accepted, const void *x, const void *dt, const void *B,
+                      const void *C, const float *A, const float *dt_bias, hipStream_t stream) {
+    return replay_scan(sh, cache, S, T, cu_host, cu, slot_idx, x, dt, B, C, A, nullptr, dt_bias,
+                       nullptr, 2, accepted, stream);
 }
 
 int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,

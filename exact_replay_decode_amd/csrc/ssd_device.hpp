@@ -65,6 +65,16 @@ __host__ __device__ __forceinline__ int replay_npos(int nbuf, int len, int Q) {
     return total < Q ? total : (nbuf > tail ? nbuf : tail);
 }
 
+// Token count of sequence s: its cu_seqlens span, capped by take[s] when
+// given (accepted draft counts; negative counts as 0).
+__device__ __forceinline__ int seq_len(const int32_t *cu, const int32_t *take, int s) {
+    const int len = cu[s + 1] - cu[s];
+    if (!take)
+        return len;
+    const int t = take[s];
+    return t < 0 ? 0 : (t < len ? t : len);
+}
+
 // ---- scalar functions that fix the rounding ------------------------------
 
 // delta = softplus(dt + bias) computed as log1p(exp(u)) for u <= 0 and

@@ -46,6 +46,12 @@ struct ScanArgs {
     const void *buf_x, *buf_dt, *buf_B;
     const int32_t *buf_len;   // [slots]
     BufMap bm;
+    // speculative drafts (replay mode): dry = outputs only, the cache is not
+    // written (verification); no_y = no outputs, only the chunk states of
+    // chunks that fill (acceptance); take[s] (device, or null) caps sequence
+    // s's token count
+    int32_t dry, no_y;
+    const int32_t *take;
 };
 
 // Write the trailing partial chunk of each sequence into the slot buffers
@@ -65,6 +71,7 @@ struct CommitArgs {
     int32_t *buf_len;
     int64_t *boundary_pos;
     BufMap bm;
+    const int32_t *take;      // [S] caps each sequence's token count, or null
 };
 
 struct DecodeArgs {

@@ -730,15 +730,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     const MLayout L(Qp, P, N);
 
     const int64_t t0 = a.cu[s];
-    const int len = a.cu[s + 1] - a.cu[s];
+    const int len = seq_len(a.cu, a.take, s);
     const int slot = a.replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
     if (a.replay && (len == 0 || slot < 0 || slot >= a.num_slots))
         return;
     const int nbuf = a.replay ? a.buf_len[slot] : 0;
     if (nbuf < 0 || nbuf >= Q)
         return;
+    // acceptance without a chunk that fills has no work here (the buffer
+    // append is the commit kernel's)
+    if (a.no_y && nbuf + len < Q)
+        return;
     const SlotRows<PG> rows(a.bm, slot, Q);
-    if (!rows.ok(a.bm, replay_npos(nbuf, len, Q)))
+    if (!rows.ok(a.bm, a.dry ? nbuf : replay_npos(nbuf, len, Q)))
         return;
 
     float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
@@ -767,15 +771,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     const float D_h = a.D ? a.D[h] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const int total = nbuf + len;
-    const int nchunks = (total + Q - 1) / Q;
     const int nfull = total / Q;
+    // without outputs only the chunks that fill are processed
+    const int nchunks = a.no_y ? nfull : (total + Q - 1) / Q;
     float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
                                               : nullptr);
     uint16_t *bnd_bf = a.replay ? static_cast<uint16_t *>(a.cache_state_bf) +
                                       ((int64_t)slot * H + h) * PN
                                 : nullptr;
-    const bool write_bnd = bnd && (!a.replay || nfull > 0);
+    const bool write_bnd = bnd && (!a.replay || nfull > 0) && !a.dry;
     uint16_t *y = static_cast<uint16_t *>(a.y);
     const int tau = wave_tblock(Qp / 32, wave);
     auto set_chunk = [&](int c) {
@@ -803,7 +808,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
                                             L);
         __syncthreads();
         const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, n_valid);
-        const bool has_rows = tau >= 0 && lo < hi;
+        const bool has_rows = tau >= 0 && lo < hi && !a.no_y;
         bf16x8 cf[N / 16];
         if (has_rows)
             load_cfrag<N, DT>(v, tau, lo, cf);

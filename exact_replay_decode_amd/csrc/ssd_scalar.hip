@@ -292,14 +292,17 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
     const LdsLayout L(P, N);
 
     const int64_t t0 = a.cu[s];
-    const int len = a.cu[s + 1] - a.cu[s];
+    const int len = seq_len(a.cu, a.take, s);
     const int slot = a.replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
     if (a.replay && (len == 0 || slot < 0 || slot >= a.num_slots))
         return;
     const int nbuf = a.replay ? a.buf_len[slot] : 0;
     if (nbuf < 0 || nbuf >= Q)  // corrupt slot metadata: leave the slot alone
         return;
-    if (a.replay && !buf_pages_ok(a.bm, slot, replay_npos(nbuf, len, Q)))
+    // acceptance without a chunk that fills: only the commit kernel's append
+    if (a.no_y && nbuf + len < Q)
+        return;
+    if (a.replay && !buf_pages_ok(a.bm, slot, a.dry ? nbuf : replay_npos(nbuf, len, Q)))
         return;
 
     const float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
@@ -322,15 +325,16 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
     const float D_h = a.D ? a.D[h] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const int total = nbuf + len;
-    const int nchunks = (total + Q - 1) / Q;
     const int nfull = total / Q;
+    // without outputs only the chunks that fill are processed
+    const int nchunks = a.no_y ? nfull : (total + Q - 1) / Q;
     float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
                                               : nullptr);
     uint16_t *bnd_bf = a.replay ? static_cast<uint16_t *>(a.cache_state_bf) +
                                       ((int64_t)slot * H + h) * PN
                                 : nullptr;
-    const bool write_bnd = bnd && (!a.replay || nfull > 0);
+    const bool write_bnd = bnd && (!a.replay || nfull > 0) && !a.dry;
     T *y = static_cast<T *>(a.y);
 
     for (int c = 0; c < nchunks; ++c) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
         v.n_valid = min(Q, total - c * Q);
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
         prepare_chunk(v, A_h, bias, d.softplus, lds, L);
-        for (int rt = (v.nb / kRows) * kRows; rt < v.n_valid; rt += kRows)
+        for (int rt = (v.nb / kRows) * kRows; !a.no_y && rt < v.n_valid; rt += kRows)
             emit_rows(v, max(rt, v.nb), min(rt + kRows, v.n_valid), D_h, y, lds, L);
         if (v.n_valid == Q || (!a.replay && a.final_state))
             chunk_state_update(v, lds, L);
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     const int H = d.H, G = d.G, P = d.P, N = d.N, Q = d.Q;
     const int slot = a.slot_idx ? a.slot_idx[s] : s;
     const int64_t t0 = a.cu[s];
-    const int len = a.cu[s + 1] - a.cu[s];
+    const int len = seq_len(a.cu, a.take, s);
     if ((!a.fresh && len == 0) || slot < 0 || slot >= a.num_slots)
         return;
     if (part > 0) {

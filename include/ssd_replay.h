@@ -236,6 +236,40 @@ int ssd_replay_decode(const ssd_shape *shape, const ssd_replay_cache *cache,
                       const float *A, const float *D, const float *dt_bias,
                       void *y, hipStream_t stream);
 
+/* Speculative verification, output only ([RSSM] "Motivation and method":
+ * drafts are verified with an output-only form instead of materialising a
+ * state per draft; the acceptance length then advances only the committed
+ * input pointer, and rejected drafts never enter the recurrence).
+ * Sequence s has draft tokens cu[s]..cu[s+1]-1 (x/dt/B/C as in prefill) and
+ * slot slot_idx[s] (NULL = s). The drafts are replayed after the slot's
+ * committed tokens through the prefill's chunk arithmetic, crossing chunk
+ * boundaries on chip, and y[T,H,P] receives every draft's output. Nothing in
+ * the cache is written. Draft j's output is bit-identical to the one a
+ * decode step would give it after drafts 0..j-1 were accepted. Paged
+ * caches need pages for the committed positions only. Slots distinct. */
+int ssd_replay_verify(const ssd_shape *shape, const ssd_replay_cache *cache,
+                      int32_t num_seqs, int64_t total_tokens,
+                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens,
+                      const int32_t *slot_idx, const void *x, const void *dt,
+                      const void *B, const void *C, const float *A,
+                      const float *D, const float *dt_bias, void *y,
+                      hipStream_t stream);
+
+/* Acceptance after ssd_replay_verify: commit the first accepted[s] drafts
+ * of each sequence (accepted: device int32 [S], clamped to [0, drafts]) as
+ * if they had been decoded one by one: they are appended to the slot's
+ * buffer, and each chunk they fill becomes the new boundary state (the
+ * prefill's chunk-state update); buf_len and boundary_pos advance. The
+ * drafts are passed again exactly as to the verification; the rejected ones
+ * are never read. No outputs are computed (D is not needed); C is read only
+ * when the cache buffers C. Slots distinct. */
+int ssd_replay_accept(const ssd_shape *shape, const ssd_replay_cache *cache,
+                      int32_t num_seqs, int64_t total_tokens,
+                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens,
+                      const int32_t *slot_idx, const int32_t *accepted,
+                      const void *x, const void *dt, const void *B, const void *C,
+                      const float *A, const float *dt_bias, hipStream_t stream);
+
 /* Recurrent selective-state update, the conventional decode path the RFC
  * compares against ([RFC] section 1; [RSSM] "Motivation and method": it
  * reads and writes the full state every token). For slot = slot_idx[b]

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     want = {"ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace_bytes",
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
-            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update"}
+            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
+            "ssd_replay_verify", "ssd_replay_accept"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -151,6 +152,26 @@ def test_replay_fails_closed():
                                 FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == -4
     assert lib.ssm_state_update(ctypes.byref(sh), 3, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, None, None, FAKE, None) == -2
+
+
+def test_speculative_entry_points_fail_closed():
+    sh = shape()
+    lib = _lib.load()
+    cu = np.asarray([0, 4], dtype=np.int32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    verify = lambda c, **k: lib.ssd_replay_verify(  # noqa: E731
+        ctypes.byref(sh), ctypes.byref(c), 1, 4, cup, FAKE, None, FAKE, FAKE, FAKE,
+        k.get("C", FAKE), FAKE, None, None, k.get("y", FAKE), None)
+    accept = lambda c, **k: lib.ssd_replay_accept(  # noqa: E731
+        ctypes.byref(sh), ctypes.byref(c), 1, 4, cup, FAKE, None, k.get("acc", FAKE), FAKE,
+        FAKE, FAKE, k.get("C", None), FAKE, None, None)
+    assert verify(cache(sh, chunk_size=32)) == -5
+    assert verify(cache(sh, state_dtype=1)) == -4
+    assert verify(cache(sh), y=None) == -1
+    assert verify(cache(sh), C=None) == -1
+    assert accept(cache(sh), acc=None) == -1
+    assert accept(cache(sh, buf_C=0x1000)) == -1             # C buffered: C needed
+    assert accept(cache(sh, chunk_size=64)) == -5
 
 
 def test_paged_cache_checks():
