@@ -41,6 +41,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
                   "ssd_internal.hpp", "ssd_conv.hip"]
 CONV_W = 4                   # conv kernel width of the conv legs
+SPEC_BATCH, SPEC_T = 512, 4  # speculative verification: sequences, drafts each
 
 
 def kernel_source_sha() -> str:
@@ -94,6 +95,30 @@ def conv_update_bytes(batch, cd, W, io=2):
     """One conv decode step: the token's xBC in, x | B | C out, the conv
     state read and written, the taps and bias."""
     return batch * (2 * cd * io + 2 * cd * (W - 1) * io) + cd * (W + 1) * 4
+
+
+def verify_step_bytes(ks, T, Q, H, G, P, N, io=2, dtb=2):
+    """One speculative verification of T drafts per sequence with ks
+    committed tokens: the state read-out operand (bf16 copy, or the fp32
+    state when the drafts cross the chunk end), the committed rows' x, B and
+    raw dt, the drafts' x, dt, B, C and their outputs."""
+    ks = np.asarray(ks, dtype=np.int64)
+    cross = ks + T > Q
+    state = np.where(cross, H * P * N * 4, H * P * N * 2)
+    per_buf_tok = H * P * io + G * N * io + H * dtb
+    draft = H * P * io + H * dtb + 2 * G * N * io + H * P * io
+    return int(state.sum() + ks.sum() * per_buf_tok + len(ks) * T * draft)
+
+
+def accept_step_bytes(ks, acc, Q, H, G, P, N, io=2, dtb=2):
+    """Committing acc drafts per sequence: read and append them; a chunk that
+    fills reads the fp32 state and the chunk's rows and writes the state and
+    its bf16 copy."""
+    ks, acc = np.asarray(ks, dtype=np.int64), np.asarray(acc, dtype=np.int64)
+    per_tok = H * P * io + G * N * io + H * dtb
+    fills = (ks + acc) >= Q
+    commit = H * P * N * (4 + 4 + 2) + Q * per_tok
+    return int(2 * acc.sum() * per_tok + fills.sum() * commit)
 
 
 def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):
@@ -301,6 +326,24 @@ def main():
             torch.empty((S, G, N), dtype=torch.bfloat16, device=dev))
     conv_plan = erd.ConvUpdatePlan(shape, S, cw, ustate, cbias)
     conv_plan.check(dxbc[0], *uout)
+
+    # speculative decoding: SPEC_BATCH sequences, SPEC_T drafts verified per
+    # step, a seeded number of them accepted (drafts drawn from a pool of 8
+    # steps' worth of tokens)
+    SB, ST = SPEC_BATCH, SPEC_T
+    spre = synth.replay_prefix_lengths(SB, Q, 5)
+    sx, sdt, sB, sC = synth.make_tokens_torch(int(spre.sum()), H, G, P, N, 5, dev)
+    scache = erd.ReplayCache(shape, SB, dev)
+    erd.ssd_replay_prefill(shape, scache, synth.cu_seqlens(spre), sx, sdt, sB, sC, A, D, bias)
+    del sx, sdt, sB, sC
+    pool = [synth.make_tokens_torch(SB * ST, H, G, P, N, 100 + i, dev) for i in range(8)]
+    scu_host = synth.cu_seqlens([ST] * SB)
+    scu = torch.from_numpy(scu_host).to(dev)
+    sy = torch.empty((SB * ST, H, P), dtype=torch.bfloat16, device=dev)
+    arng = np.random.default_rng(7)
+    accs = arng.integers(0, ST + 1, size=(total_decode, SB)).astype(np.int32)
+    accs_dev = torch.from_numpy(accs).to(dev)
+    sks = (spre % Q).astype(np.int64)
     ks256 = (pre % Q).astype(np.int64)
     ks16 = (pre % 16).astype(np.int64)
     kspg = ks256.copy()
@@ -309,11 +352,15 @@ def main():
 
     stream = torch.cuda.current_stream()
     bytes_decode256 = bytes_decode16 = bytes_decodepg = 0
+    bytes_verify = bytes_accept = 0
     decode_i = 0
 
     def step(record):
         nonlocal decode_i, bytes_decode256, bytes_decode16, bytes_decodepg, ks256, ks16, kspg
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(9)] if record else None
+        nonlocal sks, bytes_verify, bytes_accept
+        # events 0..8 bracket the legs; 9.. follow every verification and
+        # every acceptance of the speculative leg
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(9 + 2 * R)] if record else None
         if record:
             ev[0].record(stream)
         erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
@@ -361,6 +408,21 @@ def main():
             conv_plan(dxbc[decode_i + r], *uout)
         if record:
             ev[8].record(stream)
+        # speculative rounds: verify SPEC_T drafts, accept a seeded count
+        for r in range(R):
+            k = decode_i + r
+            dxs, ddts, dBs, dCs = pool[k % len(pool)]
+            erd.ssd_replay_verify(shape, scache, scu, dxs, ddts, dBs, dCs, A, D, bias, y=sy,
+                                  cu_seqlens_host=scu_host)
+            if record:
+                bytes_verify += verify_step_bytes(sks, ST, Q, H, G, P, N)
+                ev[9 + 2 * r].record(stream)
+            erd.ssd_replay_accept(shape, scache, scu, accs_dev[k], dxs, ddts, dBs, dCs, A, bias,
+                                  cu_seqlens_host=scu_host)
+            if record:
+                bytes_accept += accept_step_bytes(sks, accs[k], Q, H, G, P, N)
+                ev[10 + 2 * r].record(stream)
+            sks = (sks + accs[k]) % Q
         decode_i += R
         return ev
 
@@ -384,7 +446,9 @@ def main():
     t_decpg = span(5, 6)
     t_conv = span(6, 7)
     t_convu = span(7, 8)
-    t_total = span(0, 8)
+    t_verify = sum(span(8 if r == 0 else 8 + 2 * r, 9 + 2 * r) for r in range(R))
+    t_accept = sum(span(9 + 2 * r, 10 + 2 * r) for r in range(R))
+    t_total = span(0, 8 + 2 * R)
 
     pb = prefill_bytes(S * T, S, H, G, P, N)
     pf = prefill_flops(S * T, H, G, P, N, Q)
@@ -397,6 +461,8 @@ def main():
     dec16_gbs = bytes_decode16 / t_dec16 / 1e9
     decpg_gbs = bytes_decodepg / t_decpg / 1e9
     conv_gbs = conv_prefill_bytes(S * T, S, cd, CONV_W) * K / t_conv / 1e9
+    verify_gbs = bytes_verify / t_verify / 1e9
+    accept_gbs = bytes_accept / t_accept / 1e9
     convu_gbs = conv_update_bytes(S, cd, CONV_W) * dec_steps / t_convu / 1e9
     ssu_gbs = ssu_step_bytes(S, H, G, P, N) * dec_steps / t_ssu / 1e9
 
@@ -419,7 +485,8 @@ def main():
                         "bf16 x/dt/B/C/y, fp32 state) + boundary commit + replay decode "
                         "B=256 (chunk 256 and 16, 0..255 buffered tokens; chunk 256 also "
                         "over paged buffers) + recurrent update B=256 + causal conv1d "
-                        "(width 4 over x|B|C) prefill on the same pack and decode at B=256",
+                        "(width 4 over x|B|C) prefill on the same pack and decode at B=256 + "
+                        "speculative verification of 4 drafts and acceptance at B=512",
             "global_batch": S, "seq_len": T, "heads": H, "groups": G, "headdim": P,
             "dstate": N, "chunk_size": Q, "decode_steps_per_step": R,
         },
@@ -456,6 +523,16 @@ def main():
             "update_steps_per_s": dec_steps / t_convu,
             "update_hbm_gbs": convu_gbs,
             "update_frac": convu_gbs / HBM_PEAK_GBS,
+        },
+        "speculative": {
+            "batch": SPEC_BATCH, "drafts": SPEC_T, "chunk_size": Q,
+            "verify_steps_per_s": dec_steps / t_verify,
+            "verify_tokens_per_s": dec_steps * SPEC_BATCH * SPEC_T / t_verify,
+            "verify_hbm_gbs": verify_gbs,
+            "verify_frac": verify_gbs / HBM_PEAK_GBS,
+            "accept_steps_per_s": dec_steps / t_accept,
+            "accept_hbm_gbs": accept_gbs,
+            "accept_frac": accept_gbs / HBM_PEAK_GBS,
         },
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,
