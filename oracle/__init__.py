@@ -10,5 +10,7 @@ library.
   independent formulation used to pin ``scan``.
 - ``conv1d``: the causal depthwise conv1d before the scan (prefill and decode
   forms are one definition), in numpy.
+- ``ssu``: the recurrent update with the state rounded to the cache dtype
+  after every token (packed-history recovery), in numpy.
 """
 from .oracle import scan, threads, ensure_built  # noqa: F401
