@@ -6,7 +6,7 @@ synthetic input generator (synth).
 """
 from .api import (Shape, ReplayCache, DecodePlan, ConvUpdatePlan, ssd_prefill_varlen, ssd_commit_boundary,  # noqa: F401
                   ssd_replay_prefill, ssd_replay_decode, ssm_state_update,
-                  ssd_replay_verify, ssd_replay_accept,
+                  ssd_replay_verify, ssd_replay_accept, ssm_state_update_varlen,
                   ssd_replay_cache_bytes, ssd_replay_page_bytes, ssd_conv1d_varlen,
                   ssd_conv1d_update, conv_dim, to_device, to_f64)
 from ._lib import SsdError, load as load_library  # noqa: F401

@@ -24,7 +24,7 @@ EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
-           "ssd_replay_verify", "ssd_replay_accept")
+           "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen")
 
 
 class ssd_shape(ctypes.Structure):
@@ -92,6 +92,9 @@ def load() -> ctypes.CDLL:
     lib.ssd_conv1d_update.restype = ctypes.c_int
     lib.ssd_conv1d_update.argtypes = [shp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                       vp]
+    lib.ssm_state_update_varlen.restype = ctypes.c_int
+    lib.ssm_state_update_varlen.argtypes = [shp, i32, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp]
     lib.ssm_state_update.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [shp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib

@@ -440,12 +440,13 @@ def ssd_conv1d_update(shape: Shape, xBC, weight, conv_state, bias=None, slot_idx
 def ssm_state_update(shape: Shape, state, x, dt, B, C, A, D=None, dt_bias=None, slot_idx=None,
                      y=None, stream=None):
     """One recurrent selective-state update for x.shape[0] sequences; state
-    [num_slots,H,P,N] fp32 is updated in place."""
+    [num_slots,H,P,N] (shape.state_dtype: fp32 or bf16) is updated in
+    place."""
     dev = state.device
     H, G, P, N = shape.H, shape.G, shape.P, shape.N
     nb = int(x.shape[0])
     ns = int(state.shape[0])
-    _need(state, "state", (ns, H, P, N), torch.float32, dev)
+    _need(state, "state", (ns, H, P, N), _DT[shape.state_dtype], dev)
     _need(x, "x", (nb, H, P), shape.io, dev)
     _need(dt, "dt", (nb, H), shape.dtt, dev)
     _need(B, "B", (nb, G, N), shape.io, dev)
@@ -461,6 +462,37 @@ def ssm_state_update(shape: Shape, state, x, dt, B, C, A, D=None, dt_bias=None, 
         ctypes.byref(sh), nb, ns, _ptr(sl), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
         _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
     _lib.check(rc, "ssm_state_update")
+    return y
+
+
+def ssm_state_update_varlen(shape: Shape, state, cu_seqlens, x, dt, B, C, A, D=None,
+                            dt_bias=None, slot_idx=None, y=None, cu_seqlens_host=None,
+                            stream=None):
+    """Multi-token recurrent update over a varlen pack (packed-history
+    recovery): sequence s advances state[slot_idx[s]] token by token with
+    the state rounded to shape.state_dtype after each token. Returns y."""
+    dev = state.device
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
+    S, T = host.size - 1, int(x.shape[0])
+    ns = int(state.shape[0])
+    _need(state, "state", (ns, H, P, N), _DT[shape.state_dtype], dev)
+    _need(x, "x", (T, H, P), shape.io, dev)
+    _need(dt, "dt", (T, H), shape.dtt, dev)
+    _need(B, "B", (T, G, N), shape.io, dev)
+    _need(C, "C", (T, G, N), shape.io, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, S, dev)
+    y = torch.empty((T, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (T, H, P), shape.io, dev)
+    sh = shape.c()
+    rc = _lib.load().ssm_state_update_varlen(
+        ctypes.byref(sh), S, T, host.ctypes.data_as(ctypes.c_void_p), _ptr(cu), _ptr(sl), ns,
+        _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        _ptr(y), _stream(stream))
+    _lib.check(rc, "ssm_state_update_varlen")
     return y
 
 
@@ -505,7 +537,7 @@ class DecodePlan:
             self._cs = cache.struct()
             self._state = None
         else:
-            _need(state, "state", tuple(state.shape), torch.float32, dev)
+            _need(state, "state", tuple(state.shape), _DT[shape.state_dtype], dev)
             if state.dim() != 4 or tuple(state.shape[1:]) != (H, shape.P, shape.N):
                 raise ValueError("state must be [num_slots, H, P, N]")
             self._state = state

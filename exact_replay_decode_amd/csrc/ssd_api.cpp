@@ -18,10 +18,12 @@ bool pow2_in(int v, int lo, int hi) {
     return (v & (v - 1)) == 0;
 }
 
-int check_shape(const ssd_shape *sh, Dims *d) {
+// bf16_state: the recurrent update also takes a bf16 state; everything that
+// touches the replay cache requires fp32 ([RFC] section 4).
+int check_shape(const ssd_shape *sh, Dims *d, bool bf16_state = false) {
     if (!sh)
         return SSD_ERR_NULL;
-    if (sh->state_dtype != SSD_F32)
+    if (sh->state_dtype != SSD_F32 && !(bf16_state && sh->state_dtype == SSD_BF16))
         return SSD_ERR_STATE_NOT_FP32;
     if ((sh->io_dtype != SSD_F32 && sh->io_dtype != SSD_BF16) ||
         (sh->dt_dtype != SSD_F32 && sh->dt_dtype != SSD_BF16))
@@ -469,11 +471,11 @@ int ssd_conv1d_update(const ssd_shape *sh, int32_t W, int32_t act, int32_t batch
 }
 
 int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,
-                     const int32_t *slot_idx, float *state, const void *x, const void *dt,
+                     const int32_t *slot_idx, void *state, const void *x, const void *dt,
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, void *y, hipStream_t stream) {
     Dims d;
-    int st = check_shape(sh, &d);
+    int st = check_shape(sh, &d, true);
     if (st != SSD_OK)
         return st;
     if (batch < 0 || num_slots < 0 || (!slot_idx && batch > num_slots) ||
@@ -491,6 +493,40 @@ int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,
     a.slot_idx = slot_idx;
     a.num_slots = num_slots;
     a.state = state;
+    a.state_bf16 = sh->state_dtype == SSD_BF16;
+    a.x = x; a.dt = dt; a.B = B; a.C = C;
+    a.A = A; a.D = D; a.dt_bias = dt_bias;
+    a.y = y;
+    return hip_status(ssd::launch_ssu(a, (hipStream_t)stream));
+}
+
+int ssm_state_update_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t *cu_host,
+                            const int32_t *cu, const int32_t *slot_idx, int32_t num_slots,
+                            void *state, const void *x, const void *dt, const float *A,
+                            const void *B, const void *C, const float *D, const float *dt_bias,
+                            void *y, hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d, true);
+    if (st != SSD_OK)
+        return st;
+    if ((st = check_seqs(d, S, T, cu_host, cu)) != SSD_OK)
+        return st;
+    if (num_slots < 0 || (!slot_idx && S > num_slots))
+        return SSD_ERR_SHAPE;
+    if (S == 0)
+        return SSD_OK;
+    if (!state || !A || (T > 0 && (!x || !dt || !B || !C || !y)))
+        return SSD_ERR_NULL;
+    if (!all_a16(state, x, B, C, y))
+        return SSD_ERR_ALIGN;
+    ssd::SsuArgs a = {};
+    a.d = d;
+    a.batch = S;
+    a.slot_idx = slot_idx;
+    a.num_slots = num_slots;
+    a.state = state;
+    a.state_bf16 = sh->state_dtype == SSD_BF16;
+    a.cu = cu;
     a.x = x; a.dt = dt; a.B = B; a.C = C;
     a.A = A; a.D = D; a.dt_bias = dt_bias;
     a.y = y;

@@ -110,12 +110,16 @@ struct ConvArgs {
     void *x, *B, *C;          // outputs [T,H,P], [T,G,N], [T,G,N]
 };
 
+// Recurrent update: batch rows of one token each, or (cu given) batch
+// sequences of a varlen pack, each a run of tokens.
 struct SsuArgs {
     Dims d;
     int32_t batch;
     const int32_t *slot_idx;
     int32_t num_slots;
-    float *state;
+    void *state;              // [slots,H,P,N] fp32, or bf16 when state_bf16
+    int32_t state_bf16;
+    const int32_t *cu;        // [batch+1] or null
     const void *x, *dt, *B, *C;
     const float *A, *D, *dt_bias;
     void *y;

@@ -542,10 +542,67 @@ __global__ __launch_bounds__(kBlock) void k_refresh_state_bf(const float *state,
     }
 }
 
+// State storage of the recurrent update: fp32, or bf16 (rounded to nearest
+// even on every store, the cache-dtype rounding of each token).
+struct StF32 {
+    using T = float;
+    __device__ static __forceinline__ float4 load(const T *st, int f) {
+        return reinterpret_cast<const float4 *>(st)[f];
+    }
+    __device__ static __forceinline__ void store(T *st, int f, const float4 &v) {
+        reinterpret_cast<float4 *>(st)[f] = v;
+    }
+    // the value the store keeps (fp32: the value itself)
+    __device__ static __forceinline__ float4 round(const float4 &v) { return v; }
+};
+
+struct StBF16 {
+    using T = uint16_t;
+    __device__ static __forceinline__ float4 load(const T *st, int f) {
+        const uint2 u = reinterpret_cast<const uint2 *>(st)[f];
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+    __device__ static __forceinline__ void store(T *st, int f, const float4 &v) {
+        reinterpret_cast<uint2 *>(st)[f] =
+            make_uint2(bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
+                       bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
+    }
+    __device__ static __forceinline__ float4 round(const float4 &v) {
+        auto r = [](float a) { return __uint_as_float((uint32_t)bf16_rne(a) << 16); };
+        return make_float4(r(v.x), r(v.y), r(v.z), r(v.w));
+    }
+};
+
+// One token of the recurrent update on one float4 group of row p of the
+// [P, N] state (4 consecutive n): s = alpha s + (delta x_p) B_n, and this
+// group's share of y_p = sum_n s C_n. The one-token and the multi-token
+// kernels both use exactly this, so their bits agree.
+__device__ __forceinline__ float ssu_group(float4 &s4, float alpha, float dx, const float (&bv)[4],
+                                           const float (&cv)[4]) {
+    s4.x = fmaf(alpha, s4.x, dx * bv[0]);
+    s4.y = fmaf(alpha, s4.y, dx * bv[1]);
+    s4.z = fmaf(alpha, s4.z, dx * bv[2]);
+    s4.w = fmaf(alpha, s4.w, dx * bv[3]);
+    float part = s4.x * cv[0];
+    part = fmaf(s4.y, cv[1], part);
+    part = fmaf(s4.z, cv[2], part);
+    part = fmaf(s4.w, cv[3], part);
+    return part;
+}
+
+// Row sum over the n4 lanes holding row p (butterfly), then y_p.
+__device__ __forceinline__ float ssu_row_out(float part, int n4, float D_h, float xv) {
+    for (int off = 1; off < n4; off <<= 1)
+        part = part + __shfl_xor(part, off, 64);
+    return fmaf(D_h, xv, part) + 0.0f;   // -0 -> +0
+}
+
 // Recurrent update, one workgroup per (head, batch row). Thread t owns the
 // float4 groups f = t + 256 i of the [P, N] state (coalesced rows); row p's
-// output is a butterfly sum over the N/4 lanes that hold it.
-template <class IO, class DT>
+// output is a butterfly sum over the N/4 lanes that hold it. The state is
+// read, updated in fp32 and stored in its cache dtype.
+template <class IO, class DT, class ST>
 __global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
     using T = typename IO::T;
     using TD = typename DT::T;
@@ -572,30 +629,90 @@ __global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
         cv[i] = IO::ld(Ct, i);
     }
     const T *xt = static_cast<const T *>(a.x) + ((int64_t)b * H + h) * P;
-    float4 *st = reinterpret_cast<float4 *>(a.state + ((int64_t)slot * H + h) * P * N);
+    typename ST::T *st = static_cast<typename ST::T *>(a.state) + ((int64_t)slot * H + h) * P * N;
     T *y = static_cast<T *>(a.y) + ((int64_t)b * H + h) * P;
     const int nf = P * n4;
     for (int f = tid; f < nf; f += kBlock) {
         const int p = f / n4;
         const float xv = IO::ld(xt, p);
-        const float dx = dl * xv;
-        float4 s4 = st[f];
-        s4.x = fmaf(alpha, s4.x, dx * bv[0]);
-        s4.y = fmaf(alpha, s4.y, dx * bv[1]);
-        s4.z = fmaf(alpha, s4.z, dx * bv[2]);
-        s4.w = fmaf(alpha, s4.w, dx * bv[3]);
-        st[f] = s4;
-        float part = s4.x * cv[0];
-        part = fmaf(s4.y, cv[1], part);
-        part = fmaf(s4.z, cv[2], part);
-        part = fmaf(s4.w, cv[3], part);
-        for (int off = 1; off < n4; off <<= 1)
-            part = part + __shfl_xor(part, off, 64);
-        if (q == 0) {
-            float yv = fmaf(D_h, xv, part);
-            y[p] = IO::cvt(yv + 0.0f);
+        float4 s4 = ST::load(st, f);
+        const float part = ssu_group(s4, alpha, dl * xv, bv, cv);
+        ST::store(st, f, s4);
+        const float yv = ssu_row_out(part, n4, D_h, xv);
+        if (q == 0)
+            y[p] = IO::cvt(yv);
+    }
+}
+
+// Multi-token recurrent update over a varlen pack (packed-history recovery:
+// vLLM RFC "Mamba2: exact-replay decode ...", section 3b, replays generated
+// history with a multi-token update that rounds the state to the cache
+// dtype after every token). One workgroup per (sequence, head); the state
+// stays in registers across the sequence's tokens, rounded to the cache
+// dtype after each one exactly as a store and reload would, so the result
+// is bit-identical to one k_ssu launch per token. Outputs for every token.
+constexpr int kSsuMaxGroups = 128 * 128 / 4 / kBlock;   // float4 groups per thread
+
+template <class IO, class DT, class ST>
+__global__ __launch_bounds__(kBlock) void k_ssu_varlen(SsuArgs a) {
+    using T = typename IO::T;
+    using TD = typename DT::T;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, P = d.P, N = d.N;
+    const int s = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x;
+    const int g = h / (H / G);
+    const int slot = a.slot_idx ? a.slot_idx[s] : s;
+    const int64_t t0 = a.cu[s];
+    const int len = a.cu[s + 1] - a.cu[s];
+    if (slot < 0 || slot >= a.num_slots || len == 0)
+        return;
+    const int n4 = N / 4;
+    const int q = tid % n4;
+    const int nf = P * n4;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float A_h = a.A[h];
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    typename ST::T *st = static_cast<typename ST::T *>(a.state) + ((int64_t)slot * H + h) * P * N;
+    float4 sr[kSsuMaxGroups];
+#pragma unroll
+    for (int i = 0; i < kSsuMaxGroups; ++i)
+        if (tid + kBlock * i < nf)
+            sr[i] = ST::load(st, tid + kBlock * i);
+    const T *xs = static_cast<const T *>(a.x);
+    T *ys = static_cast<T *>(a.y);
+    for (int t = 0; t < len; ++t) {
+        const int64_t tok = t0 + t;
+        const float dl = delta_of(DT::ld(static_cast<const TD *>(a.dt), tok * H + h), bias,
+                                  d.softplus);
+        const float alpha = decay_exp(dl * A_h);
+        const T *Bt = static_cast<const T *>(a.B) + (tok * G + g) * N + 4 * q;
+        const T *Ct = static_cast<const T *>(a.C) + (tok * G + g) * N + 4 * q;
+        float bv[4], cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bv[i] = IO::ld(Bt, i);
+            cv[i] = IO::ld(Ct, i);
+        }
+        const T *xt = xs + (tok * H + h) * P;
+        T *y = ys + (tok * H + h) * P;
+#pragma unroll
+        for (int i = 0; i < kSsuMaxGroups; ++i) {
+            const int f = tid + kBlock * i;
+            if (f < nf) {   // uniform over the n4 lanes of a row
+                const int p = f / n4;
+                const float xv = IO::ld(xt, p);
+                const float part = ssu_group(sr[i], alpha, dl * xv, bv, cv);
+                sr[i] = ST::round(sr[i]);
+                const float yv = ssu_row_out(part, n4, D_h, xv);
+                if (q == 0)
+                    y[p] = IO::cvt(yv);
+            }
         }
     }
+#pragma unroll
+    for (int i = 0; i < kSsuMaxGroups; ++i)
+        if (tid + kBlock * i < nf)
+            ST::store(st, tid + kBlock * i, sr[i]);
 }
 
 template <class K>
@@ -639,7 +756,19 @@ hipError_t commit_impl(const CommitArgs &a, hipStream_t stream) {
 
 template <class IO, class DT>
 hipError_t ssu_impl(const SsuArgs &a, hipStream_t stream) {
-    k_ssu<IO, DT><<<dim3(a.d.H * a.batch), dim3(kBlock), 0, stream>>>(a);
+    // batch rows (one token each), or sequences of a varlen pack (cu given)
+    const dim3 grid(a.d.H * a.batch), block(kBlock);
+    if (a.cu) {
+        if (a.state_bf16)
+            k_ssu_varlen<IO, DT, StBF16><<<grid, block, 0, stream>>>(a);
+        else
+            k_ssu_varlen<IO, DT, StF32><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (a.state_bf16)
+            k_ssu<IO, DT, StBF16><<<grid, block, 0, stream>>>(a);
+        else
+            k_ssu<IO, DT, StF32><<<grid, block, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -66,7 +66,8 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* Problem shape shared by all calls.
  * Supported: chunk_size in {16,32,64,128,256}; P and N in {16,32,64,128};
  * H % G == 0; io_dtype (x, B, C, y) and dt_dtype in {SSD_F32, SSD_BF16};
- * state_dtype must be SSD_F32. */
+ * state_dtype must be SSD_F32, except that the recurrent update
+ * (ssm_state_update, ssm_state_update_varlen) also takes SSD_BF16. */
 typedef struct {
     int32_t H, G, P, N, chunk_size;
     int32_t io_dtype;
@@ -273,15 +274,34 @@ int ssd_replay_accept(const ssd_shape *shape, const ssd_replay_cache *cache,
 /* Recurrent selective-state update, the conventional decode path the RFC
  * compares against ([RFC] section 1; [RSSM] "Motivation and method": it
  * reads and writes the full state every token). For slot = slot_idx[b]
- * (NULL = b): state[slot] <- exp(delta A) state[slot] + delta x (outer) B;
- * y[b] <- state[slot] . C + D x. state is [num_slots,H,P,N] fp32, updated in
- * place; x[batch,H,P], dt[batch,H], B/C[batch,G,N], y[batch,H,P].
- * Slots must be distinct. */
+ * (NULL = b): h = exp(delta A) state[slot] + delta x (outer) B in fp32;
+ * y[b] <- h . C + D x; state[slot] <- h stored in the cache dtype.
+ * shape->state_dtype selects that dtype: SSD_F32, or SSD_BF16 (rounded to
+ * nearest even; the RFC's default cache). state is [num_slots,H,P,N],
+ * updated in place; x[batch,H,P], dt[batch,H], B/C[batch,G,N],
+ * y[batch,H,P]. Slots must be distinct. */
 int ssm_state_update(const ssd_shape *shape, int32_t batch, int32_t num_slots,
-                     const int32_t *slot_idx, float *state, const void *x,
+                     const int32_t *slot_idx, void *state, const void *x,
                      const void *dt, const float *A, const void *B,
                      const void *C, const float *D, const float *dt_bias,
                      void *y, hipStream_t stream);
+
+/* Multi-token recurrent update over a varlen pack, for packed-history
+ * recovery ([RFC] section 3b: generated history is replayed with a
+ * multi-token recurrent update that rounds the state to the cache dtype
+ * after every token, so the recovered state continues exactly like an
+ * uninterrupted decode). Sequence s (tokens cu[s]..cu[s+1]-1) advances
+ * state[slot_idx[s]] (NULL = s) token by token with the arithmetic and the
+ * per-token rounding of ssm_state_update, so the outputs y[T,H,P] and the
+ * final state are bit-identical to one ssm_state_update call per token. The
+ * state stays on chip between tokens. Slots must be distinct. */
+int ssm_state_update_varlen(const ssd_shape *shape, int32_t num_seqs,
+                            int64_t total_tokens, const int32_t *cu_seqlens_host,
+                            const int32_t *cu_seqlens, const int32_t *slot_idx,
+                            int32_t num_slots, void *state, const void *x,
+                            const void *dt, const float *A, const void *B,
+                            const void *C, const float *D, const float *dt_bias,
+                            void *y, hipStream_t stream);
 
 /* Causal depthwise conv1d, the step before the scan ([RFC] section 2, item
  * 6: its prefill form and its decode form give the same bits; bf16 operands

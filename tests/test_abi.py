@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
             "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
-            "ssd_replay_verify", "ssd_replay_accept"}
+            "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -148,7 +148,8 @@ def test_replay_fails_closed():
     assert lib.ssd_commit_boundary(ctypes.byref(sh), 1, 8, cu.ctypes.data_as(ctypes.c_void_p),
                                    FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
                                    ctypes.byref(cache(sh)), None) == -1
-    assert lib.ssm_state_update(ctypes.byref(shape(state_dtype=1)), 1, 1, None, FAKE, FAKE,
+    # the recurrent update takes fp32 or bf16 state; any other code fails closed
+    assert lib.ssm_state_update(ctypes.byref(shape(state_dtype=2)), 1, 1, None, FAKE, FAKE,
                                 FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == -4
     assert lib.ssm_state_update(ctypes.byref(sh), 3, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, None, None, FAKE, None) == -2
@@ -172,6 +173,20 @@ def test_speculative_entry_points_fail_closed():
     assert accept(cache(sh), acc=None) == -1
     assert accept(cache(sh, buf_C=0x1000)) == -1             # C buffered: C needed
     assert accept(cache(sh, chunk_size=64)) == -5
+
+
+def test_varlen_ssu_checks():
+    lib = _lib.load()
+    cu = np.asarray([0, 4, 9], dtype=np.int32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    call = lambda sh, **k: lib.ssm_state_update_varlen(  # noqa: E731
+        ctypes.byref(sh), 2, 9, cup, FAKE, None, k.get("ns", 2), k.get("state", FAKE), FAKE,
+        FAKE, FAKE, FAKE, FAKE, None, None, k.get("y", FAKE), None)
+    assert call(shape(state_dtype=2)) == -4
+    assert call(shape(), ns=1) == -2                        # more sequences than slots
+    assert call(shape(), state=None) == -1
+    assert call(shape(), y=None) == -1
+    assert call(shape(), state=ctypes.c_void_p(0x1004)) == -9
 
 
 def test_paged_cache_checks():
