@@ -38,10 +38,12 @@ METRIC = "SSD prefill tokens/s + replay-decode steps/s at B=256; % HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 PAGE_TOKENS = 64             # rows per buffer page in the paged replay-decode leg
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
                   "ssd_internal.hpp", "ssd_conv.hip"]
 CONV_W = 4                   # conv kernel width of the conv legs
 SPEC_BATCH, SPEC_T = 512, 4  # speculative verification: sequences, drafts each
+RECOVER_T = 255              # packed-history recovery: generated tokens replayed
 
 
 def kernel_source_sha() -> str:
@@ -119,6 +121,13 @@ def accept_step_bytes(ks, acc, Q, H, G, P, N, io=2, dtb=2):
     fills = (ks + acc) >= Q
     commit = H * P * N * (4 + 4 + 2) + Q * per_tok
     return int(2 * acc.sum() * per_tok + fills.sum() * commit)
+
+
+def recovery_bytes(S, T, H, G, P, N, io=2, dtb=2, sb=4):
+    """Packed-history recovery of T tokens for S sequences: each state read
+    and written once (cache dtype, sb bytes), every token's x, dt, B, C read
+    and y written."""
+    return S * 2 * H * P * N * sb + S * T * (2 * H * P * io + H * dtb + 2 * G * N * io)
 
 
 def ssu_step_bytes(batch, H, G, P, N, io=2, dtb=2):
@@ -344,6 +353,14 @@ def main():
     accs = arng.integers(0, ST + 1, size=(total_decode, SB)).astype(np.int32)
     accs_dev = torch.from_numpy(accs).to(dev)
     sks = (spre % Q).astype(np.int64)
+
+    # packed-history recovery: RECOVER_T generated tokens of each of the S
+    # sequences replayed with one multi-token recurrent update (fp32 cache)
+    rx, rdt, rB, rC = synth.make_tokens_torch(S * RECOVER_T, H, G, P, N, 6, dev)
+    rcu_host = synth.cu_seqlens([RECOVER_T] * S)
+    rcu = torch.from_numpy(rcu_host).to(dev)
+    rstate = torch.zeros((S, H, P, N), dtype=torch.float32, device=dev)
+    ry = torch.empty_like(rx)
     ks256 = (pre % Q).astype(np.int64)
     ks16 = (pre % 16).astype(np.int64)
     kspg = ks256.copy()
@@ -359,8 +376,9 @@ def main():
         nonlocal decode_i, bytes_decode256, bytes_decode16, bytes_decodepg, ks256, ks16, kspg
         nonlocal sks, bytes_verify, bytes_accept
         # events 0..8 bracket the legs; 9.. follow every verification and
-        # every acceptance of the speculative leg
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(9 + 2 * R)] if record else None
+        # every acceptance of the speculative leg; the last one follows the
+        # recovery
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(10 + 2 * R)] if record else None
         if record:
             ev[0].record(stream)
         erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias, y=y, boundary_state=bnd,
@@ -423,6 +441,10 @@ def main():
                 bytes_accept += accept_step_bytes(sks, accs[k], Q, H, G, P, N)
                 ev[10 + 2 * r].record(stream)
             sks = (sks + accs[k]) % Q
+        erd.ssm_state_update_varlen(shape, rstate, rcu, rx, rdt, rB, rC, A, D, bias, y=ry,
+                                    cu_seqlens_host=rcu_host)
+        if record:
+            ev[9 + 2 * R].record(stream)
         decode_i += R
         return ev
 
@@ -448,7 +470,8 @@ def main():
     t_convu = span(7, 8)
     t_verify = sum(span(8 if r == 0 else 8 + 2 * r, 9 + 2 * r) for r in range(R))
     t_accept = sum(span(9 + 2 * r, 10 + 2 * r) for r in range(R))
-    t_total = span(0, 8 + 2 * R)
+    t_recover = span(8 + 2 * R, 9 + 2 * R)
+    t_total = span(0, 9 + 2 * R)
 
     pb = prefill_bytes(S * T, S, H, G, P, N)
     pf = prefill_flops(S * T, H, G, P, N, Q)
@@ -463,6 +486,7 @@ def main():
     conv_gbs = conv_prefill_bytes(S * T, S, cd, CONV_W) * K / t_conv / 1e9
     verify_gbs = bytes_verify / t_verify / 1e9
     accept_gbs = bytes_accept / t_accept / 1e9
+    recover_gbs = recovery_bytes(S, RECOVER_T, H, G, P, N) * K / t_recover / 1e9
     convu_gbs = conv_update_bytes(S, cd, CONV_W) * dec_steps / t_convu / 1e9
     ssu_gbs = ssu_step_bytes(S, H, G, P, N) * dec_steps / t_ssu / 1e9
 
@@ -486,7 +510,8 @@ def main():
                         "B=256 (chunk 256 and 16, 0..255 buffered tokens; chunk 256 also "
                         "over paged buffers) + recurrent update B=256 + causal conv1d "
                         "(width 4 over x|B|C) prefill on the same pack and decode at B=256 + "
-                        "speculative verification of 4 drafts and acceptance at B=512",
+                        "speculative verification of 4 drafts and acceptance at B=512 + "
+                        "packed-history recovery of 255 tokens x 256 sequences",
             "global_batch": S, "seq_len": T, "heads": H, "groups": G, "headdim": P,
             "dstate": N, "chunk_size": Q, "decode_steps_per_step": R,
         },
@@ -533,6 +558,17 @@ def main():
             "accept_steps_per_s": dec_steps / t_accept,
             "accept_hbm_gbs": accept_gbs,
             "accept_frac": accept_gbs / HBM_PEAK_GBS,
+        },
+        "recovery": {
+            "sequences": S, "tokens": RECOVER_T, "state": "f32",
+            "ms": 1e3 * t_recover / K,
+            "tokens_per_s": S * RECOVER_T * K / t_recover,
+            "hbm_gbs": recover_gbs,
+            "frac": recover_gbs / HBM_PEAK_GBS,
+            # sequential in tokens: bound by fp32 vector arithmetic and its
+            # latency, 5 flops per state element and token
+            "alu_tflops": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12,
+            "alu_frac": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12 / FP32_VALU_PEAK_TFLOPS,
         },
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,

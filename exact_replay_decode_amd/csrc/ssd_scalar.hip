@@ -19,6 +19,8 @@
 //  * the decode kernel calls the very same device functions (emit_rows,
 //    chunk_state_update) with a chunk view whose first k positions read the
 //    slot buffer.
+#include <algorithm>
+
 #include "ssd_device.hpp"
 #include "ssd_internal.hpp"
 
@@ -542,67 +544,122 @@ __global__ __launch_bounds__(kBlock) void k_refresh_state_bf(const float *state,
     }
 }
 
-// State storage of the recurrent update: fp32, or bf16 (rounded to nearest
-// even on every store, the cache-dtype rounding of each token).
+// ---- recurrent update ------------------------------------------------------
+//
+// Layout: a state row spans L = N / 16 consecutive lanes; lane c of the row
+// owns the 16 columns 4(c + L k) + e (k, e < 4): four pieces of 4 columns,
+// so the row's lanes read consecutive pieces (coalesced). A workgroup
+// covers 256 / L rows per pass and a thread holds NR rows (a template
+// parameter). The row's output is the thread's 16 products in order, then a
+// lane tree over the L lanes. The one-token and the multi-token kernels
+// share this layout and every line of arithmetic (ssu_seg, ssu_row_out), so
+// their bits agree.
+
+// 4 consecutive values of an array of storage type IO.
+template <class IO>
+struct Piece4;
+template <>
+struct Piece4<IoBF16> {
+    uint2 u;
+    __device__ __forceinline__ void load(const uint16_t *p) { u = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ void get(float *f) const {
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xffff0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+};
+template <>
+struct Piece4<IoF32> {
+    uint4 u;
+    __device__ __forceinline__ void load(const float *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void get(float *f) const {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+    }
+};
+
+// A lane's 16 values of a row: pieces at element offsets 4 L k from p
+// (p = the row's column 4c).
+template <class IO>
+struct Seg16 {
+    Piece4<IO> pc[4];
+    __device__ __forceinline__ void load(const typename IO::T *p, int L) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pc[k].load(p + 4 * L * k);
+    }
+    __device__ __forceinline__ void get(float (&f)[16]) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pc[k].get(f + 4 * k);
+    }
+};
+
+// State storage: fp32, or bf16 (rounded to nearest even on every store,
+// the cache-dtype rounding of each token).
 struct StF32 {
     using T = float;
-    __device__ static __forceinline__ float4 load(const T *st, int f) {
-        return reinterpret_cast<const float4 *>(st)[f];
-    }
-    __device__ static __forceinline__ void store(T *st, int f, const float4 &v) {
-        reinterpret_cast<float4 *>(st)[f] = v;
+    using IO = IoF32;
+    __device__ static __forceinline__ void store16(T *p, int L, const float (&v)[16]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<float4 *>(p + 4 * L * k) =
+                make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
     }
     // the value the store keeps (fp32: the value itself)
-    __device__ static __forceinline__ float4 round(const float4 &v) { return v; }
+    __device__ static __forceinline__ float round(float v) { return v; }
 };
 
 struct StBF16 {
     using T = uint16_t;
-    __device__ static __forceinline__ float4 load(const T *st, int f) {
-        const uint2 u = reinterpret_cast<const uint2 *>(st)[f];
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    using IO = IoBF16;
+    __device__ static __forceinline__ void store16(T *p, int L, const float (&v)[16]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint2 *>(p + 4 * L * k) =
+                make_uint2(bf16_rne(v[4 * k]) | ((uint32_t)bf16_rne(v[4 * k + 1]) << 16),
+                           bf16_rne(v[4 * k + 2]) | ((uint32_t)bf16_rne(v[4 * k + 3]) << 16));
     }
-    __device__ static __forceinline__ void store(T *st, int f, const float4 &v) {
-        reinterpret_cast<uint2 *>(st)[f] =
-            make_uint2(bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
-                       bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
-    }
-    __device__ static __forceinline__ float4 round(const float4 &v) {
-        auto r = [](float a) { return __uint_as_float((uint32_t)bf16_rne(a) << 16); };
-        return make_float4(r(v.x), r(v.y), r(v.z), r(v.w));
+    __device__ static __forceinline__ float round(float v) {
+        return __uint_as_float((uint32_t)bf16_rne(v) << 16);
     }
 };
 
-// One token of the recurrent update on one float4 group of row p of the
-// [P, N] state (4 consecutive n): s = alpha s + (delta x_p) B_n, and this
-// group's share of y_p = sum_n s C_n. The one-token and the multi-token
-// kernels both use exactly this, so their bits agree.
-__device__ __forceinline__ float ssu_group(float4 &s4, float alpha, float dx, const float (&bv)[4],
-                                           const float (&cv)[4]) {
-    s4.x = fmaf(alpha, s4.x, dx * bv[0]);
-    s4.y = fmaf(alpha, s4.y, dx * bv[1]);
-    s4.z = fmaf(alpha, s4.z, dx * bv[2]);
-    s4.w = fmaf(alpha, s4.w, dx * bv[3]);
-    float part = s4.x * cv[0];
-    part = fmaf(s4.y, cv[1], part);
-    part = fmaf(s4.z, cv[2], part);
-    part = fmaf(s4.w, cv[3], part);
+// One token on one row segment: s = alpha s + (delta x_p) B_n, then the
+// segment's share of y_p = sum_n s C_n (products in column order).
+__device__ __forceinline__ float ssu_seg(float (&sv)[16], float alpha, float dx,
+                                         const float (&bv)[16], const float (&cv)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        sv[j] = fmaf(alpha, sv[j], dx * bv[j]);
+    float part = sv[0] * cv[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+        part = fmaf(sv[j], cv[j], part);
     return part;
 }
 
-// Row sum over the n4 lanes holding row p (butterfly), then y_p.
-__device__ __forceinline__ float ssu_row_out(float part, int n4, float D_h, float xv) {
-    for (int off = 1; off < n4; off <<= 1)
-        part = part + __shfl_xor(part, off, 64);
+// Row sum over the L = N/16 lanes of a row (L in {1, 2, 4, 8}, consecutive
+// and aligned), then y_p; complete in the row's last lane. A fixed DPP
+// tree, no LDS traffic: lane pairs 1 apart, 2 apart (quad permutes), then
+// the two quads of each 8-lane half row (half mirror). The lanes of a row
+// are active or inactive together.
+__device__ __forceinline__ float ssu_row_out(float part, int L, float D_h, float xv) {
+    if (L >= 2)
+        part = part + dpp_from<0xb1, 0xf>(part);      // quad_perm [1,0,3,2]
+    if (L >= 4)
+        part = part + dpp_from<0x4e, 0xf>(part);      // quad_perm [2,3,0,1]
+    if (L >= 8)
+        part = part + dpp_from<0x141, 0xf>(part);     // row_half_mirror
     return fmaf(D_h, xv, part) + 0.0f;   // -0 -> +0
 }
 
-// Recurrent update, one workgroup per (head, batch row). Thread t owns the
-// float4 groups f = t + 256 i of the [P, N] state (coalesced rows); row p's
-// output is a butterfly sum over the N/4 lanes that hold it. The state is
-// read, updated in fp32 and stored in its cache dtype.
-template <class IO, class DT, class ST>
+// Recurrent update, one workgroup per (head, batch row): the state is read,
+// updated in fp32 and stored in its cache dtype.
+template <class IO, class DT, class ST, int NR>
 __global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
     using T = typename IO::T;
     using TD = typename DT::T;
@@ -613,34 +670,37 @@ __global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0 || slot >= a.num_slots)
         return;
-    const int n4 = N / 4;
-    const int q = tid % n4;
+    const int L = N / 16, c = tid % L, rr = tid / L, RP = kBlock / L;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float dl = delta_of(DT::ld(static_cast<const TD *>(a.dt), (int64_t)b * H + h), bias,
                               d.softplus);
     const float alpha = decay_exp(dl * a.A[h]);
     const float D_h = a.D ? a.D[h] : 0.0f;
-    const T *Bt = static_cast<const T *>(a.B) + ((int64_t)b * G + g) * N + 4 * q;
-    const T *Ct = static_cast<const T *>(a.C) + ((int64_t)b * G + g) * N + 4 * q;
-    float bv[4], cv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bv[i] = IO::ld(Bt, i);
-        cv[i] = IO::ld(Ct, i);
-    }
+    Seg16<IO> bs, cs;
+    bs.load(static_cast<const T *>(a.B) + ((int64_t)b * G + g) * N + 4 * c, L);
+    cs.load(static_cast<const T *>(a.C) + ((int64_t)b * G + g) * N + 4 * c, L);
+    float bv[16], cv[16];
+    bs.get(bv);
+    cs.get(cv);
     const T *xt = static_cast<const T *>(a.x) + ((int64_t)b * H + h) * P;
     typename ST::T *st = static_cast<typename ST::T *>(a.state) + ((int64_t)slot * H + h) * P * N;
     T *y = static_cast<T *>(a.y) + ((int64_t)b * H + h) * P;
-    const int nf = P * n4;
-    for (int f = tid; f < nf; f += kBlock) {
-        const int p = f / n4;
-        const float xv = IO::ld(xt, p);
-        float4 s4 = ST::load(st, f);
-        const float part = ssu_group(s4, alpha, dl * xv, bv, cv);
-        ST::store(st, f, s4);
-        const float yv = ssu_row_out(part, n4, D_h, xv);
-        if (q == 0)
-            y[p] = IO::cvt(yv);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int p = rr + RP * i;
+        if (p < P) {   // uniform over the L lanes of a row
+            typename ST::T *row = st + (int64_t)p * N + 4 * c;
+            Seg16<typename ST::IO> ss;
+            ss.load(row, L);
+            float sv[16];
+            ss.get(sv);
+            const float xv = IO::ld(xt, p);
+            const float part = ssu_seg(sv, alpha, dl * xv, bv, cv);
+            ST::store16(row, L, sv);
+            const float yv = ssu_row_out(part, L, D_h, xv);
+            if (c == L - 1)
+                y[p] = IO::cvt(yv);
+        }
     }
 }
 
@@ -651,9 +711,7 @@ __global__ __launch_bounds__(kBlock) void k_ssu(SsuArgs a) {
 // stays in registers across the sequence's tokens, rounded to the cache
 // dtype after each one exactly as a store and reload would, so the result
 // is bit-identical to one k_ssu launch per token. Outputs for every token.
-constexpr int kSsuMaxGroups = 128 * 128 / 4 / kBlock;   // float4 groups per thread
-
-template <class IO, class DT, class ST>
+template <class IO, class DT, class ST, int NR>
 __global__ __launch_bounds__(kBlock) void k_ssu_varlen(SsuArgs a) {
     using T = typename IO::T;
     using TD = typename DT::T;
@@ -666,53 +724,102 @@ __global__ __launch_bounds__(kBlock) void k_ssu_varlen(SsuArgs a) {
     const int len = a.cu[s + 1] - a.cu[s];
     if (slot < 0 || slot >= a.num_slots || len == 0)
         return;
-    const int n4 = N / 4;
-    const int q = tid % n4;
-    const int nf = P * n4;
+    const int L = N / 16, c = tid % L, rr = tid / L, RP = kBlock / L;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float A_h = a.A[h];
     const float D_h = a.D ? a.D[h] : 0.0f;
     typename ST::T *st = static_cast<typename ST::T *>(a.state) + ((int64_t)slot * H + h) * P * N;
-    float4 sr[kSsuMaxGroups];
+    float sr[NR][16];
 #pragma unroll
-    for (int i = 0; i < kSsuMaxGroups; ++i)
-        if (tid + kBlock * i < nf)
-            sr[i] = ST::load(st, tid + kBlock * i);
+    for (int i = 0; i < NR; ++i) {
+        const int p = min(rr + RP * i, P - 1);   // rows past P are never stored
+        Seg16<typename ST::IO> ss;
+        ss.load(st + (int64_t)p * N + 4 * c, L);
+        ss.get(sr[i]);
+    }
     const T *xs = static_cast<const T *>(a.x);
+    const TD *dts = static_cast<const TD *>(a.dt);
+    const T *Bs = static_cast<const T *>(a.B);
+    const T *Cs = static_cast<const T *>(a.C);
     T *ys = static_cast<T *>(a.y);
+    // one token's inputs as stored (converted where used), loaded one token
+    // ahead so that their latency overlaps the current token's arithmetic
+    struct TokIn {
+        TD dt;
+        Seg16<IO> b, c;
+        T x[NR];
+    };
+    auto load_tok = [&](int64_t tok, TokIn &in) {
+        in.dt = dts[tok * H + h];
+        in.b.load(Bs + (tok * G + g) * N + 4 * c, L);
+        in.c.load(Cs + (tok * G + g) * N + 4 * c, L);
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            in.x[i] = xs[(tok * H + h) * P + min(rr + RP * i, P - 1)];
+    };
+    // delta and the decay of the next token are computed at the end of the
+    // current one (they do not depend on the state)
+    TokIn nxt;
+    load_tok(t0, nxt);
+    float dl_n = delta_of(DT::val(nxt.dt), bias, d.softplus);
+    float alpha_n = decay_exp(dl_n * A_h);
     for (int t = 0; t < len; ++t) {
         const int64_t tok = t0 + t;
-        const float dl = delta_of(DT::ld(static_cast<const TD *>(a.dt), tok * H + h), bias,
-                                  d.softplus);
-        const float alpha = decay_exp(dl * A_h);
-        const T *Bt = static_cast<const T *>(a.B) + (tok * G + g) * N + 4 * q;
-        const T *Ct = static_cast<const T *>(a.C) + (tok * G + g) * N + 4 * q;
-        float bv[4], cv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bv[i] = IO::ld(Bt, i);
-            cv[i] = IO::ld(Ct, i);
-        }
-        const T *xt = xs + (tok * H + h) * P;
+        const TokIn cur = nxt;
+        const float dl = dl_n, alpha = alpha_n;
+        if (t + 1 < len)
+            load_tok(tok + 1, nxt);
+        float bv[16], cv[16];
+        cur.b.get(bv);
+        cur.c.get(cv);
         T *y = ys + (tok * H + h) * P;
 #pragma unroll
-        for (int i = 0; i < kSsuMaxGroups; ++i) {
-            const int f = tid + kBlock * i;
-            if (f < nf) {   // uniform over the n4 lanes of a row
-                const int p = f / n4;
-                const float xv = IO::ld(xt, p);
-                const float part = ssu_group(sr[i], alpha, dl * xv, bv, cv);
-                sr[i] = ST::round(sr[i]);
-                const float yv = ssu_row_out(part, n4, D_h, xv);
-                if (q == 0)
+        for (int i = 0; i < NR; ++i) {
+            const int p = rr + RP * i;
+            if (p < P) {   // uniform over the L lanes of a row
+                const float xv = IO::val(cur.x[i]);
+                const float part = ssu_seg(sr[i], alpha, dl * xv, bv, cv);
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    sr[i][j] = ST::round(sr[i][j]);
+                const float yv = ssu_row_out(part, L, D_h, xv);
+                if (c == L - 1)
                     y[p] = IO::cvt(yv);
             }
         }
+        if (t + 1 < len) {
+            dl_n = delta_of(DT::val(nxt.dt), bias, d.softplus);
+            alpha_n = decay_exp(dl_n * A_h);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < kSsuMaxGroups; ++i)
-        if (tid + kBlock * i < nf)
-            ST::store(st, tid + kBlock * i, sr[i]);
+    for (int i = 0; i < NR; ++i) {
+        const int p = rr + RP * i;
+        if (p < P)
+            ST::store16(st + (int64_t)p * N + 4 * c, L, sr[i]);
+    }
+}
+
+// Rows per thread: P * (N/16) / 256, at least 1 (at most 8: P, N <= 128).
+template <class IO, class DT, class ST>
+void launch_ssu_kernels(const SsuArgs &a, hipStream_t stream) {
+    const dim3 grid(a.d.H * a.batch), block(kBlock);
+    const int nr = std::max(1, a.d.P * (a.d.N / 16) / kBlock);
+#define SSU_CASE(R)                                                   \
+    case R:                                                           \
+        if (a.cu)                                                     \
+            k_ssu_varlen<IO, DT, ST, R><<<grid, block, 0, stream>>>(a); \
+        else                                                          \
+            k_ssu<IO, DT, ST, R><<<grid, block, 0, stream>>>(a);        \
+        break;
+    switch (nr) {
+        SSU_CASE(1)
+        SSU_CASE(2)
+        SSU_CASE(4)
+    default:
+        SSU_CASE(8)
+    }
+#undef SSU_CASE
 }
 
 template <class K>
@@ -757,18 +864,10 @@ hipError_t commit_impl(const CommitArgs &a, hipStream_t stream) {
 template <class IO, class DT>
 hipError_t ssu_impl(const SsuArgs &a, hipStream_t stream) {
     // batch rows (one token each), or sequences of a varlen pack (cu given)
-    const dim3 grid(a.d.H * a.batch), block(kBlock);
-    if (a.cu) {
-        if (a.state_bf16)
-            k_ssu_varlen<IO, DT, StBF16><<<grid, block, 0, stream>>>(a);
-        else
-            k_ssu_varlen<IO, DT, StF32><<<grid, block, 0, stream>>>(a);
-    } else {
-        if (a.state_bf16)
-            k_ssu<IO, DT, StBF16><<<grid, block, 0, stream>>>(a);
-        else
-            k_ssu<IO, DT, StF32><<<grid, block, 0, stream>>>(a);
-    }
+    if (a.state_bf16)
+        launch_ssu_kernels<IO, DT, StBF16>(a, stream);
+    else
+        launch_ssu_kernels<IO, DT, StF32>(a, stream);
     return hipGetLastError();
 }
 
