@@ -171,11 +171,12 @@ int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, i
     a.dry = mode == 1;
     a.no_y = mode == 2;
     a.take = mode == 2 ? take : nullptr;
+    if (mode == 1)   // verification writes only y
+        return hip_status(ssd::mfma_supported(d) ? ssd::launch_verify_mfma(a, (hipStream_t)stream)
+                                                 : ssd::launch_scan(a, (hipStream_t)stream));
     hipError_t e = launch_scan_any(a, (hipStream_t)stream);
     if (e != hipSuccess)
         return SSD_ERR_HIP;
-    if (mode == 1)
-        return SSD_OK;
     ssd::CommitArgs c = {};
     c.d = d;
     c.S = S;

@@ -52,6 +52,7 @@ struct ScanArgs {
     // s's token count
     int32_t dry, no_y;
     const int32_t *take;
+    int32_t only_cross;       // dry replay of the sequences whose drafts cross the chunk end
 };
 
 // Write the trailing partial chunk of each sequence into the slot buffers
@@ -132,6 +133,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 bool mfma_supported(const Dims &d);
 hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_verify_mfma(const ScanArgs &a, hipStream_t stream);   // dry replay of drafts
 // causal conv1d (ssd_conv.hip)
 hipError_t launch_conv_fwd(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv_update(const ConvArgs &a, hipStream_t stream);

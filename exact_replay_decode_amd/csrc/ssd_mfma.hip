@@ -715,15 +715,12 @@ __device__ __forceinline__ int wave_tblock(int nT, int wave) {
 }
 
 template <int P, int N, class DT, bool PG>
-__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *lds) {
     using TD = typename DT::T;
     constexpr int NW = kPrefillWaves;
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
-    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
-    const int s = wid / H, h = wid % H;
     const int g = h / (H / G);
     const int wave = threadIdx.x >> 6;
     constexpr int PN = P * N;
@@ -738,8 +735,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     if (nbuf < 0 || nbuf >= Q)
         return;
     // acceptance without a chunk that fills has no work here (the buffer
-    // append is the commit kernel's)
-    if (a.no_y && nbuf + len < Q)
+    // append is the commit kernel's); with only_cross, verification handles
+    // just the sequences whose drafts run past the chunk end
+    if ((a.no_y && nbuf + len < Q) || (a.only_cross && nbuf + len <= Q))
         return;
     const SlotRows<PG> rows(a.bm, slot, Q);
     if (!rows.ok(a.bm, a.dry ? nbuf : replay_npos(nbuf, len, Q)))
@@ -840,6 +838,55 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     }
     if (!a.replay && a.final_state)
         state_io<P, N, NW, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
+}
+
+// One workgroup per (sequence, head).
+template <int P, int N, class DT, bool PG>
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
+    scan_one<P, N, DT, PG>(a, wid / a.d.H, wid % a.d.H, lds);
+}
+
+// Verification of drafts that run past the chunk end (dry replay, only_cross
+// set): one round of workgroups; each tests the (sequence, head) pairs
+// e = blockIdx.x + gridDim.x i in parallel, lists the crossing ones in LDS
+// and replays those (few) pairs one after another. The pairs with nothing
+// to do cost no dispatch of a large-LDS workgroup, and a sequence's heads
+// land on different workgroups.
+template <int P, int N, class DT, bool PG>
+__global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int H = a.d.H, Q = a.d.Q;
+    const MLayout L(Q < 32 ? 32 : Q, P, N);
+    int *list = reinterpret_cast<int *>(lds + L.bytes);   // [1 + 64 * kPrefillWaves]
+    const int total = a.S * H;
+    const int rounds = (total + gridDim.x - 1) / gridDim.x;   // candidates per workgroup
+    for (int base = 0; base < rounds; base += 64 * kPrefillWaves) {
+        if (threadIdx.x == 0)
+            list[0] = 0;
+        __syncthreads();
+        const int i = base + threadIdx.x;
+        const int e = blockIdx.x + gridDim.x * i;
+        if (i < rounds && e < total) {
+            const int s = e / H;
+            const int slot = a.slot_idx ? a.slot_idx[s] : s;
+            const int len = a.cu[s + 1] - a.cu[s];
+            if (len > 0 && slot >= 0 && slot < a.num_slots) {
+                const int k = a.buf_len[slot];
+                if (k >= 0 && k < Q && k + len > Q)
+                    list[1 + atomicAdd(list, 1)] = e;
+            }
+        }
+        __syncthreads();
+        const int n = list[0];
+        for (int j = 0; j < n; ++j) {
+            const int ej = list[1 + j];
+            __syncthreads();   // the previous pair's LDS use is over
+            scan_one<P, N, DT, PG>(a, ej / H, ej % H, lds);
+        }
+        __syncthreads();   // list reads are done before the next round resets it
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1317,6 +1364,228 @@ __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Speculative verification, many rows at once. A workgroup of kDecodeWaves
+// waves serves that many heads of one sequence, one wave per head (no
+// barriers: each wave has its own LDS). The wave computes the outputs of
+// the sequence's T draft rows k .. k+T-1 of the chunk (k = buf_len), t-block
+// by t-block, with the prefill's operands and MFMA order: the read-out from
+// the cache's bf16 state copy, the same in-chunk scan (one wave emulating
+// the block scan), C.B^T blocks, decay weights and X.M accumulation. An
+// output row depends only on its own columns of C and M, so each draft's
+// output has the bits decode would give it. Operands come from global
+// memory: committed rows from the slot buffer, drafts from the inputs, rows
+// after the last draft are zero. Nothing but y is written. Sequences whose
+// drafts run past the chunk end are left to the prefill kernel's dry replay.
+struct VLayout {
+    int XS;
+    int lam, u, beta, X, bytes;
+    __host__ __device__ VLayout(int Qp, int P) {
+        XS = P + kPad;
+        int o = 0;
+        lam = o;  o += Qp * 4;
+        u = o;    o += Qp * 4;
+        beta = o; o += Qp * 4;
+        X = o;    o += 32 * XS * 2;
+        bytes = (o + 15) & ~15;
+    }
+};
+
+template <int P, int N, class DT, bool PG>
+__global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char lds_all[];
+    using TD = typename DT::T;
+    constexpr int NPT = P / 32, NK = N / 16;
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int HQ = (H + kDecodeWaves - 1) / kDecodeWaves;
+    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
+    const int sq = wid / HQ;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = (wid % HQ) * kDecodeWaves + wave;
+    const VLayout L(Qp, P);
+    char *lds = lds_all + wave * L.bytes;
+    const int64_t t0 = a.cu[sq];
+    const int T = a.cu[sq + 1] - a.cu[sq];
+    const int slot = a.slot_idx ? a.slot_idx[sq] : sq;
+    if (T <= 0 || h >= H || slot < 0 || slot >= a.num_slots)
+        return;
+    const int k = a.buf_len[slot];
+    if (k < 0 || k >= Q || k + T > Q)
+        return;
+    const SlotRows<PG> rows(a.bm, slot, Q);
+    if (!rows.ok(a.bm, k))
+        return;
+    const int g = h / (H / G);
+    const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
+    const int last = k + T - 1;
+    const int tau0 = k >> 5, tau1 = last >> 5;
+    const int64_t PN = (int64_t)P * N;
+    const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pools
+    const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
+    const TD *bdt = static_cast<const TD *>(a.buf_dt);
+    const uint16_t *xin = static_cast<const uint16_t *>(a.x);
+    const uint16_t *Bin = static_cast<const uint16_t *>(a.B);
+    const uint16_t *Cin = static_cast<const uint16_t *>(a.C);
+    const TD *din = static_cast<const TD *>(a.dt);
+    // draft index of chunk row j (clamped: rows outside the drafts load a
+    // draft row whose value is never used)
+    auto dj = [&](int j) { return t0 + min(max(j - k, 0), T - 1); };
+
+    const float A2 = a.A[h] * kLog2e;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    TD rawdt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const int64_t br = rows(j);
+        rawdt[i] = j < k ? bdt[br * H + h] : din[dj(j) * H + h];
+    }
+    const uint16_t *sbf = static_cast<const uint16_t *>(a.cache_state_bf) +
+                          ((int64_t)slot * H + h) * PN;
+
+    // delta and the in-chunk cumulative sum (log2 units) over rows 0..last
+    const int nseg = (32 * (tau1 + 1) + 63) >> 6;
+    float dv[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        float dd = 0.0f, aa = 0.0f;
+        if (i < nseg && j <= last) {
+            dd = delta_of(DT::val(rawdt[i]), bias, d.softplus);
+            aa = dd * A2;
+        }
+        dv[i] = dd;
+        lv[i] = aa;
+    }
+    wave_scan_segments(lv, nseg);
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *bt = reinterpret_cast<float *>(lds + L.beta);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const float lend = __shfl(lv[i], lane | 31, 64);   // lam[j | 31]
+        if (i < nseg && j < Qp) {
+            const float l = lv[i];
+            const float u = l - flog2(dv[i]);  // +inf where delta is 0
+            lam[j] = l;
+            uu[j] = u;
+            bt[j] = fexp2(lend - u);
+        }
+    }
+
+    for (int tau = tau0; tau <= tau1; ++tau) {
+        const int t = 32 * tau + c;                    // this lane's output row
+        const bool outc = t >= k && t <= last;
+        bf16x8 cf[NK];
+        {
+            const uint16_t *crow = Cin + (dj(t) * G + g) * N;
+            uint4 raw[NK];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+                raw[kk] = *reinterpret_cast<const uint4 *>(crow + 16 * kk + 8 * gl);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+                cf[kk] = __builtin_bit_cast(bf16x8, keep_if(outc, raw[kk]));
+        }
+        const float lam_t = lam[t];
+        // read-out from the bf16 state copy (operand (pt, kk) is 1 KiB
+        // contiguous)
+        f32x16 acc[NPT];
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+            acc[pt] = readout_scale(
+                readout_raw<N>(
+                    [&](int kk) {
+                        return *reinterpret_cast<const bf16x8 *>(
+                            sbf + ((int64_t)kk * P + 32 * pt + c) * 16 + 8 * gl);
+                    },
+                    cf),
+                fexp2(lam_t));
+        // B rows and x rows of s-block sg (committed rows from the buffer,
+        // drafts from the inputs), one block ahead of their use
+        constexpr int XPL = P / 16;
+        auto load_blk = [&](int sg, uint4 (&braw)[NK], uint4 (&xr)[XPL]) {
+            const int srow = 32 * sg + c;
+            const int64_t rs = rows(srow);
+            const uint16_t *brow =
+                srow < k ? bB + (rs * G + g) * N : Bin + (dj(srow) * G + g) * N;
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+                braw[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
+#pragma unroll
+            for (int i = 0; i < XPL; ++i) {
+                const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+                const int row = 32 * sg + r;
+                const int64_t br = rows(row);
+                const uint16_t *src =
+                    row < k ? bx + (br * H + h) * P : xin + (dj(row) * H + h) * P;
+                xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+            }
+        };
+        uint4 nb_[NK], nx_[XPL];
+        load_blk(0, nb_, nx_);
+        for (int sg = 0; sg <= tau; ++sg) {
+            uint4 braw[NK], xr[XPL];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+                braw[kk] = nb_[kk];
+#pragma unroll
+            for (int i = 0; i < XPL; ++i)
+                xr[i] = nx_[i];
+            if (sg < tau)
+                load_blk(sg + 1, nb_, nx_);
+            const int srow = 32 * sg + c;
+            const bool sok = srow <= last;
+            const f32x16 gt = gram_block<N>(
+                [&](int kk) { return __builtin_bit_cast(bf16x8, keep_if(sok, braw[kk])); }, cf);
+            uint32_t mb[8];
+            if (sg == tau)
+                m_diag(gt, lam_t, uu, 32 * sg, t, mb);
+            else
+                m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                mb[q] = outc ? mb[q] : 0u;
+#pragma unroll
+            for (int i = 0; i < XPL; ++i) {
+                const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
+                *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
+                    keep_if(32 * sg + r <= last, xr[i]);
+            }
+            mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc);
+        }
+        // y for the draft rows of this t-block: fmaf(D, x, Y^T) -> bf16,
+        // -0 -> +0; x_t is row t - 32 tau of the last x tile
+        if (outc) {
+            uint16_t *yrow = static_cast<uint16_t *>(a.y) + (dj(t) * H + h) * P;
+            const char *xt = lds + L.X + c * L.XS * 2;
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = 32 * pt + 8 * q + 4 * gl;
+                    const uint2 xv = *reinterpret_cast<const uint2 *>(xt + 2 * p);
+                    const float xs[4] = {bf16_float(xv.x & 0xffff), bf16_float(xv.x >> 16),
+                                         bf16_float(xv.y & 0xffff), bf16_float(xv.y >> 16)};
+                    uint16_t o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float yv = fmaf(D_h, xs[e], acc[pt][4 * q + e]);
+                        yv = yv + 0.0f;
+                        o[e] = bf16_bits(yv);
+                    }
+                    *reinterpret_cast<uint2 *>(yrow + p) =
+                        make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+                }
+            }
+        }
+    }
+}
+
 template <class K>
 hipError_t set_lds(K kernel, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -1327,8 +1596,22 @@ template <int P, int N, class DT, bool PG>
 hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
     const MLayout L(Qp, P, N);
-    hipError_t e = set_lds(k_scan_mfma<P, N, DT, PG>, L.bytes);
-    if (e != hipSuccess)
+    hipError_t e;
+    if (a.only_cross) {
+        // the crossing-draft sweep adds its pair list after the layout
+        const size_t bytes = L.bytes + 4 * (1 + 64 * kPrefillWaves);
+        if ((e = set_lds(k_scan_cross<P, N, DT, PG>, bytes)) != hipSuccess)
+            return e;
+        int dev = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess ||
+            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+                hipSuccess)
+            return e;
+        const int grid = std::max(1, std::min(a.d.H * a.S, cus));
+        k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), bytes, stream>>>(a);
+        return hipGetLastError();
+    }
+    if ((e = set_lds(k_scan_mfma<P, N, DT, PG>, L.bytes)) != hipSuccess)
         return e;
     k_scan_mfma<P, N, DT, PG>
         <<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
@@ -1372,6 +1655,34 @@ hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
                       : decode_mfma<P, N, DT, false>(a, stream);
 }
 
+// Verification: the multi-row kernel for sequences whose drafts stay in the
+// chunk, then the prefill kernel's dry replay for those that run past its
+// end (it skips the others).
+template <int P, int N, class DT, bool PG>
+hipError_t verify_mfma(const ScanArgs &a, hipStream_t stream) {
+    const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
+    const size_t bytes = (size_t)VLayout(Qp, P).bytes * kDecodeWaves;
+    hipError_t e = set_lds(k_verify_mfma<P, N, DT, PG>, bytes);
+    if (e != hipSuccess)
+        return e;
+    const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
+    k_verify_mfma<P, N, DT, PG><<<dim3(HQ * a.S), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    ScanArgs c = a;
+    c.only_cross = 1;
+    return scan_mfma<P, N, DT, PG>(c, stream);
+}
+
+template <int P, int N>
+hipError_t verify_pn(const ScanArgs &a, hipStream_t s) {
+    if (a.bm.pages)
+        return a.d.dt_bf16 ? verify_mfma<P, N, IoBF16, true>(a, s)
+                           : verify_mfma<P, N, IoF32, true>(a, s);
+    return a.d.dt_bf16 ? verify_mfma<P, N, IoBF16, false>(a, s)
+                       : verify_mfma<P, N, IoF32, false>(a, s);
+}
+
 template <int P, int N>
 hipError_t scan_pn(const ScanArgs &a, hipStream_t s) {
     return a.d.dt_bf16 ? scan_mfma<P, N, IoBF16>(a, s) : scan_mfma<P, N, IoF32>(a, s);
@@ -1402,6 +1713,10 @@ hipError_t launch_scan_mfma(const ScanArgs &a, hipStream_t stream) { SSD_PN_SWIT
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
     SSD_PN_SWITCH(decode_pn, a, stream)
+}
+
+hipError_t launch_verify_mfma(const ScanArgs &a, hipStream_t stream) {
+    SSD_PN_SWITCH(verify_pn, a, stream)
 }
 
 }  // namespace ssd
