@@ -4,10 +4,14 @@ with the fp64 oracle, and the bit identity of its prefill and decode forms
 chained into the scan.
 
 Tolerance, derived from the arithmetic: each output is an fmaf chain of W
-products from the bias, then SiLU (expf, one division), in fp32. The chain's
-error is below W+1 fp32 half-ulps of M = |bias| + sum |w_i v_i| and SiLU
-adds a few ulps of its value, so |y32 - ref| <= 2e-6 * M + 1e-6 * |ref|
-(fp32 outputs). bf16 outputs add the storage rounding, half a bf16 ulp:
+products from the bias, then SiLU with the hardware exp2 and reciprocal, in
+fp32. The chain's error is below W+1 fp32 half-ulps of M = |bias| +
+sum |w_i v_i|. exp(-v) as exp2(-v log2 e) is off by |v| 2**-24 relative
+from the product's rounding plus an ulp, the reciprocal and product add two
+more, and SiLU passes the relative error of exp(-v) through at most 1:1, so
+|silu error| <= |ref| (|v| 2**-24 + 4 * 2**-23) <= 1e-6 |ref| + 2e-6 M
+(|v| <= M, |ref| <= |v| + 1). fp32 outputs: |y32 - ref| <= 2e-6 * M +
+1e-6 * |ref|. bf16 outputs add the storage rounding, half a bf16 ulp:
 |y - ref| <= 2**-8 * |ref| + 2e-6 * M.
 """
 import numpy as np
