@@ -148,7 +148,7 @@ def load_traffic(sha):
 
 
 CALIB_BYTES = 512 * 2 ** 20
-PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16>"
+PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16, false>"
 COPY_KERNEL = "copyBuffer"
 
 

@@ -420,7 +420,7 @@ int ssd_conv1d_varlen(const ssd_shape *sh, int32_t W, int32_t act, int32_t S, in
         return SSD_OK;
     if (!weight || (T > 0 && (!xBC || !x || !B || !C)))
         return SSD_ERR_NULL;
-    if (!all_a16(xBC, conv_state, x, B, C))
+    if (!all_a16(xBC, conv_state, x, B, C) || !all_a16(weight, bias))
         return SSD_ERR_ALIGN;
     int32_t maxlen = 0;
     for (int32_t s = 0; s < S; ++s)
@@ -456,7 +456,7 @@ int ssd_conv1d_update(const ssd_shape *sh, int32_t W, int32_t act, int32_t batch
         return SSD_OK;
     if (!weight || !xBC || !conv_state || !x || !B || !C)
         return SSD_ERR_NULL;
-    if (!all_a16(xBC, conv_state, x, B, C))
+    if (!all_a16(xBC, conv_state, x, B, C) || !all_a16(weight, bias))
         return SSD_ERR_ALIGN;
     ssd::ConvArgs a = {};
     a.d = d;

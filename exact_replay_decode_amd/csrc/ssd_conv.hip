@@ -78,18 +78,44 @@ __device__ __forceinline__ float conv_point(const float *w, const float (&v)[W],
     return act ? __fdividef(acc, 1.0f + __expf(-acc)) : acc;
 }
 
-// The thread's CG channels starting at c0: taps and bias.
+// The thread's CG channels starting at c0: taps and bias, read as 16-byte
+// pieces (the CG * W taps are contiguous and c0 * W * 4 bytes is a
+// multiple of 16 because CG * W * 4 is).
 template <int W, int CG>
 struct Taps {
     float w[CG][W];
     float b[CG];
     __device__ Taps(const float *weight, const float *bias, int c0) {
+        float f[CG * W];
+        const float4 *wp = reinterpret_cast<const float4 *>(weight + (int64_t)c0 * W);
+#pragma unroll
+        for (int k = 0; k < CG * W / 4; ++k) {
+            const float4 v = wp[k];
+            f[4 * k] = v.x;
+            f[4 * k + 1] = v.y;
+            f[4 * k + 2] = v.z;
+            f[4 * k + 3] = v.w;
+        }
 #pragma unroll
         for (int j = 0; j < CG; ++j) {
 #pragma unroll
             for (int i = 0; i < W; ++i)
-                w[j][i] = weight[(int64_t)(c0 + j) * W + i];
-            b[j] = bias ? bias[c0 + j] : 0.0f;
+                w[j][i] = f[j * W + i];
+        }
+        if (bias) {
+            const float4 *bp = reinterpret_cast<const float4 *>(bias + c0);
+#pragma unroll
+            for (int k = 0; k < CG / 4; ++k) {
+                const float4 v = bp[k];
+                b[4 * k] = v.x;
+                b[4 * k + 1] = v.y;
+                b[4 * k + 2] = v.z;
+                b[4 * k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CG; ++j)
+                b[j] = 0.0f;
         }
     }
 };
@@ -283,9 +309,12 @@ __global__ __launch_bounds__(256) void k_conv_update(ConvArgs a) {
     using T = typename IO::T;
     constexpr int CG = Lanes<IO>::CG;
     const int conv_dim = a.d.H * a.d.P + 2 * a.d.G * a.d.N;
-    const int cg = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
-    if (cg * CG >= conv_dim)
+    const int groups = conv_dim / CG;
+    // one thread per (row, channel group), rows back to back
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)a.S * groups)
         return;
+    const int b = (int)(idx / groups), cg = (int)(idx % groups);
     const int c0 = cg * CG;
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0 || slot >= a.num_slots)
@@ -332,7 +361,8 @@ template <class IO, int W>
 hipError_t conv_update(const ConvArgs &a, hipStream_t stream) {
     constexpr int CG = Lanes<IO>::CG;
     const int groups = (a.d.H * a.d.P + 2 * a.d.G * a.d.N) / CG;
-    k_conv_update<IO, W><<<dim3((groups + 255) / 256, a.S), dim3(256), 0, stream>>>(a);
+    const int64_t threads = (int64_t)a.S * groups;
+    k_conv_update<IO, W><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -848,12 +848,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     scan_one<P, N, DT, PG>(a, wid / a.d.H, wid % a.d.H, lds);
 }
 
-// Verification of drafts that run past the chunk end (dry replay, only_cross
-// set): one round of workgroups; each tests the (sequence, head) pairs
-// e = blockIdx.x + gridDim.x i in parallel, lists the crossing ones in LDS
-// and replays those (few) pairs one after another. The pairs with nothing
-// to do cost no dispatch of a large-LDS workgroup, and a sequence's heads
-// land on different workgroups.
+// Replay calls where few sequences have work: verification of drafts that
+// run past the chunk end (dry replay, only_cross), and acceptance (no_y),
+// where only the sequences whose accepted drafts fill a chunk have any.
+// One round of workgroups; each tests the (sequence, head) pairs
+// e = blockIdx.x + gridDim.x i in parallel, lists those with work in LDS
+// and replays them one after another. The pairs with nothing to do cost no
+// dispatch of a large-LDS workgroup, and a sequence's heads land on
+// different workgroups.
 template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -871,10 +873,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
         if (i < rounds && e < total) {
             const int s = e / H;
             const int slot = a.slot_idx ? a.slot_idx[s] : s;
-            const int len = a.cu[s + 1] - a.cu[s];
+            const int len = seq_len(a.cu, a.take, s);
             if (len > 0 && slot >= 0 && slot < a.num_slots) {
                 const int k = a.buf_len[slot];
-                if (k >= 0 && k < Q && k + len > Q)
+                if (k >= 0 && k < Q && (a.no_y ? k + len >= Q : k + len > Q))
                     list[1 + atomicAdd(list, 1)] = e;
             }
         }
@@ -1597,7 +1599,7 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
     const MLayout L(Qp, P, N);
     hipError_t e;
-    if (a.only_cross) {
+    if (a.only_cross || a.no_y) {
         // the crossing-draft sweep adds its pair list after the layout
         const size_t bytes = L.bytes + 4 * (1 + 64 * kPrefillWaves);
         if ((e = set_lds(k_scan_cross<P, N, DT, PG>, bytes)) != hipSuccess)

@@ -320,9 +320,9 @@ int ssm_state_update_varlen(const ssd_shape *shape, int32_t num_seqs,
  *   conv_state  [num_slots, conv_dim, W-1]  io_dtype, channel-major
  * Both forms evaluate every output with the same device routine on the same
  * W inputs, so decoding token by token reproduces the prefill's bits, and a
- * prefill split at any point reproduces the unsplit one. Pointers are
- * 16-byte aligned (SSD_ERR_ALIGN). shape->chunk_size and dt_dtype are not
- * used (any valid value). */
+ * prefill split at any point reproduces the unsplit one. Pointers,
+ * weight and bias included, are 16-byte aligned (SSD_ERR_ALIGN).
+ * shape->chunk_size and dt_dtype are not used (any valid value). */
 
 /* Prefill form over a varlen pack. Sequence s (tokens cu[s]..cu[s+1]-1)
  * starts from conv_state[slot_idx[s]] (slot_idx NULL = s) and leaves there

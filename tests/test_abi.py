@@ -233,6 +233,7 @@ def test_conv_checks():
     assert conv_prefill(sh, xBC=ctypes.c_void_p(0x1004)) == -9
     assert conv_prefill(sh, state=ctypes.c_void_p(0x1008), num_slots=1) == -9
     assert conv_prefill(sh, state=FAKE, num_slots=0) == -2     # state but no slots
+    assert conv_prefill(sh, weight=ctypes.c_void_p(0x1004)) == -9   # taps read in 16 B
     assert conv_prefill(sh, cu=[0, 4, 2, 8]) == -2
     assert conv_prefill(sh, cu=[0, 0]) == 0                    # empty sequence: nothing to do
     assert conv_prefill(shape(state_dtype=1)) == -4
