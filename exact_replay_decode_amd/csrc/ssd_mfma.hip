@@ -704,13 +704,14 @@ __device__ __forceinline__ int xcd_local_index(int bid, int nblocks) {
 }
 
 // Prefill workgroups have 8 waves (two per SIMD). With 8 t-blocks, waves w
-// and w + 4 (same SIMD) take t-blocks w and 7 - w: equal causal work per
-// SIMD. With fewer t-blocks, wave w takes t-block w.
+// and w + 4 (same SIMD) take t-blocks 7 - w and w: equal causal work per
+// SIMD, the heavy t-blocks on the older waves (which the SIMD serves first).
+// With fewer t-blocks, wave w takes t-block w.
 constexpr int kPrefillWaves = 8;
 
 __device__ __forceinline__ int wave_tblock(int nT, int wave) {
     if (nT == 8)
-        return wave < 4 ? wave : 11 - wave;
+        return wave < 4 ? 7 - wave : wave - 4;
     return wave < nT ? wave : -1;
 }
 
