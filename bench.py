@@ -239,7 +239,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scan shards by sequence and head with no "
-              "exchange, so multi-GPU runs are not part of this build (use --gpus 1)",
+              "exchange, and no multi-GPU path is built (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
