@@ -745,28 +745,35 @@ __global__ __launch_bounds__(kBlock) void k_ssu_varlen(SsuArgs a) {
     // one token's inputs as stored (converted where used), loaded one token
     // ahead so that their latency overlaps the current token's arithmetic
     struct TokIn {
-        TD dt;
         Seg16<IO> b, c;
         T x[NR];
     };
     auto load_tok = [&](int64_t tok, TokIn &in) {
-        in.dt = dts[tok * H + h];
         in.b.load(Bs + (tok * G + g) * N + 4 * c, L);
         in.c.load(Cs + (tok * G + g) * N + 4 * c, L);
 #pragma unroll
         for (int i = 0; i < NR; ++i)
             in.x[i] = xs[(tok * H + h) * P + min(rr + RP * i, P - 1)];
     };
-    // delta and the decay of the next token are computed at the end of the
-    // current one (they do not depend on the state)
+    // delta and decay depend on the token and head only: the workgroup
+    // computes them for kBlock tokens at a time, one token per thread (the
+    // same routines, so the same values as the one-token kernel), into LDS
+    __shared__ float s_dl[kBlock], s_al[kBlock];
     TokIn nxt;
     load_tok(t0, nxt);
-    float dl_n = delta_of(DT::val(nxt.dt), bias, d.softplus);
-    float alpha_n = decay_exp(dl_n * A_h);
     for (int t = 0; t < len; ++t) {
         const int64_t tok = t0 + t;
+        if (t % kBlock == 0) {
+            __syncthreads();   // the previous tokens' reads are done
+            if (t + tid < len) {
+                const float v = delta_of(DT::val(dts[(tok + tid) * H + h]), bias, d.softplus);
+                s_dl[tid] = v;
+                s_al[tid] = decay_exp(v * A_h);
+            }
+            __syncthreads();
+        }
         const TokIn cur = nxt;
-        const float dl = dl_n, alpha = alpha_n;
+        const float dl = s_dl[t % kBlock], alpha = s_al[t % kBlock];
         if (t + 1 < len)
             load_tok(tok + 1, nxt);
         float bv[16], cv[16];
@@ -786,10 +793,6 @@ __global__ __launch_bounds__(kBlock) void k_ssu_varlen(SsuArgs a) {
                 if (c == L - 1)
                     y[p] = IO::cvt(yv);
             }
-        }
-        if (t + 1 < len) {
-            dl_n = delta_of(DT::val(nxt.dt), bias, d.softplus);
-            alpha_n = decay_exp(dl_n * A_h);
         }
     }
 #pragma unroll
