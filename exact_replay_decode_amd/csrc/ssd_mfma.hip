@@ -257,18 +257,10 @@ template <int P, int N, int NW>
 struct StateTiles {
     static constexpr int NPT = P / 32, NNT = N / 32;
     static constexpr int total = NPT * NNT;
-    // Pairing needs the n-tiles to pair up and half the waves to hold them
-    // (the other waves then own no tile). It is off: with two tiles per
-    // wave the prefill kernel spills registers, for no measured gain.
-    static constexpr bool kPairTiles = false;
-    static constexpr bool paired = kPairTiles && NNT % 2 == 0 && total / 2 <= NW;
-    static constexpr int per_wave = paired ? 2 : (total + NW - 1) / NW;
+    // tiles w, w + NW, ... (round robin); giving one wave two n-tiles of a
+    // p-tile (one split for both) spills registers in the prefill kernel
+    static constexpr int per_wave = (total + NW - 1) / NW;
     __device__ static __forceinline__ bool tile(int w, int i, int &pt, int &nt) {
-        if (paired) {
-            pt = w % NPT;
-            nt = 2 * (w / NPT) + i;
-            return w < total / 2;
-        }
         const int ti = w + NW * i;
         pt = ti % NPT;
         nt = ti / NPT;
@@ -317,8 +309,8 @@ __device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds,
         return;
     for (int k = k0; k < k1; ++k) {
         const int r0 = 16 * k + 8 * g;
-        // split token operand for p-tile pt0 (shared by the wave's tiles
-        // when they are paired)
+        // split token operand for p-tile pt0 (shared by the wave's other
+        // tiles of that p-tile)
         const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt0 + 16 * ((lane >> 4) & 1));
         const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
         const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
@@ -331,7 +323,7 @@ __device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds,
             if (!ST::tile(wave, i, pt, nt))
                 continue;
             const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
-            if (!ST::paired && pt != pt0) {
+            if (pt != pt0) {
                 // round-robin tile of another p-tile: split that p-tile
                 bf16x8 qhi, qlo;
                 split_wx(lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt + 16 * ((lane >> 4) & 1)),
