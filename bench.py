@@ -195,6 +195,117 @@ def write_traffic(fetch_csv, write_csv, cmds):
     print(json.dumps(rec))
 
 
+STACK_LAYERS = 24            # layer-stack leg: layers, prompt, decode steps, chunk calls
+STACK_PROMPT, STACK_STEPS, STACK_CHUNK, STACK_CHUNKS = 600, 32, 100, 9
+GROUPED_PACK, GROUPED_COPIES = (600, 300, 900, 248), 64
+
+
+def other_workloads(erd, synth, torch, dev, warmup, steps):
+    """The survey's other measurement workloads, each timed with HIP events on
+    the launch stream after its own warm-up:
+      - prefill latency of one 2048-token sequence (H=32, G=1, P=64, N=128,
+        chunk 256; launch-bound: 32 workgroups);
+      - prefill throughput of the grouped-heads pack {600, 300, 900, 248} x 64
+        (256 sequences, 131,072 tokens; H=64, G=8, P=64, N=128, chunk 256);
+      - a 24-layer stack at batch 1 (H=24, G=1, P=64, N=128, chunk 256): per
+        layer a 600-token exact-replay prefill, then decode steps of all 24
+        layers, then 900 more tokens as 100-token chunked-prefill calls."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n   # seconds per call
+
+    out = {}
+    # W1a: one sequence
+    H, G, P, N, Q, T = 32, 1, 64, 128, 256, 2048
+    sh = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    hp = synth.make_head_params(H, 0)
+    A, D, bias = (torch.from_numpy(v).to(dev) for v in (hp.A, hp.D, hp.dt_bias))
+    x, dt, B, C = synth.make_tokens_torch(T, H, G, P, N, 7, dev)
+    cu_host = synth.cu_seqlens([T])
+    cu = torch.from_numpy(cu_host).to(dev)
+    y = torch.empty_like(x)
+    bnd = torch.empty((1, H, P, N), dtype=torch.float32, device=dev)
+    t = timed(lambda: erd.ssd_prefill_varlen(sh, cu, x, dt, A, B, C, D, bias, y=y,
+                                             boundary_state=bnd, cu_seqlens_host=cu_host,
+                                             want_final=False), steps)
+    out["prefill_1x2048"] = {"us_per_launch": 1e6 * t, "tokens_per_s": T / t,
+                             "hbm_frac": prefill_bytes(T, 1, H, G, P, N) / t / 1e9 / HBM_PEAK_GBS}
+    del x, dt, B, C, y
+
+    # W2: grouped heads, pack x 64
+    H, G = 64, 8
+    sh = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    hp = synth.make_head_params(H, 1)
+    A, D, bias = (torch.from_numpy(v).to(dev) for v in (hp.A, hp.D, hp.dt_bias))
+    lens = list(GROUPED_PACK) * GROUPED_COPIES
+    T = sum(lens)
+    x, dt, B, C = synth.make_tokens_torch(T, H, G, P, N, 8, dev)
+    cu_host = synth.cu_seqlens(lens)
+    cu = torch.from_numpy(cu_host).to(dev)
+    y = torch.empty_like(x)
+    bnd = torch.empty((len(lens), H, P, N), dtype=torch.float32, device=dev)
+    t = timed(lambda: erd.ssd_prefill_varlen(sh, cu, x, dt, A, B, C, D, bias, y=y,
+                                             boundary_state=bnd, cu_seqlens_host=cu_host,
+                                             want_final=False), steps)
+    gb = prefill_bytes(T, len(lens), H, G, P, N)
+    out["prefill_grouped_pack_x64"] = {"ms_per_launch": 1e3 * t, "tokens_per_s": T / t,
+                                       "hbm_gbs": gb / t / 1e9,
+                                       "hbm_frac": gb / t / 1e9 / HBM_PEAK_GBS,
+                                       "sequences": len(lens), "tokens": T}
+    del x, dt, B, C, y, bnd
+
+    # W4: 24-layer stack at batch 1
+    H, G, L = 24, 1, STACK_LAYERS
+    sh = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    ndec = (warmup + steps) * STACK_STEPS
+    ntok = STACK_PROMPT + ndec + STACK_CHUNK * (warmup + STACK_CHUNKS)
+    layers = []
+    for li in range(L):
+        hp = synth.make_head_params(H, 100 + li)
+        prm = tuple(torch.from_numpy(v).to(dev) for v in (hp.A, hp.D, hp.dt_bias))
+        toks = synth.make_tokens_torch(ntok, H, G, P, N, 100 + li, dev)
+        cache = erd.ReplayCache(sh, 1, dev)
+        erd.ssd_replay_prefill(sh, cache, [0, STACK_PROMPT], *(v[:STACK_PROMPT] for v in toks),
+                               *prm)
+        plan = erd.DecodePlan(sh, 1, *prm, cache=cache)
+        layers.append((prm, toks, cache, plan))
+    yd = torch.empty((1, H, P), dtype=torch.bfloat16, device=dev)
+    pos = [STACK_PROMPT]
+
+    def decode_step():
+        p0 = pos[0]
+        for prm, (x, dt, B, C), cache, plan in layers:
+            plan(x[p0:p0 + 1], dt[p0:p0 + 1], B[p0:p0 + 1], C[p0:p0 + 1], yd)
+        pos[0] = p0 + 1
+
+    t_dec = timed(decode_step, steps * STACK_STEPS)
+    chunk_cu = [0, STACK_CHUNK]
+
+    def chunk_call():
+        p0 = pos[0]
+        for prm, toks, cache, plan in layers:
+            erd.ssd_replay_prefill(sh, cache, chunk_cu, *(v[p0:p0 + STACK_CHUNK] for v in toks),
+                                   *prm)
+        pos[0] = p0 + STACK_CHUNK
+
+    t_chunk = timed(chunk_call, STACK_CHUNKS)
+    out["layer_stack_24"] = {"decode_ms_per_step": 1e3 * t_dec,
+                             "decode_us_per_layer": 1e6 * t_dec / L,
+                             "chunked_prefill_ms_per_100_tokens": 1e3 * t_chunk,
+                             "layers": L, "heads": H, "batch": 1}
+    return out
+
+
 def cpu_baseline(x, dt, B, C, hp, Q, T, target_s=10.0):
     """Time the fp64 oracle on a bounded sample of the prefill workload
     (whole 2048-token sequences, read back exactly from the device)."""
@@ -459,6 +570,8 @@ def main():
     def span(i, j):
         return sum(e[i].elapsed_time(e[j]) for e in evs) / 1e3   # seconds, summed
 
+    others = other_workloads(erd, synth, torch, dev, args.warmup, args.steps)
+
     K = args.steps
     t_prefill = span(0, 1)
     t_commit = span(1, 2)
@@ -570,6 +683,7 @@ def main():
             "alu_tflops": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12,
             "alu_frac": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12 / FP32_VALU_PEAK_TFLOPS,
         },
+        "other_workloads": others,
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,
         "kernel_source_sha": sha,
