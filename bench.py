@@ -209,7 +209,8 @@ def other_workloads(erd, synth, torch, dev, warmup, steps):
         (256 sequences, 131,072 tokens; H=64, G=8, P=64, N=128, chunk 256);
       - a 24-layer stack at batch 1 (H=24, G=1, P=64, N=128, chunk 256): per
         layer a 600-token exact-replay prefill, then decode steps of all 24
-        layers, then 900 more tokens as 100-token chunked-prefill calls."""
+        layers (launched one by one, and from a captured HIP graph), then 900
+        more tokens as 100-token chunked-prefill calls."""
     stream = torch.cuda.current_stream()
 
     def timed(fn, n):
@@ -299,8 +300,23 @@ def other_workloads(erd, synth, torch, dev, warmup, steps):
         pos[0] = p0 + STACK_CHUNK
 
     t_chunk = timed(chunk_call, STACK_CHUNKS)
+
+    # the same 24-layer decode step captured once in a HIP graph and replayed
+    # (the step needs no host-side metadata; the replays decode the captured
+    # input buffers, which hold one token per layer)
+    cs = torch.cuda.Stream()
+    gplans = [erd.DecodePlan(sh, 1, *prm, cache=cache, stream=cs)
+              for prm, toks, cache, plan in layers]
+    gin = [tuple(v[pos[0]:pos[0] + 1].clone() for v in toks) for prm, toks, cache, plan in layers]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        for gp, xs in zip(gplans, gin):
+            gp(*xs, yd)
+    t_graph = timed(graph.replay, steps * STACK_STEPS)
     out["layer_stack_24"] = {"decode_ms_per_step": 1e3 * t_dec,
                              "decode_us_per_layer": 1e6 * t_dec / L,
+                             "decode_ms_per_step_hip_graph": 1e3 * t_graph,
                              "chunked_prefill_ms_per_100_tokens": 1e3 * t_chunk,
                              "layers": L, "heads": H, "batch": 1}
     return out

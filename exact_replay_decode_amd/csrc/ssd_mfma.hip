@@ -907,9 +907,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
 constexpr int kDecodeWaves = 4;
 
 // Workgroups of the chunk-commit kernel: as many as fit on the device at
-// once (compute units x workgroups per unit that the LDS allows, at most 4),
-// each handling one head of a full chunk at a time; when no chunk filled
-// they return at once, in one dispatch round.
+// once (compute units x workgroups per unit that the LDS allows, at most 4)
+// and at most one per (sequence, head) of the batch, each handling one head
+// of a full chunk at a time; when no chunk filled they return at once, in
+// one dispatch round.
 constexpr int kLdsBytesPerCu = 160 * 1024;
 // The work array after the per-slot arrival counters: [0] number of slots
 // on the commit list, [1] finished groups, [2, 2 + kDoneGroups) finished
@@ -919,9 +920,9 @@ constexpr int kListHead = 2 + kDoneGroups;
 
 // Per-wave LDS of the decode kernel, in bytes.
 struct DLayout {
-    int XS;
-    int lam, u, beta, gc, X, bytes;
-    __host__ __device__ DLayout(int Qp, int P, int N) {
+    int XS, cXS, cBS;
+    int lam, u, beta, gc, X, cX, cB, w, bytes;
+    __host__ __device__ DLayout(int Qp, int P, int N, bool fused) {
         XS = P + kPad;
         int o = 0;
         lam = o;  o += Qp * 4;
@@ -929,8 +930,21 @@ struct DLayout {
         beta = o; o += Qp * 4;
         gc = o;   o += (kMaxQ / 32) * 32 * 4;   // C.B^T column k % 32 per s-block
         X = o;    o += 32 * XS * 2;              // padded 32-row x tile
+        // with the chunk-state update in the same launch: its 16-row blocks
+        // (x: 32 columns, B: all N) over the arrays above once the output is
+        // written, and the state weights of the chunk-filling step
+        cXS = 32 + kPad;
+        cBS = N + kPad;
+        cX = 0;
+        cB = cX + 16 * cXS * 2;
+        w = o;
+        if (fused) {
+            const int cend = cB + 16 * cBS * 2;
+            o = o > cend ? o : cend;
+            w = o;
+            o += Qp * 4;
+        }
         bytes = (o + 15) & ~15;
-        (void)N;
     }
 };
 
@@ -962,7 +976,7 @@ __device__ __forceinline__ void load_x_tile(const uint16_t *bx, const SlotRows<P
 
 // Phase 1: the wave's loads, the read-out, the append of the token, the
 // in-chunk scan and the C.B^T columns of the s-blocks this wave owns.
-template <int P, int N, class DT, bool PG>
+template <int P, int N, class DT, bool PG, bool FUSED>
 __device__ __forceinline__ void decode_front(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
                                              int slot, int h, int k, int wave, bool gshare,
                                              char *lds, const DLayout &L, DecodeCarry<P, DT> &cy) {
@@ -1101,6 +1115,17 @@ __device__ __forceinline__ void decode_front(const DecodeArgs &a, const SlotRows
         }
     }
     cy.lam_k = lam[k];
+    if (FUSED && k + 1 == Q) {
+        // the token fills the chunk: state weights 2^(lam_last - lam_j) delta_j
+        // for the chunk-state update (zero past row k)
+        float *w = reinterpret_cast<float *>(lds + L.w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = lane + 64 * i;
+            if (i < nseg && j < Qp)
+                w[j] = fexp2(cy.lam_k - lv[i]) * dv[i];
+        }
+    }
     const float el_k = fexp2(cy.lam_k);
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
@@ -1213,7 +1238,147 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<
     }
 }
 
+// Phase 3, only when the token fills the chunk: the chunk-state update of
+// the wave's head, S <- 2^lam_last S + sum_j B_j (w_j x_j), with the
+// prefill's operands and MFMA order (split_wx, state_step, K = Qp rows in
+// steps of 16, hi then lo), so the new boundary state has the bits a
+// prefill of the same tokens leaves. The weights w_j were put in LDS by
+// phase 1. Rows 16 kb .. +15 of x (32 columns of one p-tile) and of B (all
+// N columns) pass through LDS for the transposed reads, the next block's
+// rows in flight during this block's MFMAs; rows below k come from the slot
+// buffer, row k from the step's input (the buffer row written by this step
+// is not read back), rows after k are zero. Two passes (one per p-tile)
+// keep four accumulator tiles live.
 template <int P, int N, class DT, bool PG>
+__device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
+                                              int slot, int h, int k, char *lds, const DLayout &L,
+                                              float lam_last) {
+    constexpr int NPT = P / 32, NNT = N / 32;
+    constexpr int BPL = N / 32;   // 16-byte pieces of a 16-row B block per lane
+    const Dims d = a.d;
+    const int H = d.H, G = d.G, Q = d.Q;
+    const int Qp = Q < 32 ? 32 : Q;
+    const int g = h / (H / G);
+    const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
+    const int64_t PN = (int64_t)P * N;
+    const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pools
+    const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
+    const uint16_t *xin = static_cast<const uint16_t *>(a.x) + ((int64_t)b * H + h) * P;
+    const uint16_t *Bin = static_cast<const uint16_t *>(a.B) + ((int64_t)b * G + g) * N;
+    float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
+    uint16_t *sbf = static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN;
+    const float *w = reinterpret_cast<const float *>(lds + L.w);
+    const float dec = fexp2(lam_last);
+    const int nkb = Qp / 16;
+    // blocks holding rows 0..k; the later ones (chunks under 32 rows) are
+    // all zero: only zero x rows are staged for them, and the zero x operand
+    // also serves as the B operand (the bits zeroed B rows would give), so
+    // the B block stays in LDS for the next p-tile when it is the only one
+    const int nreal = (k + 16) >> 4;
+
+    auto load_block = [&](int pt, int kb, bool withB, uint4 &xr, uint4 (&br)[BPL]) {
+        {
+            const int j = 16 * kb + (lane >> 2);
+            const int64_t rj = rows(j < k ? j : 0);
+            const uint16_t *src = j < k ? bx + (rj * H + h) * P : xin;
+            xr = *reinterpret_cast<const uint4 *>(src + 32 * pt + 8 * (lane & 3));
+        }
+        if (!withB)
+            return;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int e = lane + 64 * i, j = 16 * kb + e / (N / 8);
+            const int64_t rj = rows(j < k ? j : 0);
+            const uint16_t *src = j < k ? bB + (rj * G + g) * N : Bin;
+            br[i] = *reinterpret_cast<const uint4 *>(src + 8 * (e % (N / 8)));
+        }
+    };
+    auto store_block = [&](int kb, bool withB, const uint4 &xr, const uint4 (&br)[BPL]) {
+        {
+            const int r = lane >> 2;
+            *reinterpret_cast<uint4 *>(lds + L.cX + (r * L.cXS + 8 * (lane & 3)) * 2) =
+                keep_if(16 * kb + r <= k, xr);
+        }
+        if (!withB)
+            return;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int e = lane + 64 * i, r = e / (N / 8);
+            *reinterpret_cast<uint4 *>(lds + L.cB + (r * L.cBS + 8 * (e % (N / 8))) * 2) =
+                keep_if(16 * kb + r <= k, br[i]);
+        }
+    };
+
+#pragma unroll 1
+    for (int pt = 0; pt < NPT; ++pt) {
+        const bool newB = nreal > 1 || pt == 0;
+        uint4 xa, ba[BPL];
+        load_block(pt, 0, newB, xa, ba);
+        // the old tiles in the accumulator layout S^T[n][p], p = 32 pt + c,
+        // n = 32 nt + 8 q + 4 gl + (0..3), decayed to the chunk end
+        f32x16 acc[NNT];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4 *>(
+                    st + (int64_t)(32 * pt + c) * N + 32 * nt + 8 * q + 4 * gl);
+                acc[nt][4 * q] = v.x * dec;
+                acc[nt][4 * q + 1] = v.y * dec;
+                acc[nt][4 * q + 2] = v.z * dec;
+                acc[nt][4 * q + 3] = v.w * dec;
+            }
+        for (int kb = 0; kb < nreal; ++kb) {
+            store_block(kb, newB, xa, ba);
+            if (kb + 1 < nreal)
+                load_block(pt, kb + 1, true, xa, ba);
+            const int r0 = 8 * gl;
+            const i16x8 xv = lds_tr8(lds, L.cX, L.cXS, r0, r0 + 4, 16 * ((lane >> 4) & 1));
+            const float4 w0 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0 + 4);
+            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            bf16x8 bhi, blo;
+            split_wx(xv, ws, bhi, blo);
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                const bf16x8 aop = as_bf16x8(
+                    lds_tr8(lds, L.cB, L.cBS, r0, r0 + 4, 32 * nt + 16 * ((lane >> 4) & 1)));
+                state_step(aop, bhi, blo, acc[nt]);
+            }
+        }
+        if (nreal < nkb)
+            *reinterpret_cast<uint4 *>(lds + L.cX + ((lane >> 2) * L.cXS + 8 * (lane & 3)) * 2) =
+                make_uint4(0, 0, 0, 0);
+        for (int kb = nreal; kb < nkb; ++kb) {
+            const int r0 = 8 * gl;
+            const i16x8 xv = lds_tr8(lds, L.cX, L.cXS, r0, r0 + 4, 16 * ((lane >> 4) & 1));
+            const float4 w0 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0 + 4);
+            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            bf16x8 bhi, blo;
+            split_wx(xv, ws, bhi, blo);
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+                state_step(as_bf16x8(xv), bhi, blo, acc[nt]);
+        }
+        // the new tiles of the fp32 state and of its bf16 copy
+        const int p = 32 * pt + c;
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 32 * nt + 8 * q + 4 * gl;
+                const f32x16 &t = acc[nt];
+                *reinterpret_cast<float4 *>(st + (int64_t)p * N + n) =
+                    make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
+                *reinterpret_cast<uint2 *>(sbf + state_bf_index(p, n, P)) = make_uint2(
+                    bf16_rne(t[4 * q]) | ((uint32_t)bf16_rne(t[4 * q + 1]) << 16),
+                    bf16_rne(t[4 * q + 2]) | ((uint32_t)bf16_rne(t[4 * q + 3]) << 16));
+            }
+    }
+}
+
+template <int P, int N, class DT, bool PG, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_decode_mfma(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds_all[];
@@ -1225,7 +1390,7 @@ void k_decode_mfma(DecodeArgs a) {
     const int b = wid / HQ;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int h = (wid % HQ) * kDecodeWaves + wave;
-    const DLayout L(Qp, P, N);
+    const DLayout L(Qp, P, N, FUSED);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0 || slot >= a.num_slots)
         return;
@@ -1240,8 +1405,8 @@ void k_decode_mfma(DecodeArgs a) {
     const bool gshare = (H / G) % kDecodeWaves == 0;
     DecodeCarry<P, DT> cy;
     if (h < H)
-        decode_front<P, N, DT>(a, rows, b, slot, h, k, wave, gshare, lds_all + wave * L.bytes, L,
-                               cy);
+        decode_front<P, N, DT, PG, FUSED>(a, rows, b, slot, h, k, wave, gshare,
+                                          lds_all + wave * L.bytes, L, cy);
     __syncthreads();  // C.B^T columns of every wave are in LDS
     // Every wave of this workgroup has read buf_len (and used it) by now, so
     // the workgroup counts itself in; the slot's last workgroup to arrive
@@ -1256,12 +1421,20 @@ void k_decode_mfma(DecodeArgs a) {
                                       __HIP_MEMORY_SCOPE_AGENT);
     if (h < H)
         decode_back<P, N, DT>(a, rows, b, h, k, wave, gshare, lds_all, L, cy);
+    if (FUSED && k + 1 == Q) {
+        __syncthreads();  // every wave is done with the C.B^T columns in LDS
+        if (h < H)
+            decode_commit<P, N, DT>(a, rows, b, slot, h, k, lds_all + wave * L.bytes, L,
+                                    cy.lam_k);
+    }
     if (threadIdx.x == 0 && prev == HQ - 1) {
         __hip_atomic_store(a.work + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         a.buf_len[slot] = k + 1 == Q ? 0 : k + 1;
         if (k + 1 == Q) {
-            // the chunk is full: its state update runs in k_decode_commit
             a.boundary_pos[slot] += Q;
+        }
+        if (!FUSED && k + 1 == Q) {
+            // the chunk is full: its state update runs in k_decode_commit
             int32_t *list = a.work + a.num_slots;
             const int at = __hip_atomic_fetch_add(list, 1, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
@@ -1622,25 +1795,42 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
 template <int P, int N, class DT, bool PG>
 hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
-    const size_t bytes = (size_t)DLayout(Qp, P, N).bytes * kDecodeWaves;
-    hipError_t e = set_lds(k_decode_mfma<P, N, DT, PG>, bytes);
-    if (e != hipSuccess)
-        return e;
     const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
-    k_decode_mfma<P, N, DT, PG>
+    hipError_t e;
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return e;
+    // A batch whose workgroups all run at once (three per compute unit) does
+    // the chunk-state updates inside the decode launch: one launch per step,
+    // and no workgroup waits behind an updating one. A larger batch leaves
+    // them to k_decode_commit, so that the updates do not become the tail of
+    // the decode launch.
+    if ((int64_t)HQ * a.batch <= (int64_t)std::max(1, cus) * 3) {
+        const size_t bytes = (size_t)DLayout(Qp, P, N, true).bytes * kDecodeWaves;
+        if ((e = set_lds(k_decode_mfma<P, N, DT, PG, true>, bytes)) != hipSuccess)
+            return e;
+        k_decode_mfma<P, N, DT, PG, true>
+            <<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+        return hipGetLastError();
+    }
+    const size_t bytes = (size_t)DLayout(Qp, P, N, false).bytes * kDecodeWaves;
+    if ((e = set_lds(k_decode_mfma<P, N, DT, PG, false>, bytes)) != hipSuccess)
+        return e;
+    k_decode_mfma<P, N, DT, PG, false>
         <<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const MLayout LC(Qp, P, N);
     if ((e = set_lds(k_decode_commit<P, N, DT, PG>, LC.bytes)) != hipSuccess)
         return e;
-    int dev = 0, cus = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess ||
-        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-        return e;
+    // at most one workgroup per (sequence, head) that could commit: a small
+    // batch launches a small grid
     const int per_cu = std::max(1, std::min(4, kLdsBytesPerCu / (int)LC.bytes));
-    k_decode_commit<P, N, DT, PG>
-        <<<dim3(std::max(1, cus) * per_cu), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
+    const int64_t items = (int64_t)a.batch * a.d.H;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)std::max(1, cus) * per_cu,
+                                                                  items));
+    k_decode_commit<P, N, DT, PG><<<dim3(grid), dim3(64 * kCommitWaves), LC.bytes, stream>>>(a);
     return hipGetLastError();
 }
 
