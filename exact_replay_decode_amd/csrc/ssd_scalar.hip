@@ -453,6 +453,49 @@ __global__ void k_decode_advance(int batch, const int32_t *slot_idx, int32_t *bu
 // optional boundary-state copy. Workgroup (s, 0) handles sequence s's buffer
 // and metadata; workgroup (s, 1 + h) copies head h of its boundary state
 // (and writes the bf16 copy) when state_src is given.
+// Rows [row0, row0 + ntok) of a token-major array (per elements of type E
+// per row) to buffer positions dst0.. of a slot, kCopyBatch elements per
+// thread loaded before any is stored (loads of a batch are in flight
+// together). Whole workgroup.
+constexpr int kCopyBatch = 8;
+
+template <class E, bool PAGED>
+__device__ __forceinline__ void copy_rows_batched(const BufMap &bm, int slot, int Q, int dst0,
+                                                  E *d, const E *s, int n, int per, int tid) {
+    for (int e0 = 0; e0 < n; e0 += kCopyBatch * kBlock) {
+        E v[kCopyBatch];
+#pragma unroll
+        for (int i = 0; i < kCopyBatch; ++i) {
+            const int e = e0 + tid + i * kBlock;
+            v[i] = s[e < n ? e : n - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < kCopyBatch; ++i) {
+            const int e = e0 + tid + i * kBlock;
+            const int j = dst0 + (e < n ? e : n - 1) / per;
+            const int64_t row = PAGED ? ((int64_t)bm.pages[(int64_t)slot * bm.npp + (j >> bm.shift)]
+                                         << bm.shift) + (j & ((1 << bm.shift) - 1))
+                                      : (int64_t)slot * Q + j;
+            if (e < n)
+                d[row * per + e % per] = v[i];
+        }
+    }
+}
+
+template <class E>
+__device__ __forceinline__ void copy_to_buffer(const BufMap &bm, int slot, int Q, int dst0,
+                                               void *dst, const void *src, int64_t row0,
+                                               int ntok, int per, int tid) {
+    // (32-bit element indices: at most Q rows of at most H*P elements)
+    const E *s = static_cast<const E *>(src) + row0 * per;
+    E *d = static_cast<E *>(dst);
+    const int n = ntok * per;
+    if (bm.pages)
+        copy_rows_batched<E, true>(bm, slot, Q, dst0, d, s, n, per, tid);
+    else
+        copy_rows_batched<E, false>(bm, slot, Q, dst0, d, s, n, per, tid);
+}
+
 template <class IO, class DT>
 __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     using T = typename IO::T;
@@ -472,17 +515,31 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
             return;
         const int h = part - 1;
         const int64_t PN = (int64_t)P * N;
-        const float4 *src =
-            reinterpret_cast<const float4 *>(a.state_src + ((int64_t)s * H + h) * PN);
-        float4 *dst = reinterpret_cast<float4 *>(a.cache_state + ((int64_t)slot * H + h) * PN);
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 *src =
+            reinterpret_cast<const f32x4 *>(a.state_src + ((int64_t)s * H + h) * PN);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(a.cache_state + ((int64_t)slot * H + h) * PN);
         uint16_t *dbf = static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN;
-        for (int64_t e = tid; e < PN / 4; e += kBlock) {
-            const float4 v = src[e];
-            dst[e] = v;
-            const int p = (int)((4 * e) / N), n = (int)((4 * e) % N);
-            *reinterpret_cast<uint2 *>(dbf + state_bf_index(p, n, P)) =
-                make_uint2(bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
-                           bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
+        const int n4 = (int)(PN / 4);
+        // kCopyBatch pieces per thread loaded before any is stored
+        for (int e0 = 0; e0 < n4; e0 += kCopyBatch * kBlock) {
+            f32x4 v[kCopyBatch];
+#pragma unroll
+            for (int i = 0; i < kCopyBatch; ++i) {
+                const int e = e0 + tid + i * kBlock;
+                v[i] = src[e < n4 ? e : n4 - 1];
+            }
+#pragma unroll
+            for (int i = 0; i < kCopyBatch; ++i) {
+                const int e = e0 + tid + i * kBlock;
+                if (e < n4) {
+                    dst[e] = v[i];
+                    const int p = 4 * e / N, n = 4 * e % N;
+                    *reinterpret_cast<uint2 *>(dbf + state_bf_index(p, n, P)) = make_uint2(
+                        bf16_rne(v[i].x) | ((uint32_t)bf16_rne(v[i].y) << 16),
+                        bf16_rne(v[i].z) | ((uint32_t)bf16_rne(v[i].w) << 16));
+                }
+            }
         }
         return;
     }
@@ -503,25 +560,16 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
     // token rows in 16-byte pieces (a row of x or B is a multiple of 32
     // bytes), each to the buffer row of its position
-    auto copy_rows = [&](void *dst, const void *src, int64_t row_elems) {
-        const int64_t per = row_elems * (int64_t)sizeof(T) / 16;
-        for (int64_t e = tid; e < ntok * per; e += kBlock) {
-            const int r = (int)(e / per);
-            const int64_t q = e % per;
-            const int64_t row = buf_row(a.bm, slot, Q, dst0 + r);
-            reinterpret_cast<uint4 *>(dst)[row * per + q] =
-                reinterpret_cast<const uint4 *>(src)[(t0 + src0 + r) * per + q];
-        }
-    };
-    copy_rows(a.buf_x, x, HP);
-    copy_rows(a.buf_B, B, GN);
+    const int64_t src_row0 = t0 + src0;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    copy_to_buffer<u32x4>(a.bm, slot, Q, dst0, a.buf_x, x, src_row0, ntok,
+                          (int)(HP * (int64_t)sizeof(T) / 16), tid);
+    copy_to_buffer<u32x4>(a.bm, slot, Q, dst0, a.buf_B, B, src_row0, ntok,
+                          (int)(GN * (int64_t)sizeof(T) / 16), tid);
     if (a.buf_C)
-        copy_rows(a.buf_C, C, GN);
-    TD *bdt = static_cast<TD *>(a.buf_dt);
-    for (int64_t e = tid; e < (int64_t)ntok * H; e += kBlock) {
-        const int r = (int)(e / H);
-        bdt[buf_row(a.bm, slot, Q, dst0 + r) * H + e % H] = dt[(t0 + src0) * H + e];
-    }
+        copy_to_buffer<u32x4>(a.bm, slot, Q, dst0, a.buf_C, C, src_row0, ntok,
+                              (int)(GN * (int64_t)sizeof(T) / 16), tid);
+    copy_to_buffer<TD>(a.bm, slot, Q, dst0, a.buf_dt, dt, src_row0, ntok, H, tid);
     __syncthreads();
     if (tid == 0) {
         a.buf_len[slot] = nfull == 0 ? total : tail;
