@@ -901,9 +901,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
 //   - the in-chunk scan is the prefill's block scan, one 64-row segment at a
 //     time (wave_scan_segments).
 // The last workgroup of a slot to arrive advances buf_len / boundary_pos
-// (per-slot arrival counter); when the token filled the chunk it also puts
-// the slot on a list, and a second kernel (k_decode_commit) runs the
-// chunk-state update of those slots with the prefill's own chunk routines.
+// (per-slot arrival counter). When the token filled the chunk, the
+// chunk-state update with the prefill's own chunk arithmetic follows: in
+// the same kernel (FUSED, each wave its head: decode_commit) for a batch
+// whose workgroups all run at once, else the last workgroup puts the slot
+// on a list and a second kernel (k_decode_commit) updates the listed slots.
 constexpr int kDecodeWaves = 4;
 
 // Workgroups of the chunk-commit kernel: as many as fit on the device at
