@@ -1545,7 +1545,10 @@ __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs 
 // output row depends only on its own columns of C and M, so each draft's
 // output has the bits decode would give it. Operands come from global
 // memory: committed rows from the slot buffer, drafts from the inputs, rows
-// after the last draft are zero. Nothing but y is written. Sequences whose
+// after the last draft are zero. When the workgroup's heads share a B/C
+// group, the C.B^T blocks are computed once per workgroup (each wave a
+// quarter of the s-blocks) and read by all four from LDS; the workgroup then
+// meets at two barriers per t-block. Nothing but y is written. Sequences whose
 // drafts run past the chunk end are left to the prefill kernel's dry replay.
 struct VLayout {
     int XS;
@@ -1561,7 +1564,7 @@ struct VLayout {
     }
 };
 
-template <int P, int N, class DT, bool PG>
+template <int P, int N, class DT, bool PG, bool GSHARE>
 __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds_all[];
     using TD = typename DT::T;
@@ -1576,6 +1579,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
     const int h = (wid % HQ) * kDecodeWaves + wave;
     const VLayout L(Qp, P);
     char *lds = lds_all + wave * L.bytes;
+    // GSHARE: the launcher's choice when the workgroup's heads share a B/C
+    // group ((H / G) % 4 == 0); every head of the workgroup exists then and
+    // the returns below are the same for all four waves
+    constexpr bool gshare = GSHARE;
+    float *gsh = reinterpret_cast<float *>(lds_all + kDecodeWaves * L.bytes);
     const int64_t t0 = a.cu[sq];
     const int T = a.cu[sq + 1] - a.cu[sq];
     const int slot = a.slot_idx ? a.slot_idx[sq] : sq;
@@ -1676,9 +1684,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
                     cf),
                 fexp2(lam_t));
         // B rows and x rows of s-block sg (committed rows from the buffer,
-        // drafts from the inputs), one block ahead of their use
+        // drafts from the inputs)
         constexpr int XPL = P / 16;
-        auto load_blk = [&](int sg, uint4 (&braw)[NK], uint4 (&xr)[XPL]) {
+        auto load_b = [&](int sg, uint4 (&braw)[NK]) {
             const int srow = 32 * sg + c;
             const int64_t rs = rows(srow);
             const uint16_t *brow =
@@ -1686,6 +1694,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk)
                 braw[kk] = *reinterpret_cast<const uint4 *>(brow + 16 * kk + 8 * gl);
+        };
+        auto load_x = [&](int sg, uint4 (&xr)[XPL]) {
 #pragma unroll
             for (int i = 0; i < XPL; ++i) {
                 const int e = lane + 64 * i, r = e / (P / 8), q = e % (P / 8);
@@ -1696,22 +1706,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
                 xr[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
             }
         };
-        uint4 nb_[NK], nx_[XPL];
-        load_blk(0, nb_, nx_);
-        for (int sg = 0; sg <= tau; ++sg) {
-            uint4 braw[NK], xr[XPL];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk)
-                braw[kk] = nb_[kk];
-#pragma unroll
-            for (int i = 0; i < XPL; ++i)
-                xr[i] = nx_[i];
-            if (sg < tau)
-                load_blk(sg + 1, nb_, nx_);
-            const int srow = 32 * sg + c;
-            const bool sok = srow <= last;
-            const f32x16 gt = gram_block<N>(
+        auto gram_of = [&](int sg, const uint4 (&braw)[NK]) {
+            const bool sok = 32 * sg + c <= last;
+            return gram_block<N>(
                 [&](int kk) { return __builtin_bit_cast(bf16x8, keep_if(sok, braw[kk])); }, cf);
+        };
+        // weights of s-block sg from its C.B^T block, the x rows through the
+        // wave's LDS tile, Y^T += X^T M^T
+        auto accumulate = [&](int sg, const f32x16 &gt, const uint4 (&xr)[XPL]) {
             uint32_t mb[8];
             if (sg == tau)
                 m_diag(gt, lam_t, uu, 32 * sg, t, mb);
@@ -1727,6 +1729,72 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
                     keep_if(32 * sg + r <= last, xr[i]);
             }
             mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc);
+        };
+        if constexpr (gshare) {
+            // the C.B^T blocks of this t-block, split between the waves
+            // (s-blocks wave, wave + 4, ...) and handed over in LDS, where
+            // element r of lane l sits at float (r / 4) * 256 + 4 l + r % 4
+            uint4 nx_[XPL];
+            load_x(0, nx_);
+            if (tau > tau0)
+                __syncthreads();   // the previous t-block's blocks are read
+            if (wave <= tau) {
+                uint4 nb_[NK];
+                load_b(wave, nb_);
+                for (int sg = wave; sg <= tau; sg += kDecodeWaves) {
+                    uint4 braw[NK];
+#pragma unroll
+                    for (int kk = 0; kk < NK; ++kk)
+                        braw[kk] = nb_[kk];
+                    if (sg + kDecodeWaves <= tau)
+                        load_b(sg + kDecodeWaves, nb_);
+                    const f32x16 gt = gram_of(sg, braw);
+                    float *dst = gsh + sg * 1024 + 4 * lane;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<float4 *>(dst + 256 * q) =
+                            make_float4(gt[4 * q], gt[4 * q + 1], gt[4 * q + 2], gt[4 * q + 3]);
+                }
+            }
+            __syncthreads();
+            for (int sg = 0; sg <= tau; ++sg) {
+                uint4 xr[XPL];
+#pragma unroll
+                for (int i = 0; i < XPL; ++i)
+                    xr[i] = nx_[i];
+                if (sg < tau)
+                    load_x(sg + 1, nx_);
+                const float *src = gsh + sg * 1024 + 4 * lane;
+                f32x16 gt;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + 256 * q);
+                    gt[4 * q] = v.x;
+                    gt[4 * q + 1] = v.y;
+                    gt[4 * q + 2] = v.z;
+                    gt[4 * q + 3] = v.w;
+                }
+                accumulate(sg, gt, xr);
+            }
+        } else {
+            // one block ahead of their use
+            uint4 nb_[NK], nx_[XPL];
+            load_b(0, nb_);
+            load_x(0, nx_);
+            for (int sg = 0; sg <= tau; ++sg) {
+                uint4 braw[NK], xr[XPL];
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk)
+                    braw[kk] = nb_[kk];
+#pragma unroll
+                for (int i = 0; i < XPL; ++i)
+                    xr[i] = nx_[i];
+                if (sg < tau) {
+                    load_b(sg + 1, nb_);
+                    load_x(sg + 1, nx_);
+                }
+                accumulate(sg, gram_of(sg, braw), xr);
+            }
         }
         // y for the draft rows of this t-block: fmaf(D, x, Y^T) -> bf16,
         // -0 -> +0; x_t is row t - 32 tau of the last x tile
@@ -1848,12 +1916,16 @@ hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
 template <int P, int N, class DT, bool PG>
 hipError_t verify_mfma(const ScanArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
-    const size_t bytes = (size_t)VLayout(Qp, P).bytes * kDecodeWaves;
-    hipError_t e = set_lds(k_verify_mfma<P, N, DT, PG>, bytes);
+    // per-wave areas, then the shared C.B^T blocks (32 x 32 fp32 each)
+    const bool gshare = (a.d.H / a.d.G) % kDecodeWaves == 0;
+    const size_t bytes = (size_t)VLayout(Qp, P).bytes * kDecodeWaves +
+                         (gshare ? (size_t)(Qp / 32) * 4096 : 0);
+    const auto kern = gshare ? k_verify_mfma<P, N, DT, PG, true> : k_verify_mfma<P, N, DT, PG, false>;
+    hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess)
         return e;
     const int HQ = (a.d.H + kDecodeWaves - 1) / kDecodeWaves;
-    k_verify_mfma<P, N, DT, PG><<<dim3(HQ * a.S), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+    kern<<<dim3(HQ * a.S), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     ScanArgs c = a;

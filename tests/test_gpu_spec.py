@@ -93,6 +93,8 @@ def check_cache(pr, cache, bnd_ss):
     (8, 2, 64, 128, 16, "bf16", 4, None),    # drafts cross chunk ends often
     (8, 2, 64, 128, 256, "bf16", 4, None),   # the RFC's chunk size
     (8, 2, 64, 128, 64, "bf16", 7, 16),      # paged buffers
+    (6, 3, 32, 64, 32, "bf16", 3, None),     # 2 heads per group: C.B^T per head; a half workgroup
+    (8, 1, 32, 32, 64, "bf16", 5, 16),       # C.B^T shared by a workgroup's heads; small tiles
     (4, 1, 16, 16, 16, "f32", 5, None),      # fp32-FMA engine
 ])
 def test_speculative_rounds_bitwise(H, G, P, N, Q, io, T, pt):
