@@ -91,6 +91,7 @@ struct DecodeArgs {
     int32_t *work;            // [2*slots+34]: arrival counters [slots], commit-list
                               // count and done counters [34], commit list [slots]
     BufMap bm;
+    const int32_t *order;     // or null: batch positions by rank, heaviest first
 };
 
 // Causal depthwise conv1d before the scan: prefill (S sequences of a varlen

@@ -902,10 +902,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
 //     time (wave_scan_segments).
 // The last workgroup of a slot to arrive advances buf_len / boundary_pos
 // (per-slot arrival counter). When the token filled the chunk, the
-// chunk-state update with the prefill's own chunk arithmetic follows: in
-// the same kernel (FUSED, each wave its head: decode_commit) for a batch
-// whose workgroups all run at once, else the last workgroup puts the slot
-// on a list and a second kernel (k_decode_commit) updates the listed slots.
+// chunk-state update with the prefill's own chunk arithmetic follows in the
+// same kernel (FUSED, each wave its head: decode_commit). A batch with more
+// workgroups than run at once is ranked first (k_decode_order: filling
+// slots, then the longest buffers), and its workgroups are dispatched in
+// rank order, so the heaviest start first rather than forming the launch's
+// tail. Only a batch longer than the slot count (positions outside the slot
+// range) takes the unfused form, where the last workgroup puts the slot on a
+// list and a second kernel (k_decode_commit) updates the listed slots.
 constexpr int kDecodeWaves = 4;
 
 // Workgroups of the chunk-commit kernel: as many as fit on the device at
@@ -1380,6 +1384,96 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
     }
 }
 
+// Ranking of a large batch before its decode launch: batch positions whose
+// token fills the chunk first (their workgroups also run the chunk-state
+// update), then by the number of 32-row s-blocks the replay walks, most
+// first; positions the decode skips last. A counting sort in one workgroup;
+// positions of one bin in any order (what a workgroup computes does not
+// depend on when it runs). The ranking goes to the commit-list area of the
+// work array (batch <= num_slots entries), which the decode launch then
+// reads and leaves zero.
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void k_decode_order(DecodeArgs a) {
+    constexpr int kBins = kMaxQ / 32 + 2;
+    constexpr int kHeld = 4;   // positions per thread whose bins stay in registers
+    __shared__ int count[kBins];
+    const int Q = a.d.Q;
+    int32_t *order = a.work + a.num_slots + kListHead;
+    auto bin_of = [&](int b) {
+        const int slot = a.slot_idx ? a.slot_idx[b] : b;
+        if (slot < 0 || slot >= a.num_slots)
+            return kBins - 1;
+        const int k = a.buf_len[slot];
+        if (k < 0 || k >= Q)
+            return kBins - 1;
+        return k + 1 == Q ? 0 : kMaxQ / 32 - (k >> 5);
+    };
+    if (threadIdx.x < kBins)
+        count[threadIdx.x] = 0;
+    int held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+        const int b = threadIdx.x + kOrderThreads * i;
+        held[i] = b < a.batch ? bin_of(b) : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        if (held[i] >= 0)
+            atomicAdd(&count[held[i]], 1);
+    for (int b = threadIdx.x + kOrderThreads * kHeld; b < a.batch; b += kOrderThreads)
+        atomicAdd(&count[bin_of(b)], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int at = 0;
+        for (int i = 0; i < kBins; ++i) {
+            const int n = count[i];
+            count[i] = at;   // first rank of bin i
+            at += n;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        if (held[i] >= 0)
+            order[atomicAdd(&count[held[i]], 1)] = threadIdx.x + kOrderThreads * i;
+    for (int b = threadIdx.x + kOrderThreads * kHeld; b < a.batch; b += kOrderThreads)
+        order[atomicAdd(&count[bin_of(b)], 1)] = b;
+}
+
+// End of a ranked decode launch: every workgroup counts itself out (in
+// kDoneGroups groups by blockIdx, then once per group, so that no counter
+// takes many atomics); the last one zeroes the ranking and the counters. All
+// other workgroups read their rank's entry before counting out.
+__device__ __forceinline__ void decode_order_done(const DecodeArgs &a) {
+    __shared__ int is_last;
+    int32_t *list = a.work + a.num_slots;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int last = 0;
+        const int W = gridDim.x;
+        const int grp = blockIdx.x % kDoneGroups;
+        const int members = (W - grp + kDoneGroups - 1) / kDoneGroups;
+        int32_t *sub = list + 2 + grp;
+        if (__hip_atomic_fetch_add(sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            members - 1) {
+            __hip_atomic_store(sub, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int groups = W < kDoneGroups ? W : kDoneGroups;
+            if (__hip_atomic_fetch_add(list + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                groups - 1) {
+                __hip_atomic_store(list + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = 1;
+            }
+        }
+        is_last = last;
+    }
+    __syncthreads();
+    if (is_last)
+        for (int i = threadIdx.x; i < a.batch; i += blockDim.x)
+            list[kListHead + i] = 0;
+}
+
 template <int P, int N, class DT, bool PG, bool FUSED>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_decode_mfma(DecodeArgs a) {
@@ -1387,22 +1481,52 @@ void k_decode_mfma(DecodeArgs a) {
     const int H = a.d.H, G = a.d.G, Q = a.d.Q;
     const int Qp = Q < 32 ? 32 : Q;
     const int HQ = (H + kDecodeWaves - 1) / kDecodeWaves;
-    // the workgroups of one slot run on one XCD (they share its B rows)
-    const int wid = xcd_local_index(blockIdx.x, gridDim.x);
-    const int b = wid / HQ;
+    // Workgroup -> (rank r, head quarter hq). Without a ranking, rank r is
+    // batch position r and the workgroups are renumbered so that those of
+    // one slot run on one XCD (they share its B rows). With one, they are
+    // taken in dispatch order: workgroup i runs on XCD i % 8 as that XCD's
+    // (i / 8)-th, so each XCD takes every eighth rank, in rank order, with a
+    // rank's workgroups together (rank i / HQ when the batch is not a
+    // multiple of 8).
+    int r, hq;
+    if (!a.order) {
+        const int wid = xcd_local_index(blockIdx.x, gridDim.x);
+        r = wid / HQ;
+        hq = wid % HQ;
+    } else if (a.batch % 8 == 0) {
+        const int j = blockIdx.x / 8;
+        r = (j / HQ) * 8 + blockIdx.x % 8;
+        hq = j % HQ;
+    } else {
+        r = blockIdx.x / HQ;
+        hq = blockIdx.x % HQ;
+    }
+    const int b = a.order ? a.order[r] : r;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int h = (wid % HQ) * kDecodeWaves + wave;
+    const int h = hq * kDecodeWaves + wave;
     const DLayout L(Qp, P, N, FUSED);
-    const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    if (slot < 0 || slot >= a.num_slots)
+    // nothing is done for a position outside the batch, or a slot, buffer
+    // length or page entry out of range (the same for the whole workgroup);
+    // a ranked launch still counts the workgroup out
+    const int slot = b < 0 || b >= a.batch ? -1 : a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0 || slot >= a.num_slots) {
+        if (a.order)
+            decode_order_done(a);
         return;
+    }
     const int k = a.buf_len[slot];
-    if (k < 0 || k >= Q)
+    if (k < 0 || k >= Q) {
+        if (a.order)
+            decode_order_done(a);
         return;
+    }
     // positions 0..k of the buffer are read or written
     const SlotRows<PG> rows(a.bm, slot, Q);
-    if (!rows.ok(a.bm, k + 1))
+    if (!rows.ok(a.bm, k + 1)) {
+        if (a.order)
+            decode_order_done(a);
         return;
+    }
     // the workgroup's heads share one B/C group: C.B^T is split between them
     const bool gshare = (H / G) % kDecodeWaves == 0;
     DecodeCarry<P, DT> cy;
@@ -1410,13 +1534,13 @@ void k_decode_mfma(DecodeArgs a) {
         decode_front<P, N, DT, PG, FUSED>(a, rows, b, slot, h, k, wave, gshare,
                                           lds_all + wave * L.bytes, L, cy);
     __syncthreads();  // C.B^T columns of every wave are in LDS
-    // Every wave of this workgroup has read buf_len (and used it) by now, so
-    // the workgroup counts itself in; the slot's last workgroup to arrive
-    // advances buf_len when it is done. The counter needs only atomicity, no
-    // ordering: no workgroup reads what the last one writes during this
-    // launch, and the launch boundary publishes the writes. (An
-    // acquire/release atomic here would write back and invalidate the L2 in
-    // every workgroup.)
+    // Every wave of this workgroup has read buf_len (and used it) by now,
+    // so the workgroup counts itself in; the slot's last workgroup to
+    // arrive advances buf_len when it is done. The counter needs only
+    // atomicity, no ordering: no workgroup reads what the last one writes
+    // during this launch, and the launch boundary publishes the writes.
+    // (An acquire/release atomic here would write back and invalidate the
+    // L2 in every workgroup.)
     int prev = 0;
     if (threadIdx.x == 0)
         prev = __hip_atomic_fetch_add(a.work + slot, 1, __ATOMIC_RELAXED,
@@ -1443,6 +1567,8 @@ void k_decode_mfma(DecodeArgs a) {
             list[kListHead + at] = slot;
         }
     }
+    if (a.order)
+        decode_order_done(a);
     (void)G;
 }
 
@@ -1873,15 +1999,27 @@ hipError_t decode_mfma(const DecodeArgs &a, hipStream_t stream) {
         return e;
     // A batch whose workgroups all run at once (three per compute unit) does
     // the chunk-state updates inside the decode launch: one launch per step,
-    // and no workgroup waits behind an updating one. A larger batch leaves
-    // them to k_decode_commit, so that the updates do not become the tail of
-    // the decode launch.
-    if ((int64_t)HQ * a.batch <= (int64_t)std::max(1, cus) * 3) {
+    // and no workgroup waits behind an updating one.
+    //
+    // A larger batch (with at most num_slots positions, the room the ranking
+    // has) is ranked first, heaviest workgroups first, and does the updates
+    // in the same launch too: the updating workgroups start first instead of
+    // becoming the launch's tail. Beyond that (only with positions outside
+    // the slot range) the updates are left to k_decode_commit.
+    const bool fits = (int64_t)HQ * a.batch <= (int64_t)std::max(1, cus) * 3;
+    if (fits || a.batch <= a.num_slots) {
+        DecodeArgs o = a;
+        if (!fits) {
+            k_decode_order<<<dim3(1), dim3(kOrderThreads), 0, stream>>>(a);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+            o.order = a.work + a.num_slots + kListHead;
+        }
         const size_t bytes = (size_t)DLayout(Qp, P, N, true).bytes * kDecodeWaves;
         if ((e = set_lds(k_decode_mfma<P, N, DT, PG, true>, bytes)) != hipSuccess)
             return e;
         k_decode_mfma<P, N, DT, PG, true>
-            <<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(a);
+            <<<dim3(HQ * a.batch), dim3(64 * kDecodeWaves), bytes, stream>>>(o);
         return hipGetLastError();
     }
     const size_t bytes = (size_t)DLayout(Qp, P, N, false).bytes * kDecodeWaves;

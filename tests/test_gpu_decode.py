@@ -215,6 +215,8 @@ def test_c3_batched_replay_decode_bitwise(Q):
     assert np.array_equal(bp, (lengths // Q) * Q)
     assert np.array_equal(cache.buf_len.cpu().numpy(), lengths % Q)
     assert same_bits(cache.state, bnd) and cache_consistent(cache)
+    # the ranked launches leave the bookkeeping array zero
+    assert not cache.work.any()
     # oracle parity on sampled sequences (decode rows and boundary state)
     from oracle import scan
     for s in (0, 131, 255):
@@ -237,12 +239,15 @@ def test_c3_replay_batch_invariance():
                            A, D, bias)
     it = torch.from_numpy((cu[:-1] + pre).astype(np.int64)).to(DEV)
     full = erd.ssd_replay_decode(shape, cache.clone(), x[it], dt[it], B[it], C[it], A, D, bias)
-    for sub in ([5], [17, 200, 3], list(range(0, 256, 7))):
+    # (101 slots: more workgroups than run at once, a batch that is not a
+    # multiple of 8)
+    for sub in ([5], [17, 200, 3], list(range(0, 256, 7)), list(range(255, 53, -2))):
         sl = torch.tensor(sub, dtype=torch.int32, device=DEV)
         c2 = cache.clone()
         ys = erd.ssd_replay_decode(shape, c2, x[it][sl.long()], dt[it][sl.long()],
                                    B[it][sl.long()], C[it][sl.long()], A, D, bias, slot_idx=sl)
         assert same_bits(ys, full[sl.long()])
+        assert not c2.work.any()
 
 
 def test_ssu_batch_invariance():
@@ -329,3 +334,35 @@ def test_cache_refresh_after_direct_state_write():
     assert cache_consistent(cache)
     yd = decode_tokens(pr.shape, cache, x, dt, B, C, pr.A, pr.D, pr.bias)
     assert same_bits(yd, y) and cache_consistent(cache)
+
+
+def test_large_batch_ranked_launch():
+    """4500 slots of a small shape (one workgroup per slot): the decode
+    launch ranks more positions than its ranking kernel holds in registers,
+    the batch is not a multiple of 8, and about one slot in 32 fills its
+    chunk per step. Four steps, every slot in a shuffled order, bit-identical to
+    the single-shot prefill; the bookkeeping array is left zero."""
+    S, H, G, P, N, Q, steps = 4500, 4, 1, 32, 32, 32, 4
+    shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    rng = np.random.default_rng(77)
+    pre = rng.integers(0, 100, S)
+    lengths = pre + steps
+    cu = synth.cu_seqlens(lengths)
+    x, dt, B, C = synth.make_tokens_torch(int(cu[-1]), H, G, P, N, 77, DEV)
+    hp = synth.make_head_params(H, 77)
+    A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    y_ss, _, bnd = erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias)
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    cache = erd.ReplayCache(shape, S, DEV)
+    erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip], C[ip],
+                           A, D, bias)
+    for k in range(steps):
+        perm = rng.permutation(S)
+        it = torch.from_numpy((cu[:-1] + pre + k)[perm].astype(np.int64)).to(DEV)
+        sl = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+        yd = erd.ssd_replay_decode(shape, cache, x[it], dt[it], B[it], C[it], A, D, bias,
+                                   slot_idx=sl)
+        assert same_bits(yd, y_ss[it]), k
+        assert not cache.work.any()
+    assert same_bits(cache.state, bnd) and cache_consistent(cache)
