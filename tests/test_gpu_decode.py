@@ -366,3 +366,45 @@ def test_large_batch_ranked_launch():
         assert same_bits(yd, y_ss[it]), k
         assert not cache.work.any()
     assert same_bits(cache.state, bnd) and cache_consistent(cache)
+
+
+def test_batch_longer_than_slot_count():
+    """Positions whose slot is outside [0, num_slots) are skipped (their
+    output rows are not written). A batch with more positions than slots
+    (here 1000 positions, 100 slots, more workgroups than run at once) takes
+    the unranked launch with the separate chunk-state update; the valid
+    positions' outputs and the caches equal the single-shot prefill's."""
+    S, nb, H, G, P, N, Q, steps = 100, 1000, 4, 1, 32, 32, 32, 40
+    shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    rng = np.random.default_rng(78)
+    pre = rng.integers(0, 70, S)
+    lengths = pre + steps
+    cu = synth.cu_seqlens(lengths)
+    x, dt, B, C = synth.make_tokens_torch(int(cu[-1]), H, G, P, N, 78, DEV)
+    hp = synth.make_head_params(H, 78)
+    A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    y_ss, _, bnd = erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias)
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    cache = erd.ReplayCache(shape, S, DEV)
+    erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip], C[ip],
+                           A, D, bias)
+    for k in range(steps):
+        order = rng.permutation(nb)
+        pos, rest = order[:S], order[S:]              # where the slots sit in the batch
+        slots = np.full(nb, -1, dtype=np.int32)
+        slots[rest[:300]] = -7                        # other out-of-range entries
+        slots[rest[300:600]] = S + 3
+        slots[pos] = np.arange(S, dtype=np.int32)
+        tok = np.zeros(nb, dtype=np.int64)            # skipped positions read token 0
+        tok[pos] = cu[:-1] + pre + k
+        it = torch.from_numpy(tok).to(DEV)
+        y = torch.full((nb, H, P), float("nan"), dtype=torch.bfloat16, device=DEV)
+        erd.ssd_replay_decode(shape, cache, x[it], dt[it], B[it], C[it], A, D, bias,
+                              slot_idx=torch.from_numpy(slots).to(DEV), y=y)
+        pv = torch.from_numpy(pos).to(DEV)
+        assert same_bits(y[pv], y_ss[it[pv]]), k
+        skipped = torch.ones(nb, dtype=torch.bool, device=DEV)
+        skipped[pv] = False
+        assert torch.isnan(y[skipped].float()).all()
+    assert same_bits(cache.state, bnd) and cache_consistent(cache)
