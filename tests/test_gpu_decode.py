@@ -408,3 +408,46 @@ def test_batch_longer_than_slot_count():
         skipped[pv] = False
         assert torch.isnan(y[skipped].float()).all()
     assert same_bits(cache.state, bnd) and cache_consistent(cache)
+
+
+def test_ranked_launch_with_skipped_positions():
+    """A ranked launch (more workgroups than run at once, batch <= slots)
+    whose batch holds out-of-range slot entries: their workgroups only count
+    themselves out, their output rows are not written, and the valid
+    positions equal the single-shot prefill bit for bit."""
+    S, nb, H, G, P, N, Q, steps = 1000, 900, 4, 1, 32, 32, 32, 6
+    shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    rng = np.random.default_rng(79)
+    pre = rng.integers(0, 70, S)
+    lengths = pre + steps
+    cu = synth.cu_seqlens(lengths)
+    x, dt, B, C = synth.make_tokens_torch(int(cu[-1]), H, G, P, N, 79, DEV)
+    hp = synth.make_head_params(H, 79)
+    A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    y_ss, _, _ = erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias)
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    cache = erd.ReplayCache(shape, S, DEV)
+    erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip], C[ip],
+                           A, D, bias)
+    live = rng.permutation(S)[:800]                   # slots decoded in these steps
+    for k in range(steps):
+        pos = rng.permutation(nb)
+        slots = np.full(nb, -1, dtype=np.int32)
+        slots[pos[800:850]] = S                       # other out-of-range entries
+        slots[pos[:800]] = live
+        tok = np.zeros(nb, dtype=np.int64)
+        tok[pos[:800]] = cu[live] + pre[live] + k
+        it = torch.from_numpy(tok).to(DEV)
+        y = torch.full((nb, H, P), float("nan"), dtype=torch.bfloat16, device=DEV)
+        erd.ssd_replay_decode(shape, cache, x[it], dt[it], B[it], C[it], A, D, bias,
+                              slot_idx=torch.from_numpy(slots).to(DEV), y=y)
+        pv = torch.from_numpy(pos[:800]).to(DEV)
+        assert same_bits(y[pv], y_ss[it[pv]]), k
+        skipped = torch.from_numpy(pos[800:]).to(DEV)
+        assert torch.isnan(y[skipped].float()).all()
+        assert not cache.work.any()
+    n = cache.buf_len.cpu().numpy()
+    assert np.array_equal(n[live], (pre[live] + steps) % Q)
+    rest = np.setdiff1d(np.arange(S), live)
+    assert np.array_equal(n[rest], pre[rest] % Q)
