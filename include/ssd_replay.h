@@ -101,10 +101,13 @@ typedef struct {
  *   work          [2*num_slots+34] int32   decode bookkeeping: per-slot
  *                                          arrival counters (the last
  *                                          workgroup of a slot advances
- *                                          buf_len) and the list of slots whose
- *                                          chunk filled in this step; zero
- *                                          before first use, and every call
- *                                          leaves it zero
+ *                                          buf_len), done counters, and a
+ *                                          list area: a large batch's
+ *                                          ranking (positions, heaviest
+ *                                          first) or the slots whose chunk
+ *                                          filled in this step; zero before
+ *                                          first use, and every call leaves
+ *                                          it zero
  * A fresh slot is all zeros. The struct itself is a host object; the
  * pointers in it are device pointers.
  *
@@ -230,7 +233,11 @@ int ssd_replay_prefill(const ssd_shape *shape, const ssd_replay_cache *cache,
  * the boundary state, buf_len returns to 0 and boundary_pos advances by Q.
  * y[b] is bit-identical to the row a single ssd_prefill_varlen over the
  * whole sequence produces. Inputs x[batch,H,P], dt[batch,H],
- * B/C[batch,G,N]; y[batch,H,P]. Slots must be distinct. */
+ * B/C[batch,G,N]; y[batch,H,P]. Slots must be distinct; a position whose
+ * slot_idx entry is outside [0, num_slots) is skipped (its y row is not
+ * written). One launch, or two for a batch with more workgroups than the
+ * device runs at once (a ranking of the positions, heaviest first, goes
+ * ahead of the step); no host synchronisation either way. */
 int ssd_replay_decode(const ssd_shape *shape, const ssd_replay_cache *cache,
                       int32_t batch, const int32_t *slot_idx, const void *x,
                       const void *dt, const void *B, const void *C,
