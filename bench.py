@@ -201,8 +201,9 @@ GROUPED_PACK, GROUPED_COPIES = (600, 300, 900, 248), 64
 
 
 def other_workloads(erd, synth, torch, dev, warmup, steps):
-    """The survey's other measurement workloads, each timed with HIP events on
-    the launch stream after its own warm-up:
+    """Further measurement workloads (a latency case, grouped heads and a
+    layer stack), each timed with HIP events on the launch stream after its
+    own warm-up:
       - prefill latency of one 2048-token sequence (H=32, G=1, P=64, N=128,
         chunk 256; launch-bound: 32 workgroups);
       - prefill throughput of the grouped-heads pack {600, 300, 900, 248} x 64
