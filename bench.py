@@ -17,6 +17,10 @@ Counter runs: `--prefill-only` launches only the prefill (W + K times) and
 then one plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE readings
 scale the prefill's; `--traffic FETCH.csv WRITE.csv` turns the two rocprofv3
 counter files into profiles/prefill_w1b_traffic.json (no GPU needed).
+`--decode-only` does the same for the exact-replay decode at B=256, chunk 256
+((W + K) x R steps), and `--decode-traffic FETCH.csv WRITE.csv` writes
+profiles/decode_b256_q256_traffic.json: each decode dispatch's counted bytes
+against its algorithmic bytes (the buffer fills of every step are known).
 """
 from __future__ import annotations
 
@@ -150,6 +154,7 @@ def load_traffic(sha):
 CALIB_BYTES = 512 * 2 ** 20
 PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16, false>"
 COPY_KERNEL = "copyBuffer"
+DECODE_KERNEL = "k_decode_mfma<64, 128, ssd::IoBF16, false, true>"
 
 
 def counter_means(path, counter):
@@ -194,6 +199,62 @@ def write_traffic(fetch_csv, write_csv, cmds):
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
+
+
+def decode_counters(path, counter):
+    """Per-dispatch values of one counter for the decode kernel (in dispatch
+    order) and the calibration copy's reading, from a rocprofv3
+    *_counter_collection.csv file of a --decode-only run."""
+    dec, copy = [], []
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            if DECODE_KERNEL in name:
+                dec.append((int(row["Dispatch_Id"]), float(row["Counter_Value"])))
+            elif COPY_KERNEL in name:
+                copy.append(float(row["Counter_Value"]))
+    if not dec or not copy:
+        raise SystemExit(f"{path}: no {counter} rows for the decode kernel and the copy")
+    return [v for _, v in sorted(dec)], max(copy)
+
+
+def write_decode_traffic(fetch_csv, write_csv, cmds):
+    S, H, G, P, N, Q = 256, 32, 1, 64, 128, 256
+    from exact_replay_decode_amd import synth   # seeded inputs only (no GPU)
+    f, fc = decode_counters(fetch_csv, "FETCH_SIZE")
+    w, wc = decode_counters(write_csv, "WRITE_SIZE")
+    if len(f) != len(w):
+        raise SystemExit("the two counter runs hold different numbers of decode dispatches")
+    ff = CALIB_BYTES / 1024 / fc
+    wf = CALIB_BYTES / 1024 / wc
+    k0 = synth.replay_prefix_lengths(S, Q, 1) % Q
+    alg = np.array([replay_step_bytes((k0 + i) % Q, Q, H, G, P, N) for i in range(len(f))],
+                   dtype=np.float64)
+    traffic = 1024 * (np.array(f) * ff + np.array(w) * wf)
+    fills = np.array([int(np.sum((k0 + i) % Q == Q - 1)) for i in range(len(f))])
+    rec = {
+        "what": "HBM traffic of the exact-replay decode kernel, B=256 (H=32, G=1, P=64, N=128, "
+                "chunk 256, bf16 I/O, fp32 state), buffers holding 0..255 tokens, kernel "
+                + DECODE_KERNEL + " (the chunk-state update of the filling slots inside)",
+        "commands": cmds,
+        "dispatches": len(f),
+        "fetch_kib_per_dispatch_mean": float(np.mean(f)),
+        "write_kib_per_dispatch_mean": float(np.mean(w)),
+        "copy_calibration": {"bytes": CALIB_BYTES, "fetch_kib": fc, "write_kib": wc,
+                             "fetch_factor": ff, "write_factor": wf},
+        "traffic_bytes_per_dispatch_mean": float(traffic.mean()),
+        "algorithmic_bytes_per_dispatch_mean": float(alg.mean()),
+        "traffic_over_algorithmic": float(traffic.sum() / alg.sum()),
+        "traffic_over_algorithmic_without_fill": float(
+            traffic[fills == 0].sum() / alg[fills == 0].sum()) if (fills == 0).any() else None,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    out = os.path.join(ROOT, "profiles", "decode_b256_q256_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 STACK_LAYERS = 24            # layer-stack leg: layers, prompt, decode steps, chunk calls
 STACK_PROMPT, STACK_STEPS, STACK_CHUNK, STACK_CHUNKS = 600, 32, 100, 9
@@ -357,7 +418,18 @@ def main():
                     help="only the prefill launches, then one 512 MiB calibration copy")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter files")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the B=256 chunk-256 decode steps, then the calibration copy")
+    ap.add_argument("--decode-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the decode traffic summary from two rocprofv3 counter files")
     args = ap.parse_args()
+    if args.decode_traffic:
+        cmds = [f"cd /tmp && rocprofv3 --pmc {c} -f csv -d <out> -o run -- python3 "
+                f"<repo>/bench.py --decode-only --steps 2 --warmup 1"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds.append("python3 bench.py --decode-traffic <fetch counter csv> <write counter csv>")
+        write_decode_traffic(*args.decode_traffic, cmds)
+        return
     if args.traffic:
         cmds = [f"cd /tmp && rocprofv3 --pmc {c} -f csv -d <out> -o run -- python3 "
                 f"<repo>/bench.py --prefill-only --steps 1 --warmup 1"
@@ -446,6 +518,26 @@ def main():
     planpg = erd.DecodePlan(shape, S, A, D, bias, cache=cachepg)
     plan_ssu = erd.DecodePlan(shape, S, A, D, bias, state=ssu_state)
     plan256.check(dx[0], ddt[0], dB[0], dC[0], ydec)
+    if args.decode_only:
+        # decode dispatch i sees buffer fills (pre % Q + i) % Q
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(total_decode):
+            plan256(dx[k], ddt[k], dB[k], dC[k], ydec)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        calib_dst = torch.empty_like(calib_src)
+        torch.cuda.synchronize()
+        calib_dst.copy_(calib_src)
+        torch.cuda.synchronize()
+        print(json.dumps({"decode_steps": total_decode,
+                          "decode_avg_step_us": 1e3 * e0.elapsed_time(e1) / total_decode,
+                          "calibration_copy_bytes": CALIB_BYTES,
+                          "kernel_source_sha": kernel_source_sha()}), flush=True)
+        return
 
     # conv before the scan (width CONV_W over x | B | C): prefill over the
     # same 256 x 2048 pack, decode steps at B=256
