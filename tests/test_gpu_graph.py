@@ -5,7 +5,9 @@ and the outputs copied out (eager work between replays, so a replay that
 reused stale values would show). The cache keeps buf_len on the device, so
 nothing on the host changes from step to step. Every step's outputs and the
 final caches equal the eager run bit for bit; with chunk 16 every slot
-crosses chunk ends, so the commit kernel runs inside the graph too."""
+crosses chunk ends, so the chunk-state update runs inside the graph too.
+With 200 slots (more workgroups than run at once) each captured step is the
+ranking launch followed by the ranked decode launch."""
 import pytest
 import torch
 
@@ -16,8 +18,10 @@ from gpu_cases import DEV, same_bits
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_steps_replayed_from_a_graph():
-    L, S, H, G, P, N, Q, steps = 3, 8, 8, 2, 64, 128, 16, 40
+@pytest.mark.parametrize("S,H", [(8, 8),      # all workgroups at once: one launch per step
+                                 (200, 16)])  # ranked: a ranking launch, then the step
+def test_decode_steps_replayed_from_a_graph(S, H):
+    L, G, P, N, Q, steps = 3, 2, 64, 128, 16, 40
     sh = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
     pre = [5 + 3 * s for s in range(S)]          # buffers at different offsets
     layers = []
