@@ -77,13 +77,15 @@ __device__ __forceinline__ int seq_len(const int32_t *cu, const int32_t *take, i
 
 // ---- scalar functions that fix the rounding ------------------------------
 
-// delta = softplus(dt + bias) computed as log1p(exp(u)) for u <= 0 and
-// u + log1p(exp(-u)) otherwise; or dt + bias when softplus is off.
+// delta = softplus(dt + bias) = max(u, 0) + log1p(exp(-|u|)): log1p(exp(u))
+// for u <= 0 (plus +0, which changes no value here) and u + log1p(exp(-u))
+// otherwise, with one exp/log1p evaluation for both signs; or dt + bias
+// when softplus is off.
 __device__ __forceinline__ float delta_of(float dt_raw, float bias, int softplus) {
     const float u = dt_raw + bias;
     if (!softplus)
         return u;
-    return u <= 0.0f ? log1pf(expf(u)) : u + log1pf(expf(-u));
+    return fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u)));
 }
 
 // exp(v) for the decay factors, v <= 0 up to rounding: one v_exp_f32 (2^x)
