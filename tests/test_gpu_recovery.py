@@ -40,7 +40,8 @@ def test_multi_token_update_equals_single_steps(cache, io):
     sh = shape_with_state(pr, cache)
     x, dt, B, C = pr.dev(None)
     S = len(lengths)
-    st0 = torch.randn((S + 2, 8, P, N), device=DEV).to(SDT[cache])
+    st0 = torch.randn((S + 2, 8, P, N), device=DEV,
+                      generator=torch.Generator(device=DEV).manual_seed(13)).to(SDT[cache])
     sl = torch.tensor([3, 0, 6, 1, 5], dtype=torch.int32, device=DEV)
     st_multi = st0.clone()
     y_multi = erd.ssm_state_update_varlen(sh, st_multi, pr.cu, x, dt, B, C, pr.A, pr.D,
@@ -113,7 +114,8 @@ def test_multi_token_update_matches_oracle(cache):
     pr = make_problem(lengths, H=4, G=2, P=64, N=128, Q=16, seed=14)
     sh = shape_with_state(pr, cache)
     x, dt, B, C = pr.dev(None)
-    st0 = torch.randn((3, 4, 64, 128), device=DEV).to(SDT[cache])
+    st0 = torch.randn((3, 4, 64, 128), device=DEV,
+                      generator=torch.Generator(device=DEV).manual_seed(14)).to(SDT[cache])
     st = st0.clone()
     y = erd.ssm_state_update_varlen(sh, st, pr.cu, x, dt, B, C, pr.A, pr.D, pr.bias)
     xs, dts, Bs, Cs = pr.tok.f64()
@@ -126,9 +128,14 @@ def test_multi_token_update_matches_oracle(cache):
                      init=h0)
         assert headwise_max_rel(st.cpu().numpy(), exact.final_state) <= 1e-4
     else:
+        # both sides round the state to bf16 after every token; where the
+        # fp32 and fp64 values straddle a rounding boundary they land one
+        # bf16 ulp (2^-8 of the element) apart and later tokens carry the
+        # difference. Over random initial states the worst head of this case
+        # reached 4.8 ulps of its largest element: bound 8.
         d = np.abs(erd.to_f64(st) - ref_h).reshape(3, 4, -1).max(-1)
         m = np.abs(ref_h).reshape(3, 4, -1).max(-1)
-        assert np.all(d <= 4 * 2.0 ** -8 * m)
+        assert np.all(d <= 8 * 2.0 ** -8 * m)
 
 
 def test_recurrent_error_levels_printed_by_the_rfc():
