@@ -336,13 +336,17 @@ def test_cache_refresh_after_direct_state_write():
     assert same_bits(yd, y) and cache_consistent(cache)
 
 
-def test_large_batch_ranked_launch():
-    """4500 slots of a small shape (one workgroup per slot): the decode
-    launch ranks more positions than its ranking kernel holds in registers,
-    the batch is not a multiple of 8, and about one slot in 32 fills its
-    chunk per step. Four steps, every slot in a shuffled order, bit-identical to
-    the single-shot prefill; the bookkeeping array is left zero."""
-    S, H, G, P, N, Q, steps = 4500, 4, 1, 32, 32, 32, 4
+@pytest.mark.parametrize("S,H,G,P,N", [(4500, 4, 1, 32, 32),   # one workgroup per slot
+                                       (500, 6, 3, 32, 64)])   # 2 heads per group, half workgroups
+def test_large_batch_ranked_launch(S, H, G, P, N):
+    """Ranked launches of small shapes: 4500 slots (more positions than the
+    ranking kernel holds in registers) and 500 slots of 6 heads (two per
+    group: per-head C.B^T and chunk-state update, the second workgroup of a
+    slot half empty); neither batch is a multiple of 8, and about one slot in
+    32 fills its chunk per step. Four steps, every slot in a shuffled order,
+    bit-identical to the single-shot prefill; the bookkeeping array is left
+    zero."""
+    Q, steps = 32, 4
     shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
     rng = np.random.default_rng(77)
     pre = rng.integers(0, 100, S)
