@@ -176,7 +176,7 @@ def counter_means(path, counter):
     return {"prefill": sum(vals["prefill"]) / len(vals["prefill"]), "copy": max(vals["copy"])}
 
 
-def write_traffic(fetch_csv, write_csv, cmds):
+def write_traffic(fetch_csv, write_csv, cmds, out=None):
     S, T, H, G, P, N = 256, 2048, 32, 1, 64, 128
     f = counter_means(fetch_csv, "FETCH_SIZE")
     w = counter_means(write_csv, "WRITE_SIZE")
@@ -194,10 +194,11 @@ def write_traffic(fetch_csv, write_csv, cmds):
         "algorithmic_bytes_per_launch": prefill_bytes(S * T, S, H, G, P, N),
         "kernel_source_sha": kernel_source_sha(),
     }
-    out = os.path.join(ROOT, "profiles", "prefill_w1b_traffic.json")
+    out = out or os.path.join(ROOT, "profiles", "prefill_w1b_traffic.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+    return rec
 
 
 
@@ -220,7 +221,7 @@ def decode_counters(path, counter):
     return [v for _, v in sorted(dec)], max(copy)
 
 
-def write_decode_traffic(fetch_csv, write_csv, cmds):
+def write_decode_traffic(fetch_csv, write_csv, cmds, out=None):
     S, H, G, P, N, Q = 256, 32, 1, 64, 128, 256
     from exact_replay_decode_amd import synth   # seeded inputs only (no GPU)
     f, fc = decode_counters(fetch_csv, "FETCH_SIZE")
@@ -251,10 +252,11 @@ def write_decode_traffic(fetch_csv, write_csv, cmds):
             traffic[fills == 0].sum() / alg[fills == 0].sum()) if (fills == 0).any() else None,
         "kernel_source_sha": kernel_source_sha(),
     }
-    out = os.path.join(ROOT, "profiles", "decode_b256_q256_traffic.json")
+    out = out or os.path.join(ROOT, "profiles", "decode_b256_q256_traffic.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+    return rec
 
 STACK_LAYERS = 24            # layer-stack leg: layers, prompt, decode steps, chunk calls
 STACK_PROMPT, STACK_STEPS, STACK_CHUNK, STACK_CHUNKS = 600, 32, 100, 9
