@@ -8,5 +8,6 @@ from .api import (Shape, ReplayCache, DecodePlan, ConvUpdatePlan, ssd_prefill_va
                   ssd_replay_prefill, ssd_replay_decode, ssm_state_update,
                   ssd_replay_verify, ssd_replay_accept, ssm_state_update_varlen,
                   ssd_replay_cache_bytes, ssd_replay_page_bytes, ssd_conv1d_varlen,
-                  ssd_conv1d_update, conv_dim, to_device, to_f64)
+                  ssd_conv1d_update, ssd_prefill_chunk_count, conv_dim, to_device,
+                  to_f64)
 from ._lib import SsdError, load as load_library  # noqa: F401

@@ -24,7 +24,8 @@ EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace
            "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
-           "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen")
+           "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen",
+           "ssd_prefill_chunk_count")
 
 
 class ssd_shape(ctypes.Structure):
@@ -68,7 +69,9 @@ def load() -> ctypes.CDLL:
     lib.ssd_prefill_workspace_bytes.argtypes = [shp, i32, i64]
     lib.ssd_prefill_varlen.restype = ctypes.c_int
     lib.ssd_prefill_varlen.argtypes = [shp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, vp, vp, vp, sz, vp]
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_prefill_chunk_count.restype = i64
+    lib.ssd_prefill_chunk_count.argtypes = [i32, vp, i32]
     lib.ssd_replay_page_bytes.restype = sz
     lib.ssd_replay_page_bytes.argtypes = [shp, i32, i32]
     lib.ssd_replay_cache_refresh.restype = ctypes.c_int

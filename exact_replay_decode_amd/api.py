@@ -211,11 +211,25 @@ def _slots(slot_idx, n, device):
     return _need(slot_idx, "slot_idx", (n,), torch.int32, device)
 
 
+def ssd_prefill_chunk_count(cu_seqlens_host, chunk_size: int) -> int:
+    """Rows of the prefill's chunk_states for a pack: its full chunks."""
+    host = np.ascontiguousarray(np.asarray(cu_seqlens_host), dtype=np.int32)
+    n = int(_lib.load().ssd_prefill_chunk_count(host.size - 1,
+                                                host.ctypes.data_as(ctypes.c_void_p),
+                                                int(chunk_size)))
+    if n < 0:
+        raise ValueError("ssd_prefill_chunk_count: bad cu_seqlens or chunk size")
+    return n
+
+
 def ssd_prefill_varlen(shape: Shape, cu_seqlens, x, dt, A, B, C, D=None, dt_bias=None,
                        init_state=None, y=None, final_state=None, boundary_state=None,
-                       cu_seqlens_host=None, want_final=True, want_boundary=True, stream=None):
+                       cu_seqlens_host=None, want_final=True, want_boundary=True, stream=None,
+                       chunk_states=None, want_chunk_states=False):
     """Chunked scan of a varlen pack from init_state (None = zeros).
-    Returns (y, final_state, boundary_state)."""
+    Returns (y, final_state, boundary_state), and chunk_states as a fourth
+    item with want_chunk_states (allocated unless passed: [F, H, P, N], the
+    state after each full chunk of each sequence, sequences in order)."""
     dev = x.device
     H, G, P, N = shape.H, shape.G, shape.P, shape.N
     host, cu = _cu_pair(cu_seqlens, cu_seqlens_host, dev)
@@ -236,12 +250,19 @@ def ssd_prefill_varlen(shape: Shape, cu_seqlens, x, dt, A, B, C, D=None, dt_bias
         boundary_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
     _opt(final_state, "final_state", (S, H, P, N), torch.float32, dev)
     _opt(boundary_state, "boundary_state", (S, H, P, N), torch.float32, dev)
+    if chunk_states is not None or want_chunk_states:
+        F = ssd_prefill_chunk_count(host, shape.chunk_size)
+        if chunk_states is None:
+            chunk_states = torch.empty((F, H, P, N), dtype=torch.float32, device=dev)
+        _need(chunk_states, "chunk_states", (F, H, P, N), torch.float32, dev)
     sh = shape.c()
     rc = _lib.load().ssd_prefill_varlen(
         ctypes.byref(sh), S, T, host.ctypes.data_as(ctypes.c_void_p), _ptr(cu), _ptr(x),
         _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(init_state), _ptr(y),
-        _ptr(final_state), _ptr(boundary_state), None, 0, _stream(stream))
+        _ptr(final_state), _ptr(boundary_state), _ptr(chunk_states), None, 0, _stream(stream))
     _lib.check(rc, "ssd_prefill_varlen")
+    if want_chunk_states:
+        return y, final_state, boundary_state, chunk_states
     return y, final_state, boundary_state
 
 

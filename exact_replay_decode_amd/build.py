@@ -29,11 +29,12 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-I", INCLUDE, "-I", CSRC,
-           *DEVICE_FLAGS, "-x", "hip", *sources(), "-o", tmp]
+OBJDIR = os.path.join(HERE, "_build")
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+          "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,6 +44,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (one hipcc process per file, in parallel), then
+    link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(src) + ".o") for src in sources()]
+    cmds = [[HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", src,
+             "-o", obj] for src, obj in zip(sources(), objs)]
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <vector>
 
 #include "ssd_internal.hpp"
 
@@ -110,6 +111,33 @@ ssd::BufMap buf_map(const ssd_replay_cache *c) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// Debug builds (SSD_DEBUG_CHECKS) also check that the slot_idx entries of a
+// call that lie in [0, num_slots) are distinct: every kernel reads and writes
+// a slot from one place per call, so a repeated slot is undefined behaviour
+// the release build does not look for (it would need the device array on
+// the host, a synchronising copy). Entries outside the range are the
+// skipped positions some calls allow. Returns SSD_ERR_SHAPE on a repeat.
+#ifdef SSD_DEBUG_CHECKS
+int check_slots_distinct(const int32_t *slot_idx, int32_t n, int32_t num_slots) {
+    if (!slot_idx || n <= 0 || num_slots <= 0)
+        return SSD_OK;
+    std::vector<int32_t> h((size_t)n);
+    if (ssd::copy_to_host(h.data(), slot_idx, sizeof(int32_t) * (size_t)n) != hipSuccess)
+        return SSD_ERR_HIP;
+    std::vector<char> seen((size_t)num_slots, 0);
+    for (int32_t v : h) {
+        if (v < 0 || v >= num_slots)
+            continue;
+        if (seen[(size_t)v])
+            return SSD_ERR_SHAPE;
+        seen[(size_t)v] = 1;
+    }
+    return SSD_OK;
+}
+#else
+int check_slots_distinct(const int32_t *, int32_t, int32_t) { return SSD_OK; }
+#endif
+
 // One engine per shape, so prefill and decode of a shape always share the
 // same chunk arithmetic.
 hipError_t launch_scan_any(const ssd::ScanArgs &a, hipStream_t stream) {
@@ -153,6 +181,8 @@ int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, i
         return SSD_ERR_NULL;
     if (!all_a16(x, B, C, y))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, S, cache->num_slots)) != SSD_OK)
+        return st;
     ssd::ScanArgs a = {};
     a.d = d;
     a.S = S;
@@ -265,8 +295,8 @@ int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t 
                        const int32_t *cu, const void *x, const void *dt, const float *A,
                        const void *B, const void *C, const float *D, const float *dt_bias,
                        const float *init_state, void *y, float *final_state,
-                       float *boundary_state, void *workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       float *boundary_state, float *chunk_states, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
     Dims d;
     int st = check_shape(sh, &d);
     if (st != SSD_OK)
@@ -280,7 +310,7 @@ int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t 
         return SSD_OK;
     if (!A || (T > 0 && (!x || !dt || !B || !C || !y)))
         return SSD_ERR_NULL;
-    if (!all_a16(x, B, C, y, init_state, final_state, boundary_state))
+    if (!all_a16(x, B, C, y, init_state, final_state, boundary_state, chunk_states))
         return SSD_ERR_ALIGN;
     ssd::ScanArgs a = {};
     a.d = d;
@@ -293,8 +323,21 @@ int ssd_prefill_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int32_t 
     a.init_state = init_state;
     a.final_state = final_state;
     a.boundary_state = boundary_state;
+    a.chunk_states = chunk_states;
     a.replay = 0;
     return hip_status(launch_scan_any(a, (hipStream_t)stream));
+}
+
+int64_t ssd_prefill_chunk_count(int32_t S, const int32_t *cu_host, int32_t Q) {
+    if (!cu_host || S < 0 || Q < 1)
+        return -1;
+    int64_t n = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        if (cu_host[s + 1] < cu_host[s])
+            return -1;
+        n += (cu_host[s + 1] - cu_host[s]) / Q;
+    }
+    return n;
 }
 
 int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t *cu_host,
@@ -318,6 +361,8 @@ int ssd_commit_boundary(const ssd_shape *sh, int32_t S, int64_t T, const int32_t
         return SSD_ERR_NULL;
     if (!all_a16(x, B, C, boundary_state))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, S, cache->num_slots)) != SSD_OK)
+        return st;
     ssd::CommitArgs a = {};
     a.d = d;
     a.S = S;
@@ -382,6 +427,8 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
         return SSD_ERR_NULL;
     if (!all_a16(x, B, C, y))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, batch, cache->num_slots)) != SSD_OK)
+        return st;
     ssd::DecodeArgs a = {};
     a.d = d;
     a.batch = batch;
@@ -422,6 +469,8 @@ int ssd_conv1d_varlen(const ssd_shape *sh, int32_t W, int32_t act, int32_t S, in
         return SSD_ERR_NULL;
     if (!all_a16(xBC, conv_state, x, B, C) || !all_a16(weight, bias))
         return SSD_ERR_ALIGN;
+    if (conv_state && (st = check_slots_distinct(slot_idx, S, num_slots)) != SSD_OK)
+        return st;
     int32_t maxlen = 0;
     for (int32_t s = 0; s < S; ++s)
         maxlen = std::max(maxlen, cu_host[s + 1] - cu_host[s]);
@@ -458,6 +507,8 @@ int ssd_conv1d_update(const ssd_shape *sh, int32_t W, int32_t act, int32_t batch
         return SSD_ERR_NULL;
     if (!all_a16(xBC, conv_state, x, B, C) || !all_a16(weight, bias))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, batch, num_slots)) != SSD_OK)
+        return st;
     ssd::ConvArgs a = {};
     a.d = d;
     a.W = W;
@@ -488,6 +539,8 @@ int ssm_state_update(const ssd_shape *sh, int32_t batch, int32_t num_slots,
         return SSD_ERR_NULL;
     if (!all_a16(state, x, B, C, y))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, batch, num_slots)) != SSD_OK)
+        return st;
     ssd::SsuArgs a = {};
     a.d = d;
     a.batch = batch;
@@ -520,6 +573,8 @@ int ssm_state_update_varlen(const ssd_shape *sh, int32_t S, int64_t T, const int
         return SSD_ERR_NULL;
     if (!all_a16(state, x, B, C, y))
         return SSD_ERR_ALIGN;
+    if ((st = check_slots_distinct(slot_idx, S, num_slots)) != SSD_OK)
+        return st;
     ssd::SsuArgs a = {};
     a.d = d;
     a.batch = S;

@@ -75,6 +75,28 @@ __device__ __forceinline__ int seq_len(const int32_t *cu, const int32_t *take, i
     return t < 0 ? 0 : (t < len ? t : len);
 }
 
+// Row of sequence s's first full chunk in a packed array of chunk-end
+// states: the full chunks (floor(len / Q)) of sequences 0..s-1. Every thread
+// of the workgroup calls it (blockDim.x a multiple of 64); red is one int of
+// LDS per wave, free on entry and on return.
+__device__ __forceinline__ int full_chunks_before(const int32_t *cu, int s, int Q, int *red) {
+    int v = 0;
+    for (int i = threadIdx.x; i < s; i += blockDim.x)
+        v += (cu[i + 1] - cu[i]) / Q;
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    const int nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int tot = 0;
+    for (int w = 0; w < nw; ++w)
+        tot += red[w];
+    __syncthreads();
+    return tot;
+}
+
 // ---- scalar functions that fix the rounding ------------------------------
 
 // delta = softplus(dt + bias) = max(u, 0) + log1p(exp(-|u|)): log1p(exp(u))

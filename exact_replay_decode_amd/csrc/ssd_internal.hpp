@@ -38,6 +38,7 @@ struct ScanArgs {
     const float *init_state;  // [S,H,P,N] or null
     float *final_state;       // [S,H,P,N] or null
     float *boundary_state;    // [S,H,P,N] or null
+    float *chunk_states;      // [full chunks,H,P,N] or null: state after each full chunk
     // replay mode (replay != 0): resume from the slot's boundary + buffer
     int32_t replay;
     int32_t num_slots;
@@ -142,6 +143,8 @@ hipError_t launch_conv_update(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+// synchronous device -> host copy (debug-build argument checks only)
+hipError_t copy_to_host(void *dst, const void *src, size_t bytes);
 // bf16 copy of `heads` fp32 [P][N] states (the cache's read-out operand)
 hipError_t launch_refresh_state_bf(const float *state, void *state_bf, int64_t heads, int P, int N,
                                    hipStream_t stream);

@@ -773,6 +773,13 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
                                 : nullptr;
     const bool write_bnd = bnd && (!a.replay || nfull > 0) && !a.dry;
     uint16_t *y = static_cast<uint16_t *>(a.y);
+    // chunk-end states of the full chunks (plain prefill): rows from
+    // full_chunks_before(s) on
+    float *cst = nullptr;
+    if (!a.replay && a.chunk_states)
+        cst = a.chunk_states +
+              ((int64_t)full_chunks_before(a.cu, s, Q, reinterpret_cast<int *>(lds + L.tot)) * H +
+               h) * PN;
     const int tau = wave_tblock(Qp / 32, wave);
     auto set_chunk = [&](int c) {
         v.nb = (c == 0) ? nbuf : 0;
@@ -789,6 +796,8 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
         const bool mirror = c == nfull && write_bnd && bnd_bf;
         if (c == nfull && write_bnd)
             state_io<P, N, NW, false>(bnd, S);
+        if (cst && c >= 1 && c <= nfull)   // S is the state after full chunk c - 1
+            state_io<P, N, NW, false>(cst + (int64_t)(c - 1) * H * PN, S);
         set_chunk(c);
         const int n_valid = v.n_valid;
         const bool upd = n_valid == Q || (!a.replay && a.final_state);
@@ -822,6 +831,8 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             state_to_lds<P, N, NW>(lds, L, S);
         }
     }
+    if (cst && nfull == nchunks && nfull > 0)
+        state_io<P, N, NW, false>(cst + (int64_t)(nfull - 1) * H * PN, S);
     if (nfull == nchunks && write_bnd) {
         state_io<P, N, NW, false>(bnd, S);
         if (bnd_bf) {

@@ -338,10 +338,18 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
                                 : nullptr;
     const bool write_bnd = bnd && (!a.replay || nfull > 0) && !a.dry;
     T *y = static_cast<T *>(a.y);
+    // chunk-end states of the full chunks (plain prefill)
+    float *cst = nullptr;
+    if (!a.replay && a.chunk_states)
+        cst = a.chunk_states +
+              ((int64_t)full_chunks_before(a.cu, s, Q, reinterpret_cast<int *>(lds + L.tot)) * H +
+               h) * PN;
 
     for (int c = 0; c < nchunks; ++c) {
         if (c == nfull && write_bnd)
             state_store(bnd, lds + L.S, P, N, bnd_bf);
+        if (cst && c >= 1 && c <= nfull)   // the state after full chunk c - 1
+            state_store(cst + (int64_t)(c - 1) * H * PN, lds + L.S, P, N);
         v.nb = (c == 0) ? nbuf : 0;
         v.n_valid = min(Q, total - c * Q);
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
@@ -351,6 +359,8 @@ __global__ __launch_bounds__(kBlock) void k_scan(ScanArgs a) {
         if (v.n_valid == Q || (!a.replay && a.final_state))
             chunk_state_update(v, lds, L);
     }
+    if (cst && nfull == nchunks && nfull > 0)
+        state_store(cst + (int64_t)(nfull - 1) * H * PN, lds + L.S, P, N);
     if (nfull == nchunks && write_bnd)
         state_store(bnd, lds + L.S, P, N, bnd_bf);
     if (!a.replay && a.final_state)
@@ -945,6 +955,9 @@ hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) { return dispatch<DecodeF>(a, stream); }
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream) { return dispatch<CommitF>(a, stream); }
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream) { return dispatch<SsuF>(a, stream); }
+hipError_t copy_to_host(void *dst, const void *src, size_t bytes) {
+    return hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+}
 hipError_t launch_refresh_state_bf(const float *state, void *state_bf, int64_t heads, int P, int N,
                                    hipStream_t stream) {
     if (heads <= 0)

@@ -182,6 +182,15 @@ size_t ssd_prefill_workspace_bytes(const ssd_shape *shape, int32_t num_seqs,
  *   boundary_state [S,H,P,N] state after the last full chunk, i.e. after
  *                  len - len % Q tokens; init_state when len < Q (NULL = not
  *                  stored)
+ *   chunk_states   [F,H,P,N] the intermediate states ([RFC] section 3,
+ *                  prefill bullet: the boundary is taken from the state at
+ *                  the end of the last full chunk, as prefix caching takes
+ *                  its block states): row off(s) + c holds the state after
+ *                  (c + 1) * Q tokens of sequence s, for every full chunk
+ *                  c < len_s / Q, where off(s) = sum over s' < s of
+ *                  floor(len_s' / Q) and F = off(S)
+ *                  (ssd_prefill_chunk_count). Bit-identical to the state the
+ *                  same tokens leave in boundary_state. NULL = not stored.
  * cu_seqlens_host is read synchronously for the checks; cu_seqlens is the
  * same array on the device. */
 int ssd_prefill_varlen(const ssd_shape *shape, int32_t num_seqs,
@@ -190,8 +199,16 @@ int ssd_prefill_varlen(const ssd_shape *shape, int32_t num_seqs,
                        const float *A, const void *B, const void *C,
                        const float *D, const float *dt_bias,
                        const float *init_state, void *y, float *final_state,
-                       float *boundary_state, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       float *boundary_state, float *chunk_states,
+                       void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Rows F of ssd_prefill_varlen's chunk_states for a pack: the number of full
+ * chunks, sum over sequences of floor(len_s / chunk_size), from the host
+ * copy of cu_seqlens (cu[0] = 0, non-decreasing). -1 for a NULL array, a
+ * negative count, a decreasing cu_seqlens or a chunk_size < 1. */
+int64_t ssd_prefill_chunk_count(int32_t num_seqs, const int32_t *cu_seqlens_host,
+                                int32_t chunk_size);
 
 /* Store a fresh prefill into replay-cache slots ([RFC] section 3, "Prefill
  * / chunked prefill / recompute": the boundary state comes from the last

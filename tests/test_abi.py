@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
             "ssd_prefill_varlen", "ssd_commit_boundary", "ssd_replay_prefill",
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
             "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
-            "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen"}
+            "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen",
+            "ssd_prefill_chunk_count"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -83,7 +84,7 @@ def prefill(sh, cu=(0, 8), T=8, **over):
     return lib.ssd_prefill_varlen(ctypes.byref(sh), len(cu) - 1, T,
                                   cu.ctypes.data_as(ctypes.c_void_p), args["cu_dev"], args["x"],
                                   args["dt"], args["A"], args["B"], args["C"], None, None, None,
-                                  args["y"], None, None, None, 0, None)
+                                  args["y"], None, None, args.get("cs"), None, 0, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -106,6 +107,25 @@ def test_prefill_rejects_bad_seqlens_and_nulls():
     assert prefill(shape(), cu=(0,), T=0) == 0        # nothing to do, no launch
     assert prefill(sh, x=ctypes.c_void_p(0x1002)) == -9   # misaligned x
     assert prefill(sh, y=ctypes.c_void_p(0x1008)) == -9
+    assert prefill(sh, cs=ctypes.c_void_p(0x1004)) == -9  # misaligned chunk_states
+
+
+def test_prefill_chunk_count():
+    lib = _lib.load()
+
+    def count(cu, Q):
+        cu = np.asarray(cu, dtype=np.int32)
+        return lib.ssd_prefill_chunk_count(len(cu) - 1, cu.ctypes.data_as(ctypes.c_void_p), Q)
+
+    # full chunks per sequence, summed: 600 // 256 + 300 // 256 + 900 // 256 + 248 // 256
+    assert count([0, 600, 900, 1800, 2048], 256) == 2 + 1 + 3 + 0
+    assert count([0, 2048], 256) == 8 and count([0, 2047], 256) == 7
+    assert count([0, 16, 16, 48], 16) == 1 + 0 + 2
+    assert count([0], 16) == 0
+    assert count([0, 8, 4], 16) == -1                 # decreasing
+    assert count([0, 8], 0) == -1
+    assert lib.ssd_prefill_chunk_count(1, None, 16) == -1
+    assert erd.api.ssd_prefill_chunk_count([0, 600, 900, 1800, 2048], 256) == 6
 
 
 def cache(sh_c, **kw):

@@ -10,7 +10,8 @@ import torch
 
 import exact_replay_decode_amd as erd
 from exact_replay_decode_amd import synth
-from gpu_cases import (DEV, cache_consistent, headwise_max_rel, make_problem, mean_rel_err,
+from gpu_cases import (DEV, cache_consistent, check_bf16, headwise_max_rel, make_problem,
+                       mean_rel_err, offset_invariant,
                        same_bits, y_headwise_max_rel)
 
 pytestmark = pytest.mark.gpu
@@ -210,21 +211,59 @@ def test_c3_batched_replay_decode_bitwise(Q):
     assert same_bits(ydec, want)
     # offset invariant: every committed boundary sits on the chunk grid and
     # holds exactly the single-shot state at that position
-    bp = cache.boundary_pos.cpu().numpy()
-    assert np.all(bp % Q == 0)
-    assert np.array_equal(bp, (lengths // Q) * Q)
-    assert np.array_equal(cache.buf_len.cpu().numpy(), lengths % Q)
-    assert same_bits(cache.state, bnd) and cache_consistent(cache)
+    assert offset_invariant(cache, lengths, Q, bnd) and cache_consistent(cache)
     # the ranked launches leave the bookkeeping array zero
     assert not cache.work.any()
     # oracle parity on sampled sequences (decode rows and boundary state)
     from oracle import scan
+    from oracle.bounds import chunk_error_scales
     for s in (0, 131, 255):
         a, b = int(cu[s]), int(cu[s + 1])
-        ref = scan(erd.to_f64(x[a:b]), erd.to_f64(dt[a:b]), hp.A, erd.to_f64(B[a:b]),
-                   erd.to_f64(C[a:b]), [0, b - a], Q, D=hp.D, dt_bias=hp.dt_bias)
+        args = (erd.to_f64(x[a:b]), erd.to_f64(dt[a:b]), hp.A, erd.to_f64(B[a:b]),
+                erd.to_f64(C[a:b]), [0, b - a], Q)
+        ref = scan(*args, D=hp.D, dt_bias=hp.dt_bias)
         assert mean_rel_err(ydec[s], ref.y[pre[s]:]) <= BF16_MEAN_REL
+        check_bf16(ydec[s], ref.y, chunk_error_scales(*args, D=hp.D, dt_bias=hp.dt_bias),
+                   [(0, b - a - int(pre[s]))], rows=slice(int(pre[s]), None),
+                   label=f"C3 chunk {Q} decode rows, sequence {s}")
         assert headwise_max_rel(cache.state[s:s + 1].cpu().numpy(), ref.boundary_state) <= STATE_REL
+
+
+def test_offset_invariant_catches_poisoned_slots():
+    """Negative control of the offset invariant the batched-decode test
+    asserts: a correct commit passes it, and each way of committing a slot
+    at the wrong position fails it -- a boundary state taken one token off
+    the chunk grid, a boundary position moved by a chunk, a buffer count off
+    by one (the prefix-cache poisoning page's regression test asserts the
+    same invariant directly)."""
+    Q = 64
+    lengths = [200, 64, 1, 130, 255, 0]
+    pr = make_problem(lengths, H=8, G=1, P=64, N=128, Q=Q, seed=21)
+    x, dt, B, C = pr.dev(None)
+    cu = pr.cu
+    _, _, bnd = erd.ssd_prefill_varlen(pr.shape, cu, x, dt, pr.A, B, C, pr.D, pr.bias)
+
+    def committed(states):
+        cache = erd.ReplayCache(pr.shape, len(lengths), DEV)
+        erd.ssd_commit_boundary(pr.shape, cache, cu, x, dt, B, C, states)
+        return cache
+
+    good = committed(bnd)
+    assert offset_invariant(good, lengths, Q, bnd)
+    # sequence 3's boundary state computed one token late: the chunk grid of
+    # a run that starts at its second token
+    a, b = int(cu[3]), int(cu[4])
+    _, _, off = erd.ssd_prefill_varlen(pr.shape, [0, b - a - 1], x[a + 1:b], dt[a + 1:b], pr.A,
+                                       B[a + 1:b], C[a + 1:b], pr.D, pr.bias)
+    poisoned = bnd.clone()
+    poisoned[3] = off[0]
+    assert not offset_invariant(committed(poisoned), lengths, Q, bnd)
+    moved = committed(bnd)
+    moved.boundary_pos[0] += Q
+    assert not offset_invariant(moved, lengths, Q, bnd)
+    counted = committed(bnd)
+    counted.buf_len[4] -= 1
+    assert not offset_invariant(counted, lengths, Q, bnd)
 
 
 def test_c3_replay_batch_invariance():

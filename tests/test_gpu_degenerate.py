@@ -14,8 +14,9 @@ import torch
 
 import exact_replay_decode_amd as erd
 from exact_replay_decode_amd import synth, to_device
-from gpu_cases import DEV, mean_rel_err, same_bits
+from gpu_cases import DEV, check_bf16, mean_rel_err, same_bits, seq_spans
 from oracle import scan
+from oracle.bounds import chunk_error_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -66,12 +67,15 @@ def run_case(shape, lengths, tok, A, D, bias, seed):
     xs, dts, Bs, Cs = tok.f64()
     ref = scan(xs, dts, A, Bs, Cs, cu, shape.chunk_size, D=D, dt_bias=bias,
                dt_softplus=shape.dt_softplus)
-    return y, fin, ref
+    sc = chunk_error_scales(xs, dts, A, Bs, Cs, cu, shape.chunk_size, D=D, dt_bias=bias,
+                            dt_softplus=shape.dt_softplus)
+    return y, fin, ref, sc, cu
 
 
-def check(shape, y, fin, ref):
+def check(shape, y, fin, ref, scales=None, cu=None):
     if shape.io_dtype == "bf16":
         assert mean_rel_err(y, ref.y) <= 3e-3
+        check_bf16(y, ref.y, scales, seq_spans(cu), label="degenerate")
     else:
         H = shape.H
         yy = erd.to_f64(y)
@@ -100,8 +104,8 @@ def test_raw_dt_without_D_and_bias(io):
     rng = np.random.default_rng(40)
     tok.dt = storage(rng.uniform(0.002, 0.1, tok.dt.shape), io)
     A = synth.make_head_params(H, 40).A
-    y, fin, ref = run_case(shape, lengths, tok, A, None, None, seed=40)
-    check(shape, y, fin, ref)
+    y, fin, ref, sc, cu = run_case(shape, lengths, tok, A, None, None, seed=40)
+    check(shape, y, fin, ref, sc, cu)
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
@@ -122,8 +126,8 @@ def test_zero_decay_head_and_vanishing_delta(io):
     dt[::7, 0] = m200
     dt[lengths[0]:lengths[0] + lengths[1], 2] = m200
     tok.dt = dt
-    y, fin, ref = run_case(shape, lengths, tok, A, hp.D, hp.dt_bias, seed=41)
-    check(shape, y, fin, ref)
+    y, fin, ref, sc, cu = run_case(shape, lengths, tok, A, hp.D, hp.dt_bias, seed=41)
+    check(shape, y, fin, ref, sc, cu)
     # head 2 of sequence 1 never had a nonzero delta: its state stays zero
     assert not fin[1, 2].any()
     assert float(np.abs(ref.final_state[1, 2]).max()) < 1e-80

@@ -6,8 +6,9 @@ import pytest
 import torch
 
 import exact_replay_decode_amd as erd
-from gpu_cases import (DEV, headwise_max_rel, make_problem, mean_rel_err, same_bits,
-                       split_lengths, y_headwise_max_rel)
+from gpu_cases import (DEV, check_bf16, chunk_rows, error_scales, headwise_max_rel,
+                       make_problem, mean_rel_err, same_bits, seq_spans, split_lengths,
+                       y_headwise_max_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +71,27 @@ def c1():
     return pr, y, fin, bnd
 
 
+def check_chunk_states(pr, y, bnd, ref):
+    """The prefill's chunk_states output: against the oracle's state after
+    every full chunk (per (seq, head) 1e-4), the last full chunk of each
+    sequence bit for bit equal to its boundary state, and y unchanged by
+    asking for them."""
+    x, dt, B, C = pr.dev(None)
+    y2, _, bnd2, cs = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias,
+                                             want_chunk_states=True)
+    assert same_bits(y2, y) and same_bits(bnd2, bnd)
+    rows = chunk_rows(pr.cu, pr.shape.chunk_size)
+    assert cs.shape[0] == len(rows)
+    got = cs.cpu().numpy()
+    want = np.stack([ref.chunk_states[s, c] for s, c, _ in rows])
+    assert headwise_max_rel(got, want) <= STATE_REL
+    for s in range(len(pr.lengths)):
+        mine = [r for t, _, r in rows if t == s]
+        if mine:
+            assert same_bits(cs[mine[-1]], bnd[s]), s
+    return cs
+
+
 def test_c1_oracle_parity(c1):
     pr, y, fin, bnd = c1
     ref = pr.oracle(max_chunks=8)
@@ -78,6 +100,8 @@ def test_c1_oracle_parity(c1):
     assert err <= BF16_MEAN_REL
     assert headwise_max_rel(fin.cpu().numpy(), ref.final_state) <= STATE_REL
     assert headwise_max_rel(bnd.cpu().numpy(), ref.boundary_state) <= STATE_REL
+    check_bf16(y, ref.y, error_scales(pr), seq_spans(pr.cu), label="C1")
+    check_chunk_states(pr, y, bnd, ref)
 
 
 @pytest.mark.parametrize("step", [256, 100, 257])
@@ -149,12 +173,35 @@ def c2():
 
 def test_c2_oracle_parity(c2):
     pr, y, fin, bnd = c2
-    ref = pr.oracle()
+    ref = pr.oracle(max_chunks=4)
     err = mean_rel_err(y, ref.y)
     print(f"C2 mean|dy|/mean|y| = {100 * err:.4f} %")
     assert err <= BF16_MEAN_REL
     assert headwise_max_rel(fin.cpu().numpy(), ref.final_state) <= STATE_REL
     assert headwise_max_rel(bnd.cpu().numpy(), ref.boundary_state) <= STATE_REL
+    check_bf16(y, ref.y, error_scales(pr), seq_spans(pr.cu), label="C2")
+    check_chunk_states(pr, y, bnd, ref)
+
+
+def test_ssd_error_level_printed_by_the_rfc(c1, c2):
+    """[RFC] section 2, item 1 prints the chunked scan at 0.166-0.169 % of
+    mean |y| against fp64 on these two shapes (H=32 G=1 and H=64 G=8, P=64,
+    N=128, chunk 256, 2048 tokens, bf16 I/O), against a 0.141 % floor from
+    rounding the outputs alone. This engine rounds the same two operands to
+    bf16 as the chunked kernel there (the read-out state and the masked
+    C.B^T weights), so it lands in the same place: within 0.02 points of
+    the printed band (one seed here, one there), and above the floor."""
+    levels, floors = {}, {}
+    for name, (pr, y, _, _) in (("C1", c1), ("C2", c2)):
+        ref = pr.oracle()
+        levels[name] = mean_rel_err(y, ref.y)
+        floors[name] = mean_rel_err(torch.from_numpy(ref.y).to(torch.bfloat16), ref.y)
+    print("chunked-scan error vs fp64: " +
+          ", ".join(f"{k} {100 * v:.4f} % (floor {100 * floors[k]:.4f} %)"
+                    for k, v in levels.items()), flush=True)
+    for k, v in levels.items():
+        assert 1.46e-3 <= v <= 1.89e-3, levels
+        assert v > floors[k]
 
 
 def test_c2_packing_invariance(c2):
@@ -210,11 +257,15 @@ def test_full_batch_prefill_sampled_parity():
     cu = synth.cu_seqlens([T] * S)
     A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
     y, fin, _ = erd.ssd_prefill_varlen(shape, cu, x, dt, A, B, C, D, bias)
+    from oracle.bounds import chunk_error_scales
     for s in (0, 77, 255):
         sl = slice(s * T, (s + 1) * T)
-        ref = scan(erd.to_f64(x[sl]), erd.to_f64(dt[sl]), hp.A, erd.to_f64(B[sl]),
-                   erd.to_f64(C[sl]), [0, T], Q, D=hp.D, dt_bias=hp.dt_bias)
+        args = (erd.to_f64(x[sl]), erd.to_f64(dt[sl]), hp.A, erd.to_f64(B[sl]),
+                erd.to_f64(C[sl]), [0, T], Q)
+        ref = scan(*args, D=hp.D, dt_bias=hp.dt_bias)
         assert mean_rel_err(y[sl], ref.y) <= BF16_MEAN_REL
+        check_bf16(y[sl], ref.y, chunk_error_scales(*args, D=hp.D, dt_bias=hp.dt_bias),
+                   [(0, T)], label=f"256 x 2048 launch, sequence {s}")
         assert headwise_max_rel(fin[s:s + 1].cpu().numpy(), ref.final_state) <= STATE_REL
         ys, fs, _ = erd.ssd_prefill_varlen(shape, [0, T], x[sl], dt[sl], A, B[sl], C[sl], D,
                                            bias)
