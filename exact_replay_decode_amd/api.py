@@ -367,8 +367,11 @@ def ssd_replay_accept(shape: Shape, cache: ReplayCache, cu_seqlens, accepted, x,
 
 
 def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, dt_bias=None,
-                      slot_idx=None, y=None, stream=None):
-    """One exact-replay decode step for x.shape[0] sequences."""
+                      slot_idx=None, y=None, stream=None, static_work=False):
+    """One exact-replay decode step for x.shape[0] sequences. static_work:
+    call ssd_replay_decode_static, whose bookkeeping lives in the library's
+    own per-GPU array (nothing is allocated on the device; the cache's work
+    array is not passed)."""
     dev = cache.device
     H, G, P, N = shape.H, shape.G, shape.P, shape.N
     nb = int(x.shape[0])
@@ -383,10 +386,13 @@ def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, 
     y = torch.empty((nb, H, P), dtype=shape.io, device=dev) if y is None else \
         _need(y, "y", (nb, H, P), shape.io, dev)
     sh, cs = shape.c(), cache.struct()
-    rc = _lib.load().ssd_replay_decode(
-        ctypes.byref(sh), ctypes.byref(cs), nb, _ptr(sl), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
-        _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
-    _lib.check(rc, "ssd_replay_decode")
+    lib = _lib.load()
+    if static_work:
+        cs.work = None
+    fn = lib.ssd_replay_decode_static if static_work else lib.ssd_replay_decode
+    rc = fn(ctypes.byref(sh), ctypes.byref(cs), nb, _ptr(sl), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+            _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssd_replay_decode_static" if static_work else "ssd_replay_decode")
     return y
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libssd_replay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ssd_api.cpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_conv.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_conv.hip", "ssd_scratch.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 

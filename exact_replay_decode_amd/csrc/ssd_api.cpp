@@ -72,7 +72,9 @@ bool all_a16(const T *...p) {
     return (a16(p) && ...);
 }
 
-int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
+// need_work = false: the call does not use the cache's work array (the
+// decode entry point that brings its own)
+int check_cache(const ssd_shape *sh, const ssd_replay_cache *c, bool need_work = true) {
     if (!c)
         return SSD_ERR_NULL;
     if (c->state_dtype != SSD_F32)
@@ -80,7 +82,7 @@ int check_cache(const ssd_shape *sh, const ssd_replay_cache *c) {
     if (c->chunk_size != sh->chunk_size)
         return SSD_ERR_CHUNK_MISMATCH;
     if (!c->state || !c->state_bf || !c->buf_x || !c->buf_dt || !c->buf_B || !c->buf_len ||
-        !c->boundary_pos || !c->work)
+        !c->boundary_pos || (need_work && !c->work))
         return SSD_ERR_NULL;
     if (c->num_slots <= 0)
         return SSD_ERR_SHAPE;
@@ -408,16 +410,24 @@ int ssd_replay_accept(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
                        nullptr, 2, accepted, stream);
 }
 
-int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
-                      const int32_t *slot_idx, const void *x, const void *dt, const void *B,
-                      const void *C, const float *A, const float *D, const float *dt_bias,
-                      void *y, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode step; own_work: the library's static bookkeeping array takes
+// the place of cache->work (which may then be NULL).
+int replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
+                  const int32_t *slot_idx, const void *x, const void *dt, const void *B,
+                  const void *C, const float *A, const float *D, const float *dt_bias, void *y,
+                  bool own_work, hipStream_t stream) {
     Dims d;
     int st = check_shape(sh, &d);
     if (st != SSD_OK)
         return st;
-    if ((st = check_cache(sh, cache)) != SSD_OK)
+    if ((st = check_cache(sh, cache, !own_work)) != SSD_OK)
         return st;
+    if (own_work && cache->num_slots > ssd::kStaticMaxSlots)
+        return SSD_ERR_WORKSPACE;
     if (batch < 0 || (!slot_idx && batch > cache->num_slots) ||
         (int64_t)batch * d.H > std::numeric_limits<int32_t>::max())
         return SSD_ERR_SHAPE;
@@ -444,9 +454,31 @@ int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
     a.buf_len = cache->buf_len;
     a.boundary_pos = cache->boundary_pos;
     a.work = cache->work;
+    if (own_work && ssd::static_work(&a.work, (hipStream_t)stream) != hipSuccess)
+        return SSD_ERR_HIP;
     a.bm = buf_map(cache);
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
+                      const int32_t *slot_idx, const void *x, const void *dt, const void *B,
+                      const void *C, const float *A, const float *D, const float *dt_bias,
+                      void *y, hipStream_t stream) {
+    return replay_decode(sh, cache, batch, slot_idx, x, dt, B, C, A, D, dt_bias, y, false,
+                         stream);
+}
+
+int ssd_replay_decode_static(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
+                             const int32_t *slot_idx, const void *x, const void *dt,
+                             const void *B, const void *C, const float *A, const float *D,
+                             const float *dt_bias, void *y, hipStream_t stream) {
+    return replay_decode(sh, cache, batch, slot_idx, x, dt, B, C, A, D, dt_bias, y, true,
+                         stream);
 }
 
 int ssd_conv1d_varlen(const ssd_shape *sh, int32_t W, int32_t act, int32_t S, int64_t T,

@@ -143,6 +143,11 @@ hipError_t launch_conv_update(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_decode_advance(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+// the library's own decode bookkeeping array (ssd_scratch.hip): caches of
+// at most kStaticMaxSlots slots; *out = this device's copy (all zero
+// between calls), cleared on the stream at its first use on the device
+constexpr int32_t kStaticMaxSlots = 32768;
+hipError_t static_work(int32_t **out, hipStream_t stream);
 // synchronous device -> host copy (debug-build argument checks only)
 hipError_t copy_to_host(void *dst, const void *src, size_t bytes);
 // bf16 copy of `heads` fp32 [P][N] states (the cache's read-out operand)

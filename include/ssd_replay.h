@@ -261,6 +261,28 @@ int ssd_replay_decode(const ssd_shape *shape, const ssd_replay_cache *cache,
                       const float *A, const float *D, const float *dt_bias,
                       void *y, hipStream_t stream);
 
+/* ssd_replay_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step, bit for bit, but the decode bookkeeping lives
+ * in the library's own per-GPU array instead of cache->work, which is not
+ * read and may be NULL. Nothing is allocated on any call. Limits and
+ * sharing:
+ *  - cache->num_slots <= 32768 (the array holds 2 * 32768 + 34 int32 words
+ *    per GPU, kept until the process ends); larger caches get
+ *    SSD_ERR_WORKSPACE and nothing is launched;
+ *  - every call on one GPU uses that GPU's one array: calls that overlap in
+ *    time on one GPU (streams without an ordering between them) race and
+ *    give undefined results; calls ordered on one stream are fine;
+ *  - each call leaves the array zero; the first call on a device clears it
+ *    with a small kernel on `stream` before the step.
+ * Returns what ssd_replay_decode returns, plus SSD_ERR_HIP when the array's
+ * address cannot be looked up. */
+int ssd_replay_decode_static(const ssd_shape *shape, const ssd_replay_cache *cache,
+                             int32_t batch, const int32_t *slot_idx, const void *x,
+                             const void *dt, const void *B, const void *C,
+                             const float *A, const float *D, const float *dt_bias,
+                             void *y, hipStream_t stream);
+
 /* Speculative verification, output only ([RSSM] "Motivation and method":
  * drafts are verified with an output-only form instead of materialising a
  * state per draft; the acceptance length then advances only the committed

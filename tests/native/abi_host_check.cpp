@@ -43,8 +43,10 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t) {
     seen(a.cu && a.A && a.d.H > 0 && (a.replay ? a.cache_state != nullptr : true));
     return hipSuccess;
 }
+const int32_t *g_last_work = nullptr;
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
     seen(a.x && a.y && a.work && a.batch > 0);
+    g_last_work = a.work;
     return hipSuccess;
 }
 bool mfma_supported(const Dims &) { return false; }
@@ -70,6 +72,11 @@ hipError_t launch_ssu(const SsuArgs &a, hipStream_t) {
 }
 hipError_t launch_refresh_state_bf(const float *, void *, int64_t heads, int, int, hipStream_t) {
     seen(heads > 0);
+    return hipSuccess;
+}
+int32_t g_static_work[2 * kStaticMaxSlots + 34];
+hipError_t static_work(int32_t **out, hipStream_t) {
+    *out = g_static_work;
     return hipSuccess;
 }
 hipError_t copy_to_host(void *dst, const void *src, size_t bytes) {
@@ -234,6 +241,23 @@ int main() {
         b.page_tokens = 16;
         EXPECT(ssd_replay_decode(&sh, &b, 2, nullptr, x, dt, B, C, A, D, nullptr, y, nullptr) ==
                SSD_OK);
+    }
+    // the allocation-free decode: the library's array replaces cache->work
+    {
+        ssd_replay_cache b = c;
+        b.work = nullptr;
+        set_slots({0, 1});
+        EXPECT(ssd_replay_decode_static(&sh, &b, 2, sl, x, dt, B, C, A, D, nullptr, y,
+                                        nullptr) == SSD_OK);
+        EXPECT(ssd::g_last_work == ssd::g_static_work);
+        EXPECT(ssd_replay_decode(&sh, &c, 2, sl, x, dt, B, C, A, D, nullptr, y, nullptr) ==
+               SSD_OK);
+        EXPECT(ssd::g_last_work == c.work);
+        EXPECT(ssd_replay_decode(&sh, &b, 2, sl, x, dt, B, C, A, D, nullptr, y, nullptr) ==
+               SSD_ERR_NULL);
+        b.num_slots = ssd::kStaticMaxSlots + 1;
+        EXPECT(ssd_replay_decode_static(&sh, &b, 2, sl, x, dt, B, C, A, D, nullptr, y,
+                                        nullptr) == SSD_ERR_WORKSPACE);
     }
     EXPECT(ssd_replay_cache_refresh(&sh, &c, nullptr) == SSD_OK);
     EXPECT(ssd_replay_page_bytes(&sh, 16, 1) > 0 && ssd_replay_page_bytes(&sh, 12, 1) == 0);

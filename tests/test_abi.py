@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
             "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
             "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen",
-            "ssd_prefill_chunk_count"}
+            "ssd_prefill_chunk_count", "ssd_replay_decode_static"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -140,6 +140,23 @@ def decode(sh, c, batch=2):
     lib = _lib.load()
     return lib.ssd_replay_decode(ctypes.byref(sh), ctypes.byref(c), batch, None, FAKE, FAKE,
                                  FAKE, FAKE, FAKE, None, None, FAKE, None)
+
+
+def test_static_decode_checks():
+    # the allocation-free decode needs no work array, takes at most 32768
+    # slots, and fails closed like the plain one
+    lib = _lib.load()
+
+    def dec(sh, c, batch=2):
+        return lib.ssd_replay_decode_static(ctypes.byref(sh), ctypes.byref(c), batch, None, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None)
+    sh = shape()
+    assert dec(sh, cache(sh, work=None, num_slots=32769), batch=0) == -6
+    assert dec(sh, cache(sh, work=None, state_dtype=1)) == -4
+    assert dec(sh, cache(sh, work=None, chunk_size=32)) == -5
+    assert dec(sh, cache(sh, work=None), batch=0) == 0     # nothing to do, no launch
+    assert dec(sh, cache(sh, work=None, buf_B=None)) == -1
+    assert decode(sh, cache(sh, work=None)) == -1          # the plain form needs it
 
 
 def test_replay_fails_closed():
