@@ -15,19 +15,20 @@
 //   S^T[n][p]  = exp(lam_last) S^T[n][p] + sum_s B_s[n] (w_s x_s[p]),
 //                w_s = exp(lam_last - lam_s) delta_s: the decayed state is the
 //                MFMA accumulator the chunk's inputs are added into
-//                (K = s ascending; w x split into bf16 hi + lo)
+//                (16x16x32 MFMA tiles, K = s ascending in steps of 32; w x
+//                split into bf16 hi + lo)
 // S_bf is S rounded to bf16 for the read-out contraction; C.B^T operands are
 // exact bf16; the state path keeps about 16 mantissa bits through the hi/lo
 // split and is never rounded between chunks.
 //
 // Bit identity between prefill and decode: a 32-row block of chunk rows
-// ("t-block") is always computed by tblock_output() with the same MFMA
+// ("t-block") is always computed by tblock_part() with the same MFMA
 // shapes and the same K order; decode calls it for the t-block holding the
 // new token with the rows after it zero-filled. Each output element of an
 // MFMA depends only on its own row and column operands, masked weights are
 // selected to +0 (never multiplied), so the rows after the new token cannot
-// change it. The chunk-end state is computed by chunk_state_update() in both
-// paths.
+// change it. The chunk-end state is computed tile by tile with
+// state_kstep() in both paths.
 //
 // LDS tiles are row-major with 16 bytes of padding per row; operands that
 // contract over tokens are fetched transposed with ds_read_b64_tr_b16.
@@ -70,7 +71,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 // LDS layout, in bytes, for a chunk of Qp rows (Qp = max(Q, 32)).
 struct MLayout {
     int XS, BS, SS;                 // row strides in bf16 elements
-    int X, B, S, lam, u, el, w, beta, tot, bytes;
+    int X, B, S, sbb, lam, u, el, w, beta, scb, tot, bytes;
     __host__ __device__ MLayout(int Qp, int P, int N) {
         XS = P + kPad;
         BS = N + kPad;
@@ -79,15 +80,49 @@ struct MLayout {
         X = o;   o += Qp * XS * 2;
         B = o;   o += Qp * BS * 2;
         S = o;   o += P * SS * 2;
+        sbb = o - S;               // a second S_bf follows (the prefill alternates)
+        o += sbb;
         lam = o; o += kMaxQ * 4;   // in-chunk cumulative sum, log2 units
         u = o;   o += kMaxQ * 4;   // lam - log2(delta)
         el = o;  o += kMaxQ * 4;
         w = o;   o += kMaxQ * 4;
         beta = o; o += kMaxQ * 4;  // 2^(c - u_s), c = l at the end of s's 32-block
+        scb = o - lam;             // a second set of the five per-row arrays follows
+        o += scb;
         tot = o; o += 64;     // one float per wave
         bytes = o;
     }
+    // the layout of one prefill chunk: per-row arrays and S_bf of set b (the
+    // prefill computes the next chunk's set while this chunk reads its own),
+    // x and B tile rows from row r0 on
+    __host__ __device__ MLayout chunk(int b, int r0) const {
+        MLayout r = buf(b);
+        r.S += b * sbb;
+        r.X += r0 * XS * 2;
+        r.B += r0 * BS * 2;
+        return r;
+    }
+    // the layout whose per-row arrays are set b (0 or 1)
+    __host__ __device__ MLayout buf(int b) const {
+        MLayout r = *this;
+        const int d = b * scb;
+        r.lam += d;
+        r.u += d;
+        r.el += d;
+        r.w += d;
+        r.beta += d;
+        return r;
+    }
 };
+
+// The lane index, produced afresh at each use: the compiler can neither
+// hoist nor merge it, so lane-derived addresses are recomputed where they are
+// used instead of being kept live (or spilled) across the chunk loops.
+__device__ __forceinline__ int lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
 __device__ __forceinline__ bf16x8 lds_b128(const char *lds, int byte_off) {
     return *reinterpret_cast<const bf16x8 *>(lds + byte_off);
@@ -101,7 +136,7 @@ __device__ __forceinline__ bf16x8 lds_b128(const char *lds, int byte_off) {
 // the state contraction).
 __device__ __forceinline__ i16x8 lds_tr8(const char *lds, int base, int stride, int r0,
                                          int r1, int c16) {
-    const int l = threadIdx.x & 15;
+    const int l = lane_id() & 15;
     const int rr = l >> 2, cc = c16 + 4 * (l & 3);
     const lds_char *p = (const lds_char *)lds;
     i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -154,7 +189,7 @@ __device__ __forceinline__ f32x16 gram_block(F ba, const bf16x8 *cf) {
 // otherwise (selected, never multiplied).
 __device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const float *uu, int s_base,
                                        int t, uint32_t (&mb)[8]) {
-    const int g = (threadIdx.x & 63) >> 5;
+    const int g = lane_id() >> 5;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int s0 = s_base + 8 * q + 4 * g;
@@ -175,7 +210,7 @@ __device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const floa
 // and beta_s = 2^(c - u_s), c = l at the end of the s-block.
 __device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float *bt, int s_base,
                                       uint32_t (&mb)[8]) {
-    const int g = (threadIdx.x & 63) >> 5;
+    const int g = lane_id() >> 5;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int s0 = s_base + 8 * q + 4 * g;
@@ -192,7 +227,7 @@ __device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float
 template <int PT0, int PT1>
 __device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const char *lds, int xbase,
                                               int xs, int xrow0, f32x16 *acc) {
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int g = lane >> 5;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -213,10 +248,14 @@ __device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const cha
 // chunk rows t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7]
 // (g = lane/32), zero for rows that are not outputs. acc[pt] receives
 // Y^T[p][t] (without the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
+// tblock_part takes the s-blocks [sg0, sg1] (sg1 <= tau) after the read-out
+// when sg0 == 0 (which initialises acc): the prefill runs a t-block's
+// s-blocks in two parts around its half-chunk barrier, accumulating in the
+// same order.
 template <int P, int N, int PT0, int PT1>
-__device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const char *lds,
-                                              const MLayout &L, f32x16 *acc) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void tblock_part(int tau, int sg0, int sg1, const bf16x8 *cf,
+                                            const char *lds, const MLayout &L, f32x16 *acc) {
+    const int lane = lane_id();
     const int g = lane >> 5, c = lane & 31;
     const float *lam = reinterpret_cast<const float *>(lds + L.lam);
     const float *uu = reinterpret_cast<const float *>(lds + L.u);
@@ -224,21 +263,33 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     const float *el = reinterpret_cast<const float *>(lds + L.el);
     const int t = 32 * tau + c;
 
+    if (sg0 == 0) {
+        // read-out (each chain K-ascending, as readout_raw); the operands of
+        // one K step are loaded at a time, so they do not all stay live
 #pragma unroll
-    for (int pt = PT0; pt < PT1; ++pt)
-        acc[pt] = readout_scale(
-            readout_raw<N>(
-                [&](int k) {
-                    return lds_b128(lds, L.S + ((32 * pt + c) * L.SS + 16 * k + 8 * g) * 2);
-                },
-                cf),
-            el[t]);
+        for (int pt = PT0; pt < PT1; ++pt)
+            acc[pt] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+#pragma unroll
+            for (int pt = PT0; pt < PT1; ++pt)
+                acc[pt] = mfma(lds_b128(lds, L.S + ((32 * pt + c) * L.SS + 16 * k + 8 * g) * 2),
+                               cf[k], acc[pt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int pt = PT0; pt < PT1; ++pt)
+            acc[pt] = readout_scale(acc[pt], el[t]);
+    }
 
     const float lam_t = lam[t];
-    for (int sg = 0; sg <= tau; ++sg) {
-        const f32x16 gt = gram_block<N>(
+    auto gram = [&](int sg) {
+        return gram_block<N>(
             [&](int k) { return lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2); },
             cf);
+    };
+    for (int sg = sg0; sg <= sg1; ++sg) {
+        const f32x16 gt = gram(sg);
         uint32_t mb[8];
         if (sg == tau)
             m_diag(gt, lam_t, uu, 32 * sg, t, mb);
@@ -248,23 +299,38 @@ __device__ __forceinline__ void tblock_output(int tau, const bf16x8 *cf, const c
     }
 }
 
-// Chunk-state tiles (pt, nt) of 32 x 32 and the waves that own them. When
-// the n-tiles pair up, wave w < total/2 owns tiles (pt, 2m) and (pt, 2m+1)
-// with pt = w % (P/32), m = w / (P/32): both share the split token operand.
-// Otherwise tiles are dealt round-robin, ti = w + NW i. Which wave computes
-// a tile, and next to which other tile, does not change its arithmetic.
-template <int P, int N, int NW>
-struct StateTiles {
-    static constexpr int NPT = P / 32, NNT = N / 32;
-    static constexpr int total = NPT * NNT;
-    // tiles w, w + NW, ... (round robin); giving one wave two n-tiles of a
-    // p-tile (one split for both) spills registers in the prefill kernel
-    static constexpr int per_wave = (total + NW - 1) / NW;
-    __device__ static __forceinline__ bool tile(int w, int i, int &pt, int &nt) {
-        const int ti = w + NW * i;
-        pt = ti % NPT;
-        nt = ti / NPT;
-        return ti < total;
+// ---------------------------------------------------------------------------
+// The chunk-state update. The state S (P x N, fp32) is held as 16 x 16 tiles
+// of S^T (rows n, columns p) in the accumulator layout of the 16x16x32 MFMA:
+// lane l holds p = 16 ps + l % 16 and n = 16 nt + 4 (l / 16) + r, r = 0..3
+// (ps: the tile's 16-row p-slab, nt: its n-tile). Each tile is first
+// multiplied by exp(lam_last), then takes, per K = 32 step of chunk rows
+// (steps ascending), S^T += B^T (w x) with the token operand w x split into
+// bf16 hi + lo, hi first. A tile's arithmetic does not depend on which wave
+// computes it or next to which other tile: the prefill's four state waves
+// take one p-slab each (so every element of w x is split once), the decode
+// walks its head's slabs one after another.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kStateWaves = 4;
+
+// The prefill's state waves sw = 0..3: wave sw owns p-slab sw % (P / 16) and
+// NT n-tiles from nt0 (with P = 32 each of the two slabs is shared by two
+// waves, one n-half each).
+template <int P, int N>
+struct Slab {
+    static constexpr int NPS = P / 16;
+    static constexpr int NPART = kStateWaves / NPS;
+    static constexpr int NT = (N / 16) / NPART;
+    static_assert(NPS * NPART == kStateWaves && NT >= 1, "state tiles per wave");
+    __device__ static __forceinline__ void own(int sw, int &ps, int &nt0) {
+        ps = sw % NPS;
+        nt0 = (sw / NPS) * NT;
     }
 };
 
@@ -290,131 +356,79 @@ __device__ __forceinline__ void split_wx(const i16x8 &xv, const float (&ws)[8], 
     blo = __builtin_bit_cast(bf16x8, lv);
 }
 
-// One K = 16 step of a chunk-state tile: S^T += B^T (w x) as hi then lo.
-__device__ __forceinline__ void state_step(const bf16x8 &aop, const bf16x8 &bhi, const bf16x8 &blo,
-                                           f32x16 &acc) {
-    acc = mfma(aop, bhi, acc);
-    acc = mfma(aop, blo, acc);
+// One K = 32 step for NT n-tiles (from nt0) of a p-slab: rows row0 ..
+// row0 + 31 of the row-major x tile (byte base xb, row stride xs elements,
+// the slab's first column xc) and of the B tile (bb, bs); wk points at the
+// state weights of those rows. Lane group q = (lane % 64) / 16 supplies rows
+// 8q .. 8q + 7 of the step: k index j of both operands is row 8q + j.
+template <int NT>
+__device__ __forceinline__ void state_kstep(const char *lds, int xb, int xs, int xc, int bb,
+                                            int bs, int row0, int nt0, const float *wk,
+                                            f32x4 (&acc)[NT]) {
+    const int q = lane_id() >> 4;
+    const int r0 = row0 + 8 * q;
+    const i16x8 xv = lds_tr8(lds, xb, xs, r0, r0 + 4, xc);
+    const float4 w0 = *reinterpret_cast<const float4 *>(wk + 8 * q);
+    const float4 w1 = *reinterpret_cast<const float4 *>(wk + 8 * q + 4);
+    const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    bf16x8 bhi, blo;
+    split_wx(xv, ws, bhi, blo);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const bf16x8 a = as_bf16x8(lds_tr8(lds, bb, bs, r0, r0 + 4, 16 * (nt0 + i)));
+        acc[i] = mfma16(a, bhi, acc[i]);
+        acc[i] = mfma16(a, blo, acc[i]);
+    }
 }
 
-template <int P, int N, int NW>
-__device__ __forceinline__ void chunk_state_mma(int k0, int k1, const char *lds, const MLayout &L,
-                                                f32x16 (&acc)[StateTiles<P, N, NW>::per_wave]) {
-    using ST = StateTiles<P, N, NW>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 5;
-    const float *w = reinterpret_cast<const float *>(lds + L.w);
-    int pt0, nt0;
-    if (!ST::tile(wave, 0, pt0, nt0))
-        return;
-    for (int k = k0; k < k1; ++k) {
-        const int r0 = 16 * k + 8 * g;
-        // split token operand for p-tile pt0 (shared by the wave's other
-        // tiles of that p-tile)
-        const i16x8 xv = lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt0 + 16 * ((lane >> 4) & 1));
-        const float4 w0 = *reinterpret_cast<const float4 *>(w + r0);
-        const float4 w1 = *reinterpret_cast<const float4 *>(w + r0 + 4);
-        const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        bf16x8 bhi, blo;
-        split_wx(xv, ws, bhi, blo);
+// Tiles nt0 .. nt0 + NT - 1 of p-slab ps <-> a [P][N] fp32 state in global
+// memory (one float4 per lane and tile); a null source loads zeros.
+template <int P, int N, int NT, bool LOAD>
+__device__ __forceinline__ void slab_io(float *g, int ps, int nt0, f32x4 (&S)[NT]) {
+    const int lane = lane_id();
+    const int p = 16 * ps + (lane & 15), q = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < ST::per_wave; ++i) {
-            int pt, nt;
-            if (!ST::tile(wave, i, pt, nt))
-                continue;
-            const int c16n = 32 * nt + 16 * ((lane >> 4) & 1);
-            if (pt != pt0) {
-                // round-robin tile of another p-tile: split that p-tile
-                bf16x8 qhi, qlo;
-                split_wx(lds_tr8(lds, L.X, L.XS, r0, r0 + 4, 32 * pt + 16 * ((lane >> 4) & 1)),
-                         ws, qhi, qlo);
-                const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
-                state_step(aop, qhi, qlo, acc[i]);
-                continue;
-            }
-            const bf16x8 aop = as_bf16x8(lds_tr8(lds, L.B, L.BS, r0, r0 + 4, c16n));
-            state_step(aop, bhi, blo, acc[i]);
+    for (int i = 0; i < NT; ++i) {
+        const int64_t e = (int64_t)p * N + 16 * (nt0 + i) + 4 * q;
+        if (LOAD) {
+            const float4 v = g ? *reinterpret_cast<const float4 *>(g + e)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            S[i][0] = v.x;
+            S[i][1] = v.y;
+            S[i][2] = v.z;
+            S[i][3] = v.w;
+        } else {
+            *reinterpret_cast<float4 *>(g + e) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
         }
     }
 }
 
-// S (this wave's tiles, accumulator layout S^T[n][p]) <-
-//   exp(lam_last) S + sum_s B_s[n] w_s x_s[p] over the Qp chunk rows in LDS.
-template <int P, int N, int NW>
-__device__ __forceinline__ void chunk_state_update(int Qp, int n_valid, const char *lds,
-                                                   const MLayout &L,
-                                                   f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
-    const float *lam = reinterpret_cast<const float *>(lds + L.lam);
-    const float dec = fexp2(lam[n_valid - 1]);
+// bf16 (nearest even) of the tiles: into the row-major S_bf tile in LDS
+// (byte base sb, row stride ss; sb < 0: not stored) and into a [N/16][P][16]
+// bf16 copy in global memory (gbf, or null).
+template <int P, int NT>
+__device__ __forceinline__ void slab_bf16(const f32x4 (&S)[NT], int ps, int nt0, char *lds, int sb,
+                                          int ss, uint16_t *gbf) {
+    const int lane = lane_id();
+    const int p = 16 * ps + (lane & 15), q = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i)
+    for (int i = 0; i < NT; ++i) {
+        const int n = 16 * (nt0 + i) + 4 * q;
+        const uint2 v = make_uint2(bf16_pack(S[i][0], S[i][1]), bf16_pack(S[i][2], S[i][3]));
+        if (sb >= 0)
+            *reinterpret_cast<uint2 *>(lds + sb + (p * ss + n) * 2) = v;
+        if (gbf)
+            *reinterpret_cast<uint2 *>(gbf + state_bf_index(p, n, P)) = v;
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void slab_scale(f32x4 (&S)[NT], float dec) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
             S[i][r] = S[i][r] * dec;
-    chunk_state_mma<P, N, NW>(0, Qp / 16, lds, L, S);
-}
-
-// State tiles <-> global [P][N] fp32 (one float4 per lane per r-group).
-template <int P, int N, int NW, bool LOAD>
-__device__ __forceinline__ void state_io(float *gst, f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 5, c = lane & 31;
-#pragma unroll
-    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
-        int pt, nt;
-        if (!StateTiles<P, N, NW>::tile(wave, i, pt, nt))
-            continue;
-        const int p = 32 * pt + c;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = 32 * nt + 8 * q + 4 * g;
-            if (LOAD) {
-                const float4 v = gst ? *reinterpret_cast<const float4 *>(gst + (int64_t)p * N + n)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-                S[i][4 * q + 0] = v.x;
-                S[i][4 * q + 1] = v.y;
-                S[i][4 * q + 2] = v.z;
-                S[i][4 * q + 3] = v.w;
-            } else {
-                *reinterpret_cast<float4 *>(gst + (int64_t)p * N + n) =
-                    make_float4(S[i][4 * q + 0], S[i][4 * q + 1], S[i][4 * q + 2],
-                                S[i][4 * q + 3]);
-            }
-        }
-    }
-}
-
-// S_bf[p][n] <- bf16(S) from this wave's tiles.
-template <int P, int N, int NW>
-__device__ __forceinline__ void state_to_lds(char *lds, const MLayout &L,
-                                             const f32x16 (&S)[StateTiles<P, N, NW>::per_wave]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 5, c = lane & 31;
-#pragma unroll
-    for (int i = 0; i < StateTiles<P, N, NW>::per_wave; ++i) {
-        int pt, nt;
-        if (!StateTiles<P, N, NW>::tile(wave, i, pt, nt))
-            continue;
-        const int p = 32 * pt + c;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = 32 * nt + 8 * q + 4 * g;
-            const uint32_t lo = bf16_bits(S[i][4 * q + 0]) | ((uint32_t)bf16_bits(S[i][4 * q + 1]) << 16);
-            const uint32_t hi = bf16_bits(S[i][4 * q + 2]) | ((uint32_t)bf16_bits(S[i][4 * q + 3]) << 16);
-            *reinterpret_cast<uint2 *>(lds + L.S + (p * L.SS + n) * 2) = make_uint2(lo, hi);
-        }
-    }
-}
-
-// S_bf (the LDS bf16 copy of the state, made by state_to_lds) -> the cache's
-// bf16 state copy ([N/16][P][16]), by the whole workgroup.
-template <int P, int N>
-__device__ __forceinline__ void state_bf_from_lds(uint16_t *gbf, const char *lds, const MLayout &L) {
-    for (int e = threadIdx.x; e < P * N / 8; e += blockDim.x) {
-        const int half = e & 1, p = (e >> 1) % P, kk = (e >> 1) / P;
-        *reinterpret_cast<uint4 *>(gbf + 8 * (int64_t)e) =
-            *reinterpret_cast<const uint4 *>(lds + L.S + (p * L.SS + 16 * kk + 8 * half) * 2);
-    }
 }
 
 // Buffer row of buffered position j of one slot, for one wave.
@@ -439,13 +453,13 @@ struct SlotRows<true> {
     int ent, shift;
     SlotRows() = default;
     __device__ SlotRows(const BufMap &m, int slot, int) : shift(m.shift) {
-        ent = m.pages[(int64_t)slot * m.npp + ((threadIdx.x & 63) & (m.npp - 1))];
+        ent = m.pages[(int64_t)slot * m.npp + (lane_id() & (m.npp - 1))];
     }
     // the entries of positions [0, npos) are pages of the pool (same answer
     // in every lane)
     __device__ bool ok(const BufMap &m, int npos) const {
         const int n = (npos + (1 << shift) - 1) >> shift;
-        const bool bad = (threadIdx.x & 63) < n && (ent < 0 || ent >= m.num_pages);
+        const bool bad = lane_id() < n && (ent < 0 || ent >= m.num_pages);
         return __ballot(bad) == 0;
     }
     __device__ int64_t operator()(int j) const {
@@ -469,50 +483,107 @@ struct MView {
     __device__ int64_t token(int j) const { return tok_base + (j - nb); }
 };
 
-// Register-staged copy of a chunk's X / B rows and raw dt, loaded one chunk
-// ahead by the prefill workgroup (NT threads) so the global-load latency
-// overlaps the previous chunk's matrix work.
-template <int P, int N, int NT, class DT>
-struct ChunkRegs {
-    static constexpr int XC = P / 8, BC = N / 8;  // 16-byte pieces per row
-    static constexpr int XPT = (kMaxQ * XC + NT - 1) / NT;
-    static constexpr int BPT = (kMaxQ * BC + NT - 1) / NT;
-    uint4 x[XPT], b[BPT];
-    typename DT::T dt;   // raw (converted where it is used)
-};
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &u) {
+    return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
+}
 
-// One code path for every chunk shape, branch-free: each piece's source is
-// selected (buffer rows below nb, input tokens after; pieces past the chunk
-// read row 0 and are zeroed when stored), so the loads stay in flight until
-// their values are used.
-template <int P, int N, int NT, class DT, bool PG>
-__device__ __forceinline__ void load_chunk_regs(const MView<DT, PG> &v, int rows,
-                                                ChunkRegs<P, N, NT, DT> &r) {
-    using CR = ChunkRegs<P, N, NT, DT>;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < CR::XPT; ++i) {
-        const int e = tid + NT * i, q = e % CR::XC;
-        int j = e / CR::XC;
-        j = (e < rows * CR::XC && j < v.n_valid) ? j : 0;
-        const int64_t br = v.rows(j);
-        const uint16_t *src = j < v.nb ? v.bx + (br * v.H + v.h) * P
-                                       : v.x + (v.token(j) * v.H + v.h) * P;
-        r.x[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+// Chunk rows [r0, r0 + kSlab) of x and B straight from global memory into
+// LDS tile rows [h0, h0 + kSlab), with no registers in between (gfx950's
+// direct loads to LDS: a wave's 64 lanes fill 1 KB of LDS, 16 bytes each,
+// in lane order). The x and B regions of the slab are whole 1 KB pieces;
+// wave wv of the NWV waves that stage takes pieces wv, wv + NWV, .... Lanes
+// whose 16 bytes fall in a row's padding or in a row past n_valid load
+// nothing; the rows past n_valid are zeroed by the same waves. The loads
+// count in vmcnt: the staging waves wait (wait_vmcnt<0>) before the barrier
+// that publishes the rows. Buffered rows (below nb) come from the slot
+// buffer, the others from the input.
+constexpr int kSlab = 128;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One stream (x or B) of a slab: K pieces of 1 KB, of which this wave takes
+// k0, k0 + NWV, ...; a piece covers bytes [1024 k, 1024 k + 1024) of the
+// LDS tile rows (RB bytes each, VB of them data). A lane's (row, byte)
+// advances by a constant step from piece to piece.
+template <int VB, int RB, int K, int NWV>
+__device__ __forceinline__ void stage_stream(const char *gbase, int gstride, int r0, int n_valid,
+                                             int k0, char *ldst) {
+    constexpr int DR = NWV * 1024 / RB, DC = NWV * 1024 % RB;
+    const int o = k0 * 1024 + 16 * lane_id();
+    int row = o / RB, cb = o - (o / RB) * RB;
+    for (int k = k0; k < K; k += NWV) {
+        const int j = r0 + row;
+        if (cb < VB && j < n_valid)
+            __builtin_amdgcn_global_load_lds(gbase + (uint32_t)(j * gstride + cb),
+                                             (lds_void *)(ldst + k * 1024), 16, 0, 0);
+        row += DR;
+        cb += DC;
+        if (cb >= RB) {
+            cb -= RB;
+            ++row;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < CR::BPT; ++i) {
-        const int e = tid + NT * i, q = e % CR::BC;
-        int j = e / CR::BC;
-        j = (e < rows * CR::BC && j < v.n_valid) ? j : 0;
-        const int64_t br = v.rows(j);
-        const uint16_t *src = j < v.nb ? v.bB + (br * v.G + v.g) * N
-                                       : v.B + (v.token(j) * v.G + v.g) * N;
-        r.b[i] = *reinterpret_cast<const uint4 *>(src + 8 * q);
+}
+
+template <int P, int N, class DT, bool PG>
+__device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h0, int wv,
+                                           char *lds, const MLayout &L) {
+    constexpr int NWV = kStateWaves;
+    constexpr int XRB = (P + kPad) * 2, BRB = (N + kPad) * 2;   // row strides, bytes
+    constexpr int XK = kSlab * XRB / 1024, BK = kSlab * BRB / 1024;
+    static_assert(XK * 1024 == kSlab * XRB && BK * 1024 == kSlab * BRB, "1 KB pieces");
+    const int lane = lane_id();
+    if (v.nb == 0) {
+        // every row is an input token: row j at base + j * stride; the
+        // pieces are dealt to the waves as one sequence, x then B
+        const char *xb = reinterpret_cast<const char *>(v.x + (v.token(0) * v.H + v.h) * P);
+        const char *bb = reinterpret_cast<const char *>(v.B + (v.token(0) * v.G + v.g) * N);
+        stage_stream<P * 2, XRB, XK, NWV>(xb, v.H * P * 2, r0, v.n_valid, wv,
+                                          lds + L.X + h0 * XRB);
+        stage_stream<N * 2, BRB, BK, NWV>(bb, v.G * N * 2, r0, v.n_valid,
+                                          ((wv - XK) % NWV + NWV) % NWV, lds + L.B + h0 * BRB);
+    } else {
+        for (int k = wv; k < XK + BK; k += NWV) {
+            const bool isx = k < XK;
+            const int kk = isx ? k : k - XK;
+            const int o = kk * 1024 + 16 * lane;
+            const int row = isx ? o / XRB : o / BRB, cb = isx ? o % XRB : o % BRB;
+            const int j = r0 + row;
+            const bool ok = cb < (isx ? P * 2 : N * 2) && j < v.n_valid;
+            const int jj = ok ? j : 0;
+            const int64_t br = v.rows(jj);   // (paged: every lane takes part)
+            const bool buf = jj < v.nb;
+            const uint16_t *src =
+                isx ? (buf ? v.bx + (br * v.H + v.h) * P : v.x + (v.token(jj) * v.H + v.h) * P)
+                    : (buf ? v.bB + (br * v.G + v.g) * N : v.B + (v.token(jj) * v.G + v.g) * N);
+            char *dst = lds + (isx ? L.X + h0 * XRB : L.B + h0 * BRB) + kk * 1024;
+            if (ok)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(src) + cb,
+                                                 (lds_void *)dst, 16, 0, 0);
+        }
     }
-    const int jd = tid < v.n_valid ? tid : 0;
-    const int64_t brd = v.rows(jd);
-    r.dt = jd < v.nb ? v.bdt[brd * v.H + v.h] : v.dt[v.token(jd) * v.H + v.h];
+    // rows of the slab past n_valid: zeros (16-byte pieces, x then B)
+    const int v0 = min(max(v.n_valid - r0, 0), kSlab);
+    const int nz = (kSlab - v0) * (P / 8 + N / 8);
+    for (int e = lane + 64 * wv; e < nz; e += 64 * NWV) {
+        const int row = v0 + e / (P / 8 + N / 8), q = e % (P / 8 + N / 8);
+        char *dst = q < P / 8 ? lds + L.X + ((h0 + row) * (P + kPad) + 8 * q) * 2
+                              : lds + L.B + ((h0 + row) * (N + kPad) + 8 * (q - P / 8)) * 2;
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Raw dt of chunk rows lane + 64 i (one wave; rows past the chunk load row 0).
+template <class DT, bool PG>
+__device__ __forceinline__ void load_dt(const MView<DT, PG> &v, typename DT::T (&raw)[4]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const int jd = j < v.n_valid ? j : 0;
+        const int64_t br = v.rows(jd);
+        raw[i] = jd < v.nb ? v.bdt[br * v.H + v.h] : v.dt[v.token(jd) * v.H + v.h];
+    }
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -524,9 +595,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &u) {
-    return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
-}
 
 // Per-row quantities of a chunk, computed by the whole workgroup (one row per
 // thread; rows past n_valid have delta 0): lam (in-chunk cumulative sum of
@@ -560,31 +628,51 @@ __device__ __forceinline__ void chunk_scalars(float dt_raw, int n_valid, float A
     }
 }
 
-// LDS copy of the register-staged chunk, then chunk_scalars.
-template <int P, int N, int NT, class DT>
-__device__ __forceinline__ void store_chunk_regs(const ChunkRegs<P, N, NT, DT> &r, int rows,
-                                                 int n_valid, float A2_h, float bias,
-                                                 int softplus, bool weights, char *lds,
-                                                 const MLayout &L) {
-    using CR = ChunkRegs<P, N, NT, DT>;
-    const int tid = threadIdx.x;
-    const bool full = n_valid == rows;
+// The same per-row quantities computed by one wave for rows j = lane + 64 i
+// (wave_scan_segments evaluates the block scan's tree), into the per-row
+// arrays of layout L; the state weights always.
+template <class DT>
+__device__ __forceinline__ void chunk_scalars_wave(const typename DT::T (&raw)[4], int n_valid,
+                                                   float A2_h, float bias, int softplus,
+                                                   char *lds, const MLayout &L) {
+    const int lane = lane_id();
+    float *lam = reinterpret_cast<float *>(lds + L.lam);
+    float *uu = reinterpret_cast<float *>(lds + L.u);
+    float *el = reinterpret_cast<float *>(lds + L.el);
+    float *w = reinterpret_cast<float *>(lds + L.w);
+    float *bt = reinterpret_cast<float *>(lds + L.beta);
+    float dv[4], lv[4];
 #pragma unroll
-    for (int i = 0; i < CR::XPT; ++i) {
-        const int e = tid + NT * i, j = e / CR::XC, q = e % CR::XC;
-        if (e < rows * CR::XC)
-            *reinterpret_cast<uint4 *>(lds + L.X + (j * L.XS + 8 * q) * 2) =
-                full ? r.x[i] : keep_if(j < n_valid, r.x[i]);
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        float dd = 0.0f, aa = 0.0f;
+        if (j < n_valid) {
+            dd = delta_of(DT::val(raw[i]), bias, softplus);
+            aa = dd * A2_h;
+        }
+        dv[i] = dd;
+        lv[i] = aa;
+    }
+    wave_scan_segments(lv, 4);
+    // lam of the chunk's last row
+    const int jl = n_valid - 1;
+    float last = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float t = __shfl(lv[i], jl & 63, 64);
+        last = (jl >> 6) == i ? t : last;
     }
 #pragma unroll
-    for (int i = 0; i < CR::BPT; ++i) {
-        const int e = tid + NT * i, j = e / CR::BC, q = e % CR::BC;
-        if (e < rows * CR::BC)
-            *reinterpret_cast<uint4 *>(lds + L.B + (j * L.BS + 8 * q) * 2) =
-                full ? r.b[i] : keep_if(j < n_valid, r.b[i]);
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const float l = lv[i];
+        const float u = l - flog2(dv[i]);
+        lam[j] = l;
+        uu[j] = u;
+        el[j] = fexp2(l);
+        bt[j] = fexp2(__shfl(l, lane | 31, 64) - u);
+        w[j] = fexp2(last - l) * dv[i];
     }
-    // (a thread past the chunk loaded row 0's dt; chunk_scalars ignores it)
-    chunk_scalars(DT::val(r.dt), n_valid, A2_h, bias, softplus, weights, lds, L);
 }
 
 // Rows [0, rows) of the chunk's x (CX 16-byte pieces per row) and B (CB
@@ -632,7 +720,7 @@ template <int N, class DT, bool PG>
 __device__ __forceinline__ void load_cfrag(const MView<DT, PG> &v, int tau, int row_lo,
                                            bf16x8 (&cf)[N / 16]) {
     // rows outside [row_lo, n_valid) load row row_lo and are zeroed after
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int g = lane >> 5, t = 32 * tau + (lane & 31);
     const bool ok = t >= row_lo && t < v.n_valid && t >= v.nb;
     const bool all = row_lo <= 32 * tau && 32 * tau + 32 <= v.n_valid && v.nb <= 32 * tau;
@@ -658,29 +746,32 @@ template <int P, int PT0, int PT1, class V>
 __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int row_hi,
                                             float D_h, const char *lds, const MLayout &L,
                                             const f32x16 *acc, uint16_t *y) {
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int g = lane >> 5, c = lane & 31;
     const int t = 32 * tau + c;
     if (t < row_lo || t >= row_hi)
         return;
     uint16_t *yrow = y + (v.token(t) * v.H + v.h) * P;
+    const char *xrow = lds + L.X + t * L.XS * 2;
+    // four outputs at a time (bf16 pairs rounded to nearest even, as one
+    // conversion each), so that few of them are live at once
 #pragma unroll
     for (int pt = PT0; pt < PT1; ++pt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int p = 32 * pt + 8 * q + 4 * g;
-            const uint2 xr = *reinterpret_cast<const uint2 *>(lds + L.X + (t * L.XS + p) * 2);
-            const float xs[4] = {bf16_float(xr.x & 0xffff), bf16_float(xr.x >> 16),
-                                 bf16_float(xr.y & 0xffff), bf16_float(xr.y >> 16)};
-            uint16_t o[4];
+            const uint2 xr = *reinterpret_cast<const uint2 *>(xrow + 2 * p);
+            float yv[4];
+            yv[0] = fmaf(D_h, bf16_float(xr.x & 0xffff), acc[pt][4 * q]);
+            yv[1] = fmaf(D_h, bf16_float(xr.x >> 16), acc[pt][4 * q + 1]);
+            yv[2] = fmaf(D_h, bf16_float(xr.y & 0xffff), acc[pt][4 * q + 2]);
+            yv[3] = fmaf(D_h, bf16_float(xr.y >> 16), acc[pt][4 * q + 3]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float yv = fmaf(D_h, xs[e], acc[pt][4 * q + e]);
-                yv = yv + 0.0f;  // -0 -> +0
-                o[e] = bf16_bits(yv);
-            }
+            for (int e = 0; e < 4; ++e)
+                yv[e] = yv[e] + 0.0f;  // -0 -> +0
             *reinterpret_cast<uint2 *>(yrow + p) =
-                make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+                make_uint2(bf16_pack(yv[0], yv[1]), bf16_pack(yv[2], yv[3]));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -695,66 +786,76 @@ __device__ __forceinline__ int xcd_local_index(int bid, int nblocks) {
     return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
-// Prefill workgroups have 8 waves (two per SIMD). With 8 t-blocks, waves w
-// and w + 4 (same SIMD) take t-blocks 7 - w and w: equal causal work per
-// SIMD, the heavy t-blocks on the older waves (which the SIMD serves first).
-// With fewer t-blocks, wave w takes t-block w.
-constexpr int kPrefillWaves = 8;
+// Prefill workgroups have 12 waves (three per SIMD; wave w runs on SIMD
+// w % 4). Waves 0..3 are the state waves: each owns a quarter of the fp32
+// state in registers and updates it over the chunk, and they stage the
+// chunk rows into LDS; wave 0 also computes the next chunk's per-row
+// quantities (into the other set of per-row arrays). Waves 4..11 each
+// compute the outputs of one 32-row t-block: with 8 t-blocks wave 4 + k
+// takes 7 - k and wave 8 + k takes k, so every SIMD has the same causal work
+// and the heavy t-block on its older wave.
+constexpr int kPrefillWaves = 12;
 
 __device__ __forceinline__ int wave_tblock(int nT, int wave) {
+    const int i = wave - kStateWaves;
+    if (i < 0)
+        return -1;
     if (nT == 8)
-        return wave < 4 ? 7 - wave : wave - 4;
-    return wave < nT ? wave : -1;
+        return i < 4 ? 7 - i : i - 4;
+    return i < nT ? i : -1;
 }
 
-template <int P, int N, class DT, bool PG>
+template <int P, int N, class DT, bool PG, bool RP>
 __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *lds) {
     using TD = typename DT::T;
-    constexpr int NW = kPrefillWaves;
+    using SL = Slab<P, N>;
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
     const int g = h / (H / G);
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool swave = wave < kStateWaves;
     constexpr int PN = P * N;
-    const MLayout L(Qp, P, N);
+    const MLayout L(kMaxQ, P, N);
+    // replay calls (RP) read the slot cache and buffer; plain prefill does not
+    constexpr bool replay = RP;
 
     const int64_t t0 = a.cu[s];
     const int len = seq_len(a.cu, a.take, s);
-    const int slot = a.replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
-    if (a.replay && (len == 0 || slot < 0 || slot >= a.num_slots))
+    const int slot = replay ? (a.slot_idx ? a.slot_idx[s] : s) : s;
+    if (replay && (len == 0 || slot < 0 || slot >= a.num_slots))
         return;
-    const int nbuf = a.replay ? a.buf_len[slot] : 0;
+    const int nbuf = replay ? a.buf_len[slot] : 0;
     if (nbuf < 0 || nbuf >= Q)
         return;
     // acceptance without a chunk that fills has no work here (the buffer
     // append is the commit kernel's); with only_cross, verification handles
     // just the sequences whose drafts run past the chunk end
-    if ((a.no_y && nbuf + len < Q) || (a.only_cross && nbuf + len <= Q))
+    if (((RP && a.no_y) && nbuf + len < Q) || ((RP && a.only_cross) && nbuf + len <= Q))
         return;
     const SlotRows<PG> rows(a.bm, slot, Q);
-    if (!rows.ok(a.bm, a.dry ? nbuf : replay_npos(nbuf, len, Q)))
+    if (!rows.ok(a.bm, (RP && a.dry) ? nbuf : replay_npos(nbuf, len, Q)))
         return;
 
-    float *init = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+    float *init = replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                            : (a.init_state ? const_cast<float *>(a.init_state) +
                                                  ((int64_t)s * H + h) * PN
                                            : nullptr);
-    f32x16 S[StateTiles<P, N, NW>::per_wave];
-    state_io<P, N, NW, true>(init, S);
-    // the initial state is in registers before the chunk loop starts (so no
-    // wait inside the loop has to account for these loads)
-    wait_vmcnt<0>();
-    state_to_lds<P, N, NW>(lds, L, S);
+    // the state waves' tiles of the state, and its bf16 read-out copy in LDS
+    int ps, nt0;
+    SL::own(swave ? wave : 0, ps, nt0);
+    f32x4 S[SL::NT];
+    if (swave)
+        slab_io<P, N, SL::NT, true>(init, ps, nt0, S);
 
     MView<DT, PG> v;
     v.x = static_cast<const uint16_t *>(a.x);
     v.B = static_cast<const uint16_t *>(a.B);
     v.C = static_cast<const uint16_t *>(a.C);
     v.dt = static_cast<const TD *>(a.dt);
-    v.bx = a.replay ? static_cast<const uint16_t *>(a.buf_x) : nullptr;
-    v.bB = a.replay ? static_cast<const uint16_t *>(a.buf_B) : nullptr;
-    v.bdt = a.replay ? static_cast<const TD *>(a.buf_dt) : nullptr;
+    v.bx = replay ? static_cast<const uint16_t *>(a.buf_x) : nullptr;
+    v.bB = replay ? static_cast<const uint16_t *>(a.buf_B) : nullptr;
+    v.bdt = replay ? static_cast<const TD *>(a.buf_dt) : nullptr;
     v.rows = rows;
     v.h = h; v.g = g; v.H = H; v.G = G;
 
@@ -764,19 +865,19 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     const int total = nbuf + len;
     const int nfull = total / Q;
     // without outputs only the chunks that fill are processed
-    const int nchunks = a.no_y ? nfull : (total + Q - 1) / Q;
-    float *bnd = a.replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+    const int nchunks = (RP && a.no_y) ? nfull : (total + Q - 1) / Q;
+    float *bnd = replay ? a.cache_state + ((int64_t)slot * H + h) * PN
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
                                               : nullptr);
-    uint16_t *bnd_bf = a.replay ? static_cast<uint16_t *>(a.cache_state_bf) +
+    uint16_t *bnd_bf = replay ? static_cast<uint16_t *>(a.cache_state_bf) +
                                       ((int64_t)slot * H + h) * PN
                                 : nullptr;
-    const bool write_bnd = bnd && (!a.replay || nfull > 0) && !a.dry;
+    const bool write_bnd = bnd && (!replay || nfull > 0) && !(RP && a.dry);
     uint16_t *y = static_cast<uint16_t *>(a.y);
     // chunk-end states of the full chunks (plain prefill): rows from
     // full_chunks_before(s) on
     float *cst = nullptr;
-    if (!a.replay && a.chunk_states)
+    if (!replay && a.chunk_states)
         cst = a.chunk_states +
               ((int64_t)full_chunks_before(a.cu, s, Q, reinterpret_cast<int *>(lds + L.tot)) * H +
                h) * PN;
@@ -787,69 +888,161 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
         v.tok_base = t0 + (int64_t)c * Q + v.nb - nbuf;
     };
 
-    ChunkRegs<P, N, 64 * NW, DT> regs;
+    // The chunk rows pass through LDS in slabs of 128 rows, double-buffered
+    // in the two halves of the x and B tiles, by direct loads (no registers),
+    // all staged by the state waves:
+    //  - chunk size 256: rows 0..127 (slab A) in half 0, 128..255 (slab B)
+    //    in half 1. Phase 1: every t-block takes its s-blocks 0..3 (t-blocks
+    //    0..3 finish), the state waves their K steps 0..3 while they stage
+    //    slab B. Phase 2: t-blocks 4..7 take s-blocks 4.., the state waves
+    //    their K steps 4..7 while they stage the next chunk's slab A. Two
+    //    barriers per chunk.
+    //  - chunk size <= 128: chunk c in half c % 2, the next chunk staged in
+    //    the other half during this one. One barrier.
+    // S_bf and the per-row arrays alternate between two sets, so the state
+    // waves write the next chunk's while this chunk reads its own.
+    const bool two = Qp > kSlab;
+    auto lay = [&](int c) { return L.chunk(c & 1, two ? 0 : kSlab * (c & 1)); };
     if (nchunks > 0) {
         set_chunk(0);
-        load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
-    }
-    for (int c = 0; c < nchunks; ++c) {
-        const bool mirror = c == nfull && write_bnd && bnd_bf;
-        if (c == nfull && write_bnd)
-            state_io<P, N, NW, false>(bnd, S);
-        if (cst && c >= 1 && c <= nfull)   // S is the state after full chunk c - 1
-            state_io<P, N, NW, false>(cst + (int64_t)(c - 1) * H * PN, S);
-        set_chunk(c);
-        const int n_valid = v.n_valid;
-        const bool upd = n_valid == Q || (!a.replay && a.final_state);
-        __syncthreads();  // previous chunk's LDS reads (and S_bf writes) are done
-        if (mirror)  // S_bf in LDS is the bf16 copy of the state just stored
-            state_bf_from_lds<P, N>(bnd_bf, lds, L);
-        store_chunk_regs<P, N, 64 * NW, DT>(regs, Qp, n_valid, A2_h, bias, d.softplus, upd, lds,
-                                            L);
+        if (swave) {
+            slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.S, L.SS, nullptr);
+            stage_slab<P, N>(v, 0, 0, wave, lds, L);
+            if (two)
+                stage_slab<P, N>(v, kSlab, kSlab, wave, lds, L);
+            if (wave == 0) {
+                TD rawdt[4];
+                load_dt<DT>(v, rawdt);
+                chunk_scalars_wave<DT>(rawdt, v.n_valid, A2_h, bias, d.softplus, lds,
+                                       L.buf(0));
+            }
+            wait_vmcnt<0>();
+        }
         __syncthreads();
-        const int lo = max(32 * tau, v.nb), hi = min(32 * tau + 32, n_valid);
-        const bool has_rows = tau >= 0 && lo < hi && !a.no_y;
+    }
+    // The two roles run separate copies of the chunk loop (so that neither
+    // keeps the other's registers live), meeting at the same barriers.
+    if (swave) {
+        for (int c = 0; c < nchunks; ++c) {
+            const MLayout Lc = lay(c);
+            // S is the state after c chunks
+            if (c == nfull && write_bnd) {
+                slab_io<P, N, SL::NT, false>(bnd, ps, nt0, S);
+                if (bnd_bf)
+                    slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
+            }
+            if (cst && c >= 1 && c <= nfull)
+                slab_io<P, N, SL::NT, false>(cst + (int64_t)(c - 1) * H * PN, ps, nt0, S);
+            set_chunk(c);
+            const int n_valid = v.n_valid;
+            const bool upd = n_valid == Q || (!replay && a.final_state);
+            const bool more = c + 1 < nchunks;
+            const MView<DT, PG> vc = v;
+            if (more)
+                set_chunk(c + 1);
+            // the next chunk's raw dt; staging: this chunk's slab B (two
+            // slabs), or the next chunk in the other half
+            TD rawdt[4];
+            if (wave == 0 && more)
+                load_dt<DT>(v, rawdt);
+            if (two) {
+                if (c > 0)
+                    stage_slab<P, N>(vc, kSlab, kSlab, wave, lds, L);
+            } else if (more) {
+                stage_slab<P, N>(v, 0, kSlab * ((c + 1) & 1), wave, lds, L);
+            }
+            const float *w = reinterpret_cast<const float *>(lds + Lc.w);
+            const int nk = Qp / 32, nk1 = two ? kSlab / 32 : nk;
+            if (upd) {
+                slab_scale<SL::NT>(
+                    S, fexp2(reinterpret_cast<const float *>(lds + Lc.lam)[n_valid - 1]));
+                for (int kk = 0; kk < nk1; ++kk)
+                    state_kstep<SL::NT>(lds, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
+                                        w + 32 * kk, S);
+            }
+            if (two) {
+                wait_vmcnt<0>();
+                __syncthreads();   // phase 2: slab B is in, slab A is free
+                if (more)
+                    stage_slab<P, N>(v, 0, 0, wave, lds, L);
+                if (upd)
+                    for (int kk = nk1; kk < nk; ++kk)
+                        state_kstep<SL::NT>(lds, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
+                                            w + 32 * kk, S);
+            }
+            // the next chunk's read-out copy and per-row arrays
+            if (upd && more)
+                slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.chunk((c + 1) & 1, 0).S, L.SS, nullptr);
+            if (wave == 0 && more)
+                chunk_scalars_wave<DT>(rawdt, v.n_valid, A2_h, bias, d.softplus, lds,
+                                       L.buf((c + 1) & 1));
+            wait_vmcnt<0>();
+            __syncthreads();   // end of chunk c
+        }
+        if (cst && nfull == nchunks && nfull > 0)
+            slab_io<P, N, SL::NT, false>(cst + (int64_t)(nfull - 1) * H * PN, ps, nt0, S);
+        if (nfull == nchunks && write_bnd) {
+            slab_io<P, N, SL::NT, false>(bnd, ps, nt0, S);
+            if (bnd_bf)
+                slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
+        }
+        if (!replay && a.final_state)
+            slab_io<P, N, SL::NT, false>(a.final_state + ((int64_t)s * H + h) * PN, ps, nt0, S);
+    } else {
+        // t-block waves. The C rows of the t-block's next chunk go out right
+        // after its outputs; a t-block without output rows loads, and
+        // zeroes, the chunk's last row (n_valid - 1 >= nb is an input token).
         bf16x8 cf[N / 16];
-        if (has_rows)
-            load_cfrag<N, DT>(v, tau, lo, cf);
-        // next chunk's inputs: in flight during this chunk's matrix work
-        const MView<DT, PG> vc = v;
-        if (c + 1 < nchunks) {
-            set_chunk(c + 1);
-            load_chunk_regs<P, N, 64 * NW, DT>(v, Qp, regs);
+        auto load_c = [&](const MView<DT, PG> &vv) {
+            const int lo = max(32 * tau, vv.nb), hi = min(32 * tau + 32, vv.n_valid);
+            load_cfrag<N, DT>(vv, tau, lo < hi ? lo : vv.n_valid - 1, cf);
+        };
+        if (nchunks > 0 && tau >= 0) {
+            set_chunk(0);
+            load_c(v);
         }
-        // new state first (registers only; S_bf keeps the chunk-start state)
-        if (upd)
-            chunk_state_update<P, N, NW>(Qp, n_valid, lds, L, S);
-        if (has_rows) {
+        const int sgA = kSlab / 32 - 1;   // last s-block of slab A
+        for (int c = 0; c < nchunks; ++c) {
+            const MLayout Lc = lay(c);
+            set_chunk(c);
+            const MView<DT, PG> vc = v;
+            const bool more = c + 1 < nchunks;
+            if (more)
+                set_chunk(c + 1);
+            const int lo = max(32 * tau, vc.nb), hi = min(32 * tau + 32, vc.n_valid);
+            const bool out = tau >= 0 && lo < hi && !(RP && a.no_y);
             f32x16 acc[P / 32];
-            tblock_output<P, N, 0, P / 32>(tau, cf, lds, L, acc);
-            emit_tblock<P, 0, P / 32>(vc, tau, lo, hi, D_h, lds, L, acc, y);
-        }
-        if (upd) {
-            __syncthreads();  // all waves are done reading S_bf
-            state_to_lds<P, N, NW>(lds, L, S);
+            // s-blocks of slab A (all of them with one slab)
+            if (out)
+                tblock_part<P, N, 0, P / 32>(tau, 0, two ? min(tau, sgA) : tau, cf, lds, Lc, acc);
+            if (!two || tau <= sgA) {
+                if (out)
+                    emit_tblock<P, 0, P / 32>(vc, tau, lo, hi, D_h, lds, Lc, acc, y);
+                if (tau >= 0 && more)
+                    load_c(v);
+            }
+            if (two) {
+                __syncthreads();   // phase 2: slab B is in
+                if (tau > sgA) {
+                    if (out) {
+                        tblock_part<P, N, 0, P / 32>(tau, sgA + 1, tau, cf, lds, Lc, acc);
+                        emit_tblock<P, 0, P / 32>(vc, tau, lo, hi, D_h, lds, Lc, acc, y);
+                    }
+                    if (more)
+                        load_c(v);
+                }
+            }
+            __syncthreads();   // end of chunk c
         }
     }
-    if (cst && nfull == nchunks && nfull > 0)
-        state_io<P, N, NW, false>(cst + (int64_t)(nfull - 1) * H * PN, S);
-    if (nfull == nchunks && write_bnd) {
-        state_io<P, N, NW, false>(bnd, S);
-        if (bnd_bf) {
-            __syncthreads();
-            state_bf_from_lds<P, N>(bnd_bf, lds, L);
-        }
-    }
-    if (!a.replay && a.final_state)
-        state_io<P, N, NW, false>(a.final_state + ((int64_t)s * H + h) * PN, S);
 }
 
 // One workgroup per (sequence, head).
-template <int P, int N, class DT, bool PG>
+template <int P, int N, class DT, bool PG, bool RP>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int wid = xcd_local_index(blockIdx.x, gridDim.x);
-    scan_one<P, N, DT, PG>(a, wid / a.d.H, wid % a.d.H, lds);
+    scan_one<P, N, DT, PG, RP>(a, wid / a.d.H, wid % a.d.H, lds);
 }
 
 // Replay calls where few sequences have work: verification of drafts that
@@ -864,7 +1057,7 @@ template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int H = a.d.H, Q = a.d.Q;
-    const MLayout L(Q < 32 ? 32 : Q, P, N);
+    const MLayout L(kMaxQ, P, N);   // scan_one's layout
     int *list = reinterpret_cast<int *>(lds + L.bytes);   // [1 + 64 * kPrefillWaves]
     const int total = a.S * H;
     const int rounds = (total + gridDim.x - 1) / gridDim.x;   // candidates per workgroup
@@ -889,7 +1082,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
         for (int j = 0; j < n; ++j) {
             const int ej = list[1 + j];
             __syncthreads();   // the previous pair's LDS use is over
-            scan_one<P, N, DT, PG>(a, ej / H, ej % H, lds);
+            scan_one<P, N, DT, PG, true>(a, ej / H, ej % H, lds);
         }
         __syncthreads();   // list reads are done before the next round resets it
     }
@@ -947,16 +1140,17 @@ struct DLayout {
         beta = o; o += Qp * 4;
         gc = o;   o += (kMaxQ / 32) * 32 * 4;   // C.B^T column k % 32 per s-block
         X = o;    o += 32 * XS * 2;              // padded 32-row x tile
-        // with the chunk-state update in the same launch: its 16-row blocks
-        // (x: 32 columns, B: all N) over the arrays above once the output is
-        // written, and the state weights of the chunk-filling step
-        cXS = 32 + kPad;
+        // with the chunk-state update in the same launch: its 32-row blocks
+        // (x: the 16 columns of one p-slab, B: all N) over the arrays above
+        // once the output is written, and the state weights of the
+        // chunk-filling step
+        cXS = 16 + kPad;
         cBS = N + kPad;
         cX = 0;
-        cB = cX + 16 * cXS * 2;
+        cB = cX + 32 * cXS * 2;
         w = o;
         if (fused) {
-            const int cend = cB + 16 * cBS * 2;
+            const int cend = cB + 32 * cBS * 2;
             o = o > cend ? o : cend;
             w = o;
             o += Qp * 4;
@@ -1257,26 +1451,26 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<
 
 // Phase 3, only when the token fills the chunk: the chunk-state update of
 // the wave's head, S <- 2^lam_last S + sum_j B_j (w_j x_j), with the
-// prefill's operands and MFMA order (split_wx, state_step, K = Qp rows in
-// steps of 16, hi then lo), so the new boundary state has the bits a
-// prefill of the same tokens leaves. The weights w_j were put in LDS by
-// phase 1. Rows 16 kb .. +15 of x (32 columns of one p-tile) and of B (all
-// N columns) pass through LDS for the transposed reads, the next block's
-// rows in flight during this block's MFMAs; rows below k come from the slot
-// buffer, row k from the step's input (the buffer row written by this step
-// is not read back), rows after k are zero. Two passes (one per p-tile)
-// keep four accumulator tiles live.
+// prefill's tile arithmetic (state_kstep: K = 32 rows per step, hi then lo),
+// so the new boundary state has the bits a prefill of the same tokens
+// leaves. The weights w_j were put in LDS by phase 1. The head's p-slabs are
+// done one after another (all n-tiles of a slab live); per step, rows
+// 32 kk .. +31 of x (the slab's 16 columns) and of B (all N) pass through
+// LDS for the transposed reads, the next step's rows in flight during this
+// step's MFMAs; rows below k come from the slot buffer, row k from the
+// step's input (the buffer row written by this step is not read back), rows
+// after k are zero.
 template <int P, int N, class DT, bool PG>
 __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
                                               int slot, int h, int k, char *lds, const DLayout &L,
                                               float lam_last) {
-    constexpr int NPT = P / 32, NNT = N / 32;
-    constexpr int BPL = N / 32;   // 16-byte pieces of a 16-row B block per lane
+    constexpr int NPS = P / 16, NT = N / 16;
+    constexpr int BPL = N / 16;   // 16-byte pieces of a 32-row B block per lane
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
     const int g = h / (H / G);
-    const int lane = threadIdx.x & 63, gl = lane >> 5, c = lane & 31;
+    const int lane = threadIdx.x & 63;
     const int64_t PN = (int64_t)P * N;
     const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pools
     const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
@@ -1286,112 +1480,54 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
     uint16_t *sbf = static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN;
     const float *w = reinterpret_cast<const float *>(lds + L.w);
     const float dec = fexp2(lam_last);
-    const int nkb = Qp / 16;
-    // blocks holding rows 0..k; the later ones (chunks under 32 rows) are
-    // all zero: only zero x rows are staged for them, and the zero x operand
-    // also serves as the B operand (the bits zeroed B rows would give), so
-    // the B block stays in LDS for the next p-tile when it is the only one
-    const int nreal = (k + 16) >> 4;
+    const int nkk = Qp / 32;
 
-    auto load_block = [&](int pt, int kb, bool withB, uint4 &xr, uint4 (&br)[BPL]) {
+    auto load_block = [&](int ps, int kk, uint4 &xr, uint4 (&br)[BPL]) {
         {
-            const int j = 16 * kb + (lane >> 2);
+            const int j = 32 * kk + (lane >> 1);
             const int64_t rj = rows(j < k ? j : 0);
             const uint16_t *src = j < k ? bx + (rj * H + h) * P : xin;
-            xr = *reinterpret_cast<const uint4 *>(src + 32 * pt + 8 * (lane & 3));
+            xr = *reinterpret_cast<const uint4 *>(src + 16 * ps + 8 * (lane & 1));
         }
-        if (!withB)
-            return;
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
-            const int e = lane + 64 * i, j = 16 * kb + e / (N / 8);
+            const int e = lane + 64 * i, j = 32 * kk + e / (N / 8);
             const int64_t rj = rows(j < k ? j : 0);
             const uint16_t *src = j < k ? bB + (rj * G + g) * N : Bin;
             br[i] = *reinterpret_cast<const uint4 *>(src + 8 * (e % (N / 8)));
         }
     };
-    auto store_block = [&](int kb, bool withB, const uint4 &xr, const uint4 (&br)[BPL]) {
+    auto store_block = [&](int kk, const uint4 &xr, const uint4 (&br)[BPL]) {
         {
-            const int r = lane >> 2;
-            *reinterpret_cast<uint4 *>(lds + L.cX + (r * L.cXS + 8 * (lane & 3)) * 2) =
-                keep_if(16 * kb + r <= k, xr);
+            const int r = lane >> 1;
+            *reinterpret_cast<uint4 *>(lds + L.cX + (r * L.cXS + 8 * (lane & 1)) * 2) =
+                keep_if(32 * kk + r <= k, xr);
         }
-        if (!withB)
-            return;
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
             const int e = lane + 64 * i, r = e / (N / 8);
             *reinterpret_cast<uint4 *>(lds + L.cB + (r * L.cBS + 8 * (e % (N / 8))) * 2) =
-                keep_if(16 * kb + r <= k, br[i]);
+                keep_if(32 * kk + r <= k, br[i]);
         }
     };
 
 #pragma unroll 1
-    for (int pt = 0; pt < NPT; ++pt) {
-        const bool newB = nreal > 1 || pt == 0;
+    for (int ps = 0; ps < NPS; ++ps) {
         uint4 xa, ba[BPL];
-        load_block(pt, 0, newB, xa, ba);
-        // the old tiles in the accumulator layout S^T[n][p], p = 32 pt + c,
-        // n = 32 nt + 8 q + 4 gl + (0..3), decayed to the chunk end
-        f32x16 acc[NNT];
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = *reinterpret_cast<const float4 *>(
-                    st + (int64_t)(32 * pt + c) * N + 32 * nt + 8 * q + 4 * gl);
-                acc[nt][4 * q] = v.x * dec;
-                acc[nt][4 * q + 1] = v.y * dec;
-                acc[nt][4 * q + 2] = v.z * dec;
-                acc[nt][4 * q + 3] = v.w * dec;
-            }
-        for (int kb = 0; kb < nreal; ++kb) {
-            store_block(kb, newB, xa, ba);
-            if (kb + 1 < nreal)
-                load_block(pt, kb + 1, true, xa, ba);
-            const int r0 = 8 * gl;
-            const i16x8 xv = lds_tr8(lds, L.cX, L.cXS, r0, r0 + 4, 16 * ((lane >> 4) & 1));
-            const float4 w0 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0);
-            const float4 w1 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0 + 4);
-            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            bf16x8 bhi, blo;
-            split_wx(xv, ws, bhi, blo);
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
-                const bf16x8 aop = as_bf16x8(
-                    lds_tr8(lds, L.cB, L.cBS, r0, r0 + 4, 32 * nt + 16 * ((lane >> 4) & 1)));
-                state_step(aop, bhi, blo, acc[nt]);
-            }
-        }
-        if (nreal < nkb)
-            *reinterpret_cast<uint4 *>(lds + L.cX + ((lane >> 2) * L.cXS + 8 * (lane & 3)) * 2) =
-                make_uint4(0, 0, 0, 0);
-        for (int kb = nreal; kb < nkb; ++kb) {
-            const int r0 = 8 * gl;
-            const i16x8 xv = lds_tr8(lds, L.cX, L.cXS, r0, r0 + 4, 16 * ((lane >> 4) & 1));
-            const float4 w0 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0);
-            const float4 w1 = *reinterpret_cast<const float4 *>(w + 16 * kb + r0 + 4);
-            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            bf16x8 bhi, blo;
-            split_wx(xv, ws, bhi, blo);
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt)
-                state_step(as_bf16x8(xv), bhi, blo, acc[nt]);
+        load_block(ps, 0, xa, ba);
+        // the slab's old tiles, decayed to the chunk end
+        f32x4 acc[NT];
+        slab_io<P, N, NT, true>(st, ps, 0, acc);
+        slab_scale<NT>(acc, dec);
+        for (int kk = 0; kk < nkk; ++kk) {
+            store_block(kk, xa, ba);
+            if (kk + 1 < nkk)
+                load_block(ps, kk + 1, xa, ba);
+            state_kstep<NT>(lds, L.cX, L.cXS, 0, L.cB, L.cBS, 0, 0, w + 32 * kk, acc);
         }
         // the new tiles of the fp32 state and of its bf16 copy
-        const int p = 32 * pt + c;
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = 32 * nt + 8 * q + 4 * gl;
-                const f32x16 &t = acc[nt];
-                *reinterpret_cast<float4 *>(st + (int64_t)p * N + n) =
-                    make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
-                *reinterpret_cast<uint2 *>(sbf + state_bf_index(p, n, P)) = make_uint2(
-                    bf16_rne(t[4 * q]) | ((uint32_t)bf16_rne(t[4 * q + 1]) << 16),
-                    bf16_rne(t[4 * q + 2]) | ((uint32_t)bf16_rne(t[4 * q + 3]) << 16));
-            }
+        slab_io<P, N, NT, false>(st, ps, 0, acc);
+        slab_bf16<P, NT>(acc, ps, 0, lds, -1, 0, sbf);
     }
 }
 
@@ -1586,7 +1722,8 @@ void k_decode_mfma(DecodeArgs a) {
 // Chunk-state update of the slots whose chunk the decode step filled (the
 // list k_decode_commit finds in the cache's work array): one head of one
 // slot per workgroup at a time, with the prefill's chunk arithmetic (the
-// per-row quantities of chunk_scalars, chunk_state_update on 32 x 32 tiles),
+// per-row quantities of chunk_scalars, the state tiles of state_kstep with
+// the prefill's four-wave split),
 // on the chunk's Q tokens, all in the slot buffer now. Writes the new fp32
 // boundary state and its bf16 copy. The last workgroup to finish empties the
 // list.
@@ -1596,7 +1733,7 @@ template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     using TD = typename DT::T;
-    constexpr int NW = kCommitWaves;
+    static_assert(kCommitWaves == kStateWaves, "the commit's waves are the state tiles' owners");
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
@@ -1626,8 +1763,11 @@ __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs 
         const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
         const TD *bdt = static_cast<const TD *>(a.buf_dt);
         float *st = a.cache_state + ((int64_t)slot * H + h) * PN;
-        f32x16 S[StateTiles<P, N, NW>::per_wave];
-        state_io<P, N, NW, true>(st, S);
+        using SL = Slab<P, N>;
+        int ps, nt0;
+        SL::own(threadIdx.x >> 6, ps, nt0);
+        f32x4 S[SL::NT];
+        slab_io<P, N, SL::NT, true>(st, ps, nt0, S);
         const int64_t rd = rows(threadIdx.x < Q ? threadIdx.x : 0);
         const float dt_raw = DT::ld(bdt, rd * H + h);
         __syncthreads();  // the previous entry's LDS reads are done
@@ -1636,13 +1776,13 @@ __global__ __launch_bounds__(64 * kCommitWaves) void k_decode_commit(DecodeArgs 
         chunk_scalars(dt_raw, Q, a.A[h] * kLog2e, a.dt_bias ? a.dt_bias[h] : 0.0f, d.softplus,
                       true, lds, L);
         __syncthreads();
-        chunk_state_update<P, N, NW>(Qp, Q, lds, L, S);
-        state_io<P, N, NW, false>(st, S);
-        state_to_lds<P, N, NW>(lds, L, S);
-        __syncthreads();
-        state_bf_from_lds<P, N>(static_cast<uint16_t *>(a.cache_state_bf) +
-                                    ((int64_t)slot * H + h) * PN,
-                                lds, L);
+        slab_scale<SL::NT>(S, fexp2(reinterpret_cast<const float *>(lds + L.lam)[Q - 1]));
+        for (int kk = 0; kk < Qp / 32; ++kk)
+            state_kstep<SL::NT>(lds, L.X, L.XS, 16 * ps, L.B, L.BS, 32 * kk, nt0,
+                                reinterpret_cast<const float *>(lds + L.w) + 32 * kk, S);
+        slab_io<P, N, SL::NT, false>(st, ps, nt0, S);
+        slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0,
+                             static_cast<uint16_t *>(a.cache_state_bf) + ((int64_t)slot * H + h) * PN);
     }
     // The workgroups that had entries ([0, W)) count themselves out, in 32
     // groups (blockIdx % 32) and then once per group, so that no counter
@@ -1969,8 +2109,7 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int P, int N, class DT, bool PG>
 hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
-    const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
-    const MLayout L(Qp, P, N);
+    const MLayout L(kMaxQ, P, N);   // scan_one's layout: full-height tiles for every chunk size
     hipError_t e;
     if (a.only_cross || a.no_y) {
         // the crossing-draft sweep adds its pair list after the layout
@@ -1986,9 +2125,18 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
         k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), bytes, stream>>>(a);
         return hipGetLastError();
     }
-    if ((e = set_lds(k_scan_mfma<P, N, DT, PG>, L.bytes)) != hipSuccess)
+    if (a.replay) {
+        if ((e = set_lds(k_scan_mfma<P, N, DT, PG, true>, L.bytes)) != hipSuccess)
+            return e;
+        k_scan_mfma<P, N, DT, PG, true>
+            <<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
+        return hipGetLastError();
+    }
+    if (PG)
+        return hipErrorInvalidValue;   // paged buffers belong to replay calls
+    if ((e = set_lds(k_scan_mfma<P, N, DT, false, false>, L.bytes)) != hipSuccess)
         return e;
-    k_scan_mfma<P, N, DT, PG>
+    k_scan_mfma<P, N, DT, false, false>
         <<<dim3(a.d.H * a.S), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
     return hipGetLastError();
 }
