@@ -128,22 +128,23 @@ __device__ __forceinline__ bf16x8 lds_b128(const char *lds, int byte_off) {
     return *reinterpret_cast<const bf16x8 *>(lds + byte_off);
 }
 
-// Transposed fetch of an MFMA operand from a row-major bf16 tile: the lane
-// gets rows r0 + 0..3 (read 1) and r1 + 0..3 (read 2) of column c, where
-// r0/r1 are the rows of the lane's k-group and c = c16 + (lane % 16). The
-// 16 lanes of a group supply addresses row (lane%16)/4, columns 4*(lane%4).
-// Returned as raw bf16 bit patterns (elements are read out individually by
-// the state contraction).
-__device__ __forceinline__ i16x8 lds_tr8(const char *lds, int base, int stride, int r0,
-                                         int r1, int c16) {
-    const int l = lane_id() & 15;
-    const int rr = l >> 2, cc = c16 + 4 * (l & 3);
-    const lds_char *p = (const lds_char *)lds;
-    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(p + base + ((r0 + rr) * stride + cc) * 2));
-    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(p + base + ((r1 + rr) * stride + cc) * 2));
-    i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Transposed fetch of an MFMA operand from a row-major bf16 tile (row
+// stride `stride` elements): each 16-lane group reads a 4-row x 16-column
+// block, lane l of the group supplying row l / 4, columns 4 (l % 4) .. +3,
+// and receives rows 0..3 of one column. tr_lane is that per-lane byte
+// offset; lds_tr8 fetches the blocks at byte addresses a and a + d (plus
+// the lane offset `la`, which may include further per-lane terms), giving
+// the lane 8 k-values of its column. Returned as raw bf16 bit patterns.
+__device__ __forceinline__ int tr_lane(int lane, int stride) {
+    const int l = lane & 15;
+    return ((l >> 2) * stride + 4 * (l & 3)) * 2;
+}
+
+__device__ __forceinline__ i16x8 lds_tr8(const char *lds, int la, int a, int d) {
+    const lds_char *p = (const lds_char *)lds + la;
+    i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + a));
+    i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + a + d));
+    i16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return v;
 }
 
@@ -188,8 +189,8 @@ __device__ __forceinline__ f32x16 gram_block(F ba, const bf16x8 *cf) {
 // G[t][s] for s = s_base + 8q + 4g + e; m = G 2^(l_t - u_s) for s <= t and +0
 // otherwise (selected, never multiplied).
 __device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const float *uu, int s_base,
-                                       int t, uint32_t (&mb)[8]) {
-    const int g = lane_id() >> 5;
+                                       int t, uint32_t (&mb)[8], int lane) {
+    const int g = lane >> 5;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int s0 = s_base + 8 * q + 4 * g;
@@ -209,8 +210,8 @@ __device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const floa
 // Weights of an earlier s-block: (G alpha) beta_s with alpha = 2^(l_t - c)
 // and beta_s = 2^(c - u_s), c = l at the end of the s-block.
 __device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float *bt, int s_base,
-                                      uint32_t (&mb)[8]) {
-    const int g = lane_id() >> 5;
+                                      uint32_t (&mb)[8], int lane) {
+    const int g = lane >> 5;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int s0 = s_base + 8 * q + 4 * g;
@@ -226,19 +227,19 @@ __device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float
 // at xrow0); mb[4 half .. 4 half + 3] holds the matching M^T rows.
 template <int PT0, int PT1>
 __device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const char *lds, int xbase,
-                                              int xs, int xrow0, f32x16 *acc) {
-    const int lane = lane_id();
+                                              int xs, int xrow0, f32x16 *acc, int lane) {
     const int g = lane >> 5;
+    // lane terms: the k-group's rows 4g.., the 16-column half of the p-tile
+    const int la = tr_lane(lane, xs) + (4 * g * xs + 16 * ((lane >> 4) & 1)) * 2;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 bv = {mb[4 * half], mb[4 * half + 1], mb[4 * half + 2], mb[4 * half + 3]};
         const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
-        const int r0 = xrow0 + 16 * half + 4 * g;
 #pragma unroll
         for (int pt = PT0; pt < PT1; ++pt) {
-            const int c16 = 32 * pt + 16 * ((lane >> 4) & 1);
-            const bf16x8 aop = as_bf16x8(lds_tr8(lds, xbase, xs, r0, r0 + 8, c16));
+            const int a = xbase + ((xrow0 + 16 * half) * xs + 32 * pt) * 2;
+            const bf16x8 aop = as_bf16x8(lds_tr8(lds, la, a, 8 * xs * 2));
             acc[pt] = mfma(aop, bop, acc[pt]);
         }
     }
@@ -292,10 +293,10 @@ __device__ __forceinline__ void tblock_part(int tau, int sg0, int sg1, const bf1
         const f32x16 gt = gram(sg);
         uint32_t mb[8];
         if (sg == tau)
-            m_diag(gt, lam_t, uu, 32 * sg, t, mb);
+            m_diag(gt, lam_t, uu, 32 * sg, t, mb, lane);
         else
-            m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb);
-        mx_accumulate<PT0, PT1>(mb, lds, L.X, L.XS, 32 * sg, acc);
+            m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb, lane);
+        mx_accumulate<PT0, PT1>(mb, lds, L.X, L.XS, 32 * sg, acc, lane);
     }
 }
 
@@ -365,17 +366,20 @@ template <int NT>
 __device__ __forceinline__ void state_kstep(const char *lds, int xb, int xs, int xc, int bb,
                                             int bs, int row0, int nt0, const float *wk,
                                             f32x4 (&acc)[NT]) {
-    const int q = lane_id() >> 4;
-    const int r0 = row0 + 8 * q;
-    const i16x8 xv = lds_tr8(lds, xb, xs, r0, r0 + 4, xc);
+    const int lane = lane_id();
+    const int q = lane >> 4;
+    const i16x8 xv = lds_tr8(lds, tr_lane(lane, xs) + 8 * q * xs * 2, xb + (row0 * xs + xc) * 2,
+                             4 * xs * 2);
     const float4 w0 = *reinterpret_cast<const float4 *>(wk + 8 * q);
     const float4 w1 = *reinterpret_cast<const float4 *>(wk + 8 * q + 4);
     const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     bf16x8 bhi, blo;
     split_wx(xv, ws, bhi, blo);
+    const int lab = tr_lane(lane, bs) + 8 * q * bs * 2;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const bf16x8 a = as_bf16x8(lds_tr8(lds, bb, bs, r0, r0 + 4, 16 * (nt0 + i)));
+        const bf16x8 a = as_bf16x8(lds_tr8(lds, lab, bb + (row0 * bs + 16 * (nt0 + i)) * 2,
+                                           4 * bs * 2));
         acc[i] = mfma16(a, bhi, acc[i]);
         acc[i] = mfma16(a, blo, acc[i]);
     }
@@ -525,10 +529,9 @@ __device__ __forceinline__ void stage_stream(const char *gbase, int gstride, int
     }
 }
 
-template <int P, int N, class DT, bool PG>
+template <int P, int N, int NWV, class DT, bool PG>
 __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h0, int wv,
                                            char *lds, const MLayout &L) {
-    constexpr int NWV = kStateWaves;
     constexpr int XRB = (P + kPad) * 2, BRB = (N + kPad) * 2;   // row strides, bytes
     constexpr int XK = kSlab * XRB / 1024, BK = kSlab * BRB / 1024;
     static_assert(XK * 1024 == kSlab * XRB && BK * 1024 == kSlab * BRB, "1 KB pieces");
@@ -789,12 +792,15 @@ __device__ __forceinline__ int xcd_local_index(int bid, int nblocks) {
 // Prefill workgroups have 12 waves (three per SIMD; wave w runs on SIMD
 // w % 4). Waves 0..3 are the state waves: each owns a quarter of the fp32
 // state in registers and updates it over the chunk, and they stage the
-// chunk rows into LDS; wave 0 also computes the next chunk's per-row
-// quantities (into the other set of per-row arrays). Waves 4..11 each
-// compute the outputs of one 32-row t-block: with 8 t-blocks wave 4 + k
-// takes 7 - k and wave 8 + k takes k, so every SIMD has the same causal work
-// and the heavy t-block on its older wave.
+// chunk rows into LDS. Waves 4..11 each compute the outputs of one 32-row
+// t-block: with 8 t-blocks wave 4 + k takes 7 - k and wave 8 + k takes k, so
+// every SIMD has the same causal work and the heavy t-block on its older
+// wave. Wave 8 also computes the next chunk's per-row quantities (into the
+// other set of per-row arrays) once its own t-block is done.
 constexpr int kPrefillWaves = 12;
+// the t-block wave that also computes the next chunk's per-row arrays:
+// t-block 0 with eight t-blocks (no work in phase 2), idle with four or fewer
+constexpr int kScalarWave = kStateWaves + 4;
 
 __device__ __forceinline__ int wave_tblock(int nT, int wave) {
     const int i = wave - kStateWaves;
@@ -893,9 +899,9 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     // all staged by the state waves:
     //  - chunk size 256: rows 0..127 (slab A) in half 0, 128..255 (slab B)
     //    in half 1. Phase 1: every t-block takes its s-blocks 0..3 (t-blocks
-    //    0..3 finish), the state waves their K steps 0..3 while they stage
-    //    slab B. Phase 2: t-blocks 4..7 take s-blocks 4.., the state waves
-    //    their K steps 4..7 while they stage the next chunk's slab A. Two
+    //    0..3 finish), the state waves stage slab B and take their K steps
+    //    0..3. Phase 2: t-blocks 4..7 take s-blocks 4.., the state waves
+    //    stage the next chunk's slab A and take their K steps 4..7. Two
     //    barriers per chunk.
     //  - chunk size <= 128: chunk c in half c % 2, the next chunk staged in
     //    the other half during this one. One barrier.
@@ -907,9 +913,9 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
         set_chunk(0);
         if (swave) {
             slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.S, L.SS, nullptr);
-            stage_slab<P, N>(v, 0, 0, wave, lds, L);
+            stage_slab<P, N, kStateWaves>(v, 0, 0, wave, lds, L);
             if (two)
-                stage_slab<P, N>(v, kSlab, kSlab, wave, lds, L);
+                stage_slab<P, N, kStateWaves>(v, kSlab, kSlab, wave, lds, L);
             if (wave == 0) {
                 TD rawdt[4];
                 load_dt<DT>(v, rawdt);
@@ -940,42 +946,43 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             const MView<DT, PG> vc = v;
             if (more)
                 set_chunk(c + 1);
-            // the next chunk's raw dt; staging: this chunk's slab B (two
-            // slabs), or the next chunk in the other half
-            TD rawdt[4];
-            if (wave == 0 && more)
-                load_dt<DT>(v, rawdt);
+            const int nk = Qp / 32, nk1 = two ? kSlab / 32 : nk;
+            // K steps [k0, k1) of this chunk, through tile pointer t
+            auto ksteps = [&](char *t, int k0, int k1) {
+                const float *w = reinterpret_cast<const float *>(t + Lc.w);
+                for (int kk = k0; kk < k1; ++kk)
+                    state_kstep<SL::NT>(t, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
+                                        w + 32 * kk, S);
+            };
+            // Phase 1 (or the only phase): staging this chunk's slab B (two
+            // slabs) or the next chunk into the other half, then the K steps
+            // over the rows that are in
             if (two) {
                 if (c > 0)
-                    stage_slab<P, N>(vc, kSlab, kSlab, wave, lds, L);
+                    stage_slab<P, N, kStateWaves>(vc, kSlab, kSlab, wave, lds, L);
             } else if (more) {
-                stage_slab<P, N>(v, 0, kSlab * ((c + 1) & 1), wave, lds, L);
+                stage_slab<P, N, kStateWaves>(v, 0, kSlab * ((c + 1) & 1), wave, lds, L);
             }
-            const float *w = reinterpret_cast<const float *>(lds + Lc.w);
-            const int nk = Qp / 32, nk1 = two ? kSlab / 32 : nk;
             if (upd) {
                 slab_scale<SL::NT>(
                     S, fexp2(reinterpret_cast<const float *>(lds + Lc.lam)[n_valid - 1]));
-                for (int kk = 0; kk < nk1; ++kk)
-                    state_kstep<SL::NT>(lds, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
-                                        w + 32 * kk, S);
+                ksteps(lds, 0, nk1);
             }
+            if (!two && upd && more)
+                slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.chunk((c + 1) & 1, 0).S, L.SS, nullptr);
             if (two) {
                 wait_vmcnt<0>();
                 __syncthreads();   // phase 2: slab B is in, slab A is free
+                // staging the next chunk's slab A, the remaining K steps and
+                // the next chunk's read-out copy
                 if (more)
-                    stage_slab<P, N>(v, 0, 0, wave, lds, L);
+                    stage_slab<P, N, kStateWaves>(v, 0, 0, wave, lds, L);
                 if (upd)
-                    for (int kk = nk1; kk < nk; ++kk)
-                        state_kstep<SL::NT>(lds, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
-                                            w + 32 * kk, S);
+                    ksteps(lds, nk1, nk);
+                if (upd && more)
+                    slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.chunk((c + 1) & 1, 0).S, L.SS,
+                                         nullptr);
             }
-            // the next chunk's read-out copy and per-row arrays
-            if (upd && more)
-                slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.chunk((c + 1) & 1, 0).S, L.SS, nullptr);
-            if (wave == 0 && more)
-                chunk_scalars_wave<DT>(rawdt, v.n_valid, A2_h, bias, d.softplus, lds,
-                                       L.buf((c + 1) & 1));
             wait_vmcnt<0>();
             __syncthreads();   // end of chunk c
         }
@@ -1031,6 +1038,14 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
                     if (more)
                         load_c(v);
                 }
+            }
+            // the next chunk's per-row arrays (the scalar wave has no phase-2
+            // t-block work, so the dt load's latency is not in its way)
+            if (wave == kScalarWave && more) {
+                TD rawdt[4];
+                load_dt<DT>(v, rawdt);
+                chunk_scalars_wave<DT>(rawdt, v.n_valid, A2_h, bias, d.softplus, lds,
+                                       L.buf((c + 1) & 1));
             }
             __syncthreads();   // end of chunk c
         }
@@ -1399,9 +1414,9 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<
         }
         uint32_t mb[8];
         if (sg == tau)
-            m_diag(gt, cy.lam_k, uu, 32 * sg, k, mb);
+            m_diag(gt, cy.lam_k, uu, 32 * sg, k, mb, lane);
         else
-            m_off(gt, fexp2(cy.lam_k - lam[32 * sg + 31]), bt, 32 * sg, mb);
+            m_off(gt, fexp2(cy.lam_k - lam[32 * sg + 31]), bt, 32 * sg, mb, lane);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             mb[q] = col ? mb[q] : 0u;
@@ -1418,7 +1433,7 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<
         }
         if (sg + 2 <= tau)
             load_x_tile<P>(bx, rows, xin, H, h, k, sg + 2, xb);
-        mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, cy.acc);
+        mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, cy.acc, lane);
     }
 
     // y row k: fmaf(D, x, Y^T) -> bf16, -0 -> +0 (lanes of column k % 32);
@@ -1993,9 +2008,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
         auto accumulate = [&](int sg, const f32x16 &gt, const uint4 (&xr)[XPL]) {
             uint32_t mb[8];
             if (sg == tau)
-                m_diag(gt, lam_t, uu, 32 * sg, t, mb);
+                m_diag(gt, lam_t, uu, 32 * sg, t, mb, lane);
             else
-                m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb);
+                m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb, lane);
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 mb[q] = outc ? mb[q] : 0u;
@@ -2005,7 +2020,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
                 *reinterpret_cast<uint4 *>(lds + L.X + (r * L.XS + 8 * q) * 2) =
                     keep_if(32 * sg + r <= last, xr[i]);
             }
-            mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc);
+            mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc, lane);
         };
         if constexpr (gshare) {
             // the C.B^T blocks of this t-block, split between the waves
