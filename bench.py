@@ -42,9 +42,12 @@ METRIC = "SSD prefill tokens/s + replay-decode steps/s at B=256; % HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 PAGE_TOKENS = 64             # rows per buffer page in the paged replay-decode leg
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
+# MI355X fp32 vector peak without packed fp32 (the library is built with
+# packed fp32 instructions off, which halves the 157.3 TFLOP/s packed figure)
+FP32_VALU_PEAK_TFLOPS = 78.6
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
-                  "ssd_internal.hpp", "ssd_conv.hip"]
+                  "ssd_internal.hpp", "ssd_conv.hip", "ssd_scratch.hip"]
+W1A_COPIES = 48              # input copies the 1 x 2048 latency leg rotates through
 CONV_W = 4                   # conv kernel width of the conv legs
 SPEC_BATCH, SPEC_T = 512, 4  # speculative verification: sequences, drafts each
 RECOVER_T = 255              # packed-history recovery: generated tokens replayed
@@ -152,7 +155,7 @@ def load_traffic(sha):
 
 
 CALIB_BYTES = 512 * 2 ** 20
-PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16, false>"
+PREFILL_KERNEL = "k_scan_mfma<64, 128, ssd::IoBF16, false, false>"
 COPY_KERNEL = "copyBuffer"
 DECODE_KERNEL = "k_decode_mfma<64, 128, ssd::IoBF16, false, true>"
 
@@ -290,22 +293,33 @@ def other_workloads(erd, synth, torch, dev, warmup, steps):
         return e0.elapsed_time(e1) / 1e3 / n   # seconds per call
 
     out = {}
-    # W1a: one sequence
+    # W1a: one sequence. The launches rotate through W1A_COPIES copies of the
+    # inputs and outputs (about 0.45 GB), more than the last-level cache
+    # holds, so each launch reads its inputs from HBM.
     H, G, P, N, Q, T = 32, 1, 64, 128, 256, 2048
     sh = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
     hp = synth.make_head_params(H, 0)
     A, D, bias = (torch.from_numpy(v).to(dev) for v in (hp.A, hp.D, hp.dt_bias))
-    x, dt, B, C = synth.make_tokens_torch(T, H, G, P, N, 7, dev)
+    copies = []
+    for i in range(W1A_COPIES):
+        xi, dti, Bi, Ci = synth.make_tokens_torch(T, H, G, P, N, 7 + i, dev)
+        copies.append((xi, dti, Bi, Ci, torch.empty_like(xi),
+                       torch.empty((1, H, P, N), dtype=torch.float32, device=dev)))
     cu_host = synth.cu_seqlens([T])
     cu = torch.from_numpy(cu_host).to(dev)
-    y = torch.empty_like(x)
-    bnd = torch.empty((1, H, P, N), dtype=torch.float32, device=dev)
-    t = timed(lambda: erd.ssd_prefill_varlen(sh, cu, x, dt, A, B, C, D, bias, y=y,
-                                             boundary_state=bnd, cu_seqlens_host=cu_host,
-                                             want_final=False), steps)
+    rot = [0]
+
+    def w1a():
+        xi, dti, Bi, Ci, yi, bi = copies[rot[0] % W1A_COPIES]
+        rot[0] += 1
+        erd.ssd_prefill_varlen(sh, cu, xi, dti, A, Bi, Ci, D, bias, y=yi, boundary_state=bi,
+                               cu_seqlens_host=cu_host, want_final=False)
+
+    t = timed(w1a, max(steps, W1A_COPIES))
     out["prefill_1x2048"] = {"us_per_launch": 1e6 * t, "tokens_per_s": T / t,
-                             "hbm_frac": prefill_bytes(T, 1, H, G, P, N) / t / 1e9 / HBM_PEAK_GBS}
-    del x, dt, B, C, y
+                             "hbm_frac": prefill_bytes(T, 1, H, G, P, N) / t / 1e9 / HBM_PEAK_GBS,
+                             "input_copies_rotated": W1A_COPIES}
+    del copies
 
     # W2: grouped heads, pack x 64
     H, G = 64, 8
@@ -386,11 +400,28 @@ def other_workloads(erd, synth, torch, dev, warmup, steps):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(x, dt, B, C, hp, Q, T, target_s=10.0):
-    """Time the fp64 oracle on a bounded sample of the prefill workload
-    (whole 2048-token sequences, read back exactly from the device)."""
-    from exact_replay_decode_amd import to_f64
-    from oracle import scan, threads
+    """Time the fp64 oracle, as it is, on bounded samples of the workloads:
+    the prefill (whole 2048-token sequences read back exactly from the
+    device, all host threads; the headline figure), one 2048-token sequence
+    on one thread, a sequence of each length of the grouped-heads pack, the
+    B=256 decode step and the 24-layer stack's decode step at batch 1 (the
+    last three from host-drawn inputs of the same distributions; a decode
+    step is one token per sequence through the recurrence from a carried
+    state)."""
+    from exact_replay_decode_amd import synth, to_f64
+    from oracle import scan, set_threads, threads
 
     def run(n):
         xs, dts = to_f64(x[:n * T]), to_f64(dt[:n * T])
@@ -400,13 +431,85 @@ def cpu_baseline(x, dt, B, C, hp, Q, T, target_s=10.0):
         scan(xs, dts, hp.A, Bs, Cs, cu, Q, D=hp.D, dt_bias=hp.dt_bias)
         return time.perf_counter() - t0
 
+    cores = threads()
     t1 = run(1)
-    n = int(max(1, min(256, round(target_s / max(t1, 1e-3)))))
+    n = int(max(1, min(x.shape[0] // T, round(target_s / max(t1, 1e-3)))))
     tn = run(n) if n > 1 else t1
-    return {"value": n * T / tn, "unit": "tokens/s", "cores": threads(), "kind": "oracle",
+    set_threads(1)
+    try:
+        t_single = run(1)
+    finally:
+        set_threads(cores)
+
+    def host_scan(lengths, H, G, seed, init=False, reps=1):
+        """Seconds per scan of host-drawn sequences of the given lengths
+        (P=64, N=128, chunk 256), from carried states when init is set."""
+        P, N = 64, 128
+        hpp = synth.make_head_params(H, seed)
+        tok = synth.concat([synth.make_tokens(L, H, G, P, N, seed, stream=i)
+                            for i, L in enumerate(lengths)]).f64()
+        h0 = (np.random.default_rng(seed).standard_normal((len(lengths), H, P, N)) * 0.1
+              if init else None)
+        cu = synth.cu_seqlens(lengths)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            scan(*tok[:2], hpp.A, *tok[2:], cu, 256, D=hpp.D, dt_bias=hpp.dt_bias, init=h0)
+        return (time.perf_counter() - t0) / reps
+
+    # grouped pack: one sequence of each length (2048 tokens), H=64, G=8
+    t_w2 = host_scan(list(GROUPED_PACK), 64, 8, 21)
+    # decode at B=256 (H=32): 32 sequences x 1 token from carried states
+    t_w3 = host_scan([1] * 32, 32, 1, 22, init=True, reps=4) * (256 / 32)
+    # 24-layer stack at batch 1 (H=24): one layer's token, times 24
+    t_w4 = host_scan([1], 24, 1, 23, init=True, reps=16) * STACK_LAYERS
+    return {"value": n * T / tn, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of 256 sequences x {T} tokens of the prefill workload "
                       f"({tn:.1f} s, fp64 sequential recurrence, OpenMP over sequence x head)",
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model(),
+            "single_thread_1x2048": {"tokens_per_s": T / t_single, "cores": 1,
+                                     "seconds": t_single},
+            "grouped_pack": {"tokens_per_s": sum(GROUPED_PACK) / t_w2, "cores": cores,
+                             "sample": "one sequence of each pack length (2048 tokens), "
+                                       "H=64 G=8"},
+            "decode_b256": {"steps_per_s": 1.0 / t_w3, "cores": cores,
+                            "sample": "32 of 256 sequences x 1 token from carried states, "
+                                      "4 repeats, scaled to 256"},
+            "layer_stack_24": {"steps_per_s": 1.0 / t_w4, "cores": cores,
+                               "sample": "one layer's decode token (H=24) from a carried "
+                                         "state, 16 repeats, times 24 layers"}}
+
+
+def copy_gbs(torch, dev, reps=5):
+    """Device-to-device copy of CALIB_BYTES (read + write), GB/s: the
+    measured ceiling for streaming kernels on this GPU."""
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * CALIB_BYTES * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    return gbs
+
+
+def load_decode_ratio(sha):
+    """Counted over algorithmic bytes of the B=256 chunk-256 decode kernel,
+    from the committed counter summary, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "decode_b256_q256_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha") != sha:
+        return None
+    return rec.get("traffic_over_algorithmic")
 
 
 def main():
@@ -681,6 +784,29 @@ def main():
     def span(i, j):
         return sum(e[i].elapsed_time(e[j]) for e in evs) / 1e3   # seconds, summed
 
+    def spread(pairs, per=1):
+        """Per bench step: the leg's time (the sum over the event pairs), ms
+        per unit (per = units per bench step): mean, p10, p90 over steps."""
+        v = np.array([sum(e[i].elapsed_time(e[j]) for i, j in pairs) for e in evs]) / per
+        return {"ms_mean": float(v.mean()), "ms_p10": float(np.percentile(v, 10)),
+                "ms_p90": float(np.percentile(v, 90))}
+
+    legs = {
+        "prefill": spread([(0, 1)]),
+        "commit": spread([(1, 2)]),
+        "replay_decode_q256_per_step": spread([(2, 3)], R),
+        "ssu_per_step": spread([(3, 4)], R),
+        "replay_decode_q16_per_step": spread([(4, 5)], R),
+        "replay_decode_q256_paged_per_step": spread([(5, 6)], R),
+        "conv_prefill": spread([(6, 7)]),
+        "conv_update_per_step": spread([(7, 8)], R),
+        "verify_per_round": spread([(8 if r == 0 else 8 + 2 * r, 9 + 2 * r) for r in range(R)],
+                                   R),
+        "accept_per_round": spread([(9 + 2 * r, 10 + 2 * r) for r in range(R)], R),
+        "recovery": spread([(8 + 2 * R, 9 + 2 * R)]),
+    }
+    ceiling = copy_gbs(torch, dev)
+
     others = other_workloads(erd, synth, torch, dev, args.warmup, args.steps)
 
     K = args.steps
@@ -705,6 +831,7 @@ def main():
     traffic = load_traffic(sha)
     dec_steps = K * R
     dec256_gbs = bytes_decode256 / t_dec256 / 1e9
+    dec_ratio = load_decode_ratio(sha)
     dec16_gbs = bytes_decode16 / t_dec16 / 1e9
     decpg_gbs = bytes_decodepg / t_decpg / 1e9
     conv_gbs = conv_prefill_bytes(S * T, S, cd, CONV_W) * K / t_conv / 1e9
@@ -746,11 +873,19 @@ def main():
             "avg_launch_ms": 1e3 * prefill_launch_s,
             "mfma_util": pf / prefill_launch_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "algorithmic_flops_per_launch": pf,
+            "measured_copy_gbs": ceiling,
+            "frac_of_measured_copy": achieved / ceiling,
         },
         "decode": {
             "replay_q256_steps_per_s": dec_steps / t_dec256,
             "replay_q256_hbm_gbs": dec256_gbs,
             "replay_q256_frac": dec256_gbs / HBM_PEAK_GBS,
+            # the same steps scored on the bytes the counters see (the
+            # committed decode traffic summary's counted / algorithmic ratio)
+            "replay_q256_counter_frac": (dec256_gbs * dec_ratio / HBM_PEAK_GBS
+                                         if dec_ratio else None),
+            "replay_q256_us_per_step": 1e6 * t_dec256 / dec_steps,
+            "replay_q16_us_per_step": 1e6 * t_dec16 / dec_steps,
             "replay_q16_steps_per_s": dec_steps / t_dec16,
             "replay_q16_hbm_gbs": dec16_gbs,
             "replay_q16_frac": dec16_gbs / HBM_PEAK_GBS,
@@ -790,11 +925,14 @@ def main():
             "hbm_gbs": recover_gbs,
             "frac": recover_gbs / HBM_PEAK_GBS,
             # sequential in tokens: bound by fp32 vector arithmetic and its
-            # latency, 5 flops per state element and token
+            # latency, 5 flops per state element and token, against the fp32
+            # vector peak without packed instructions
             "alu_tflops": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12,
             "alu_frac": 5 * H * P * N * S * RECOVER_T * K / t_recover / 1e12 / FP32_VALU_PEAK_TFLOPS,
+            "alu_peak_tflops": FP32_VALU_PEAK_TFLOPS,
         },
         "other_workloads": others,
+        "legs": legs,
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,
         "kernel_source_sha": sha,

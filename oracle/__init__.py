@@ -13,4 +13,4 @@ library.
 - ``ssu``: the recurrent update with the state rounded to the cache dtype
   after every token (packed-history recovery), in numpy.
 """
-from .oracle import scan, threads, ensure_built  # noqa: F401
+from .oracle import scan, threads, set_threads, ensure_built  # noqa: F401

@@ -35,12 +35,20 @@ def _load():
                                         dp, dp, dp, dp, dp, i32, dp, dp, dp,
                                         dp, dp, dp, lp, dp, i32]
         lib.ssd_oracle_threads.restype = ctypes.c_int
+        lib.ssd_oracle_set_threads.restype = None
+        lib.ssd_oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
 
 def threads() -> int:
     return int(_load().ssd_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of later scans (timing of the oracle itself; results do not
+    depend on it)."""
+    _load().ssd_oracle_set_threads(int(n))
 
 
 def _dptr(a):

@@ -57,6 +57,18 @@ int ssd_oracle_threads(void)
 #endif
 }
 
+/* Threads of later scans (n >= 1): timing runs of the oracle itself, e.g.
+ * one core against the host's all. The arithmetic does not depend on it. */
+void ssd_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Returns 0 on success, -1 on bad arguments, -2 when out of memory.
  * init, D, dt_bias, final_state, boundary_state, boundary_len and
