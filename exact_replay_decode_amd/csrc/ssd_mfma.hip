@@ -1156,10 +1156,10 @@ struct DLayout {
         gc = o;   o += (kMaxQ / 32) * 32 * 4;   // C.B^T column k % 32 per s-block
         X = o;    o += 32 * XS * 2;              // padded 32-row x tile
         // with the chunk-state update in the same launch: its 32-row blocks
-        // (x: the 16 columns of one p-slab, B: all N) over the arrays above
+        // (x: the 32 columns of two p-slabs, B: all N) over the arrays above
         // once the output is written, and the state weights of the
         // chunk-filling step
-        cXS = 16 + kPad;
+        cXS = 32 + kPad;
         cBS = N + kPad;
         cX = 0;
         cB = cX + 32 * cXS * 2;
@@ -1469,23 +1469,25 @@ __device__ __forceinline__ void decode_back(const DecodeArgs &a, const SlotRows<
 // prefill's tile arithmetic (state_kstep: K = 32 rows per step, hi then lo),
 // so the new boundary state has the bits a prefill of the same tokens
 // leaves. The weights w_j were put in LDS by phase 1. The head's p-slabs are
-// done one after another (all n-tiles of a slab live); per step, rows
-// 32 kk .. +31 of x (the slab's 16 columns) and of B (all N) pass through
-// LDS for the transposed reads, the next step's rows in flight during this
-// step's MFMAs; rows below k come from the slot buffer, row k from the
-// step's input (the buffer row written by this step is not read back), rows
-// after k are zero.
+// taken two at a time (all n-tiles of both live); per step, rows
+// 32 kk .. +31 of x (the two slabs' 32 columns) and of B (all N) pass
+// through LDS for the transposed reads, the next step's rows in flight
+// during this step's MFMAs; rows below k come from the slot buffer, row k
+// from the step's input (the buffer row written by this step is not read
+// back), rows after k are zero.
 template <int P, int N, class DT, bool PG>
 __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRows<PG> &rows, int b,
                                               int slot, int h, int k, char *lds, const DLayout &L,
                                               float lam_last) {
     constexpr int NPS = P / 16, NT = N / 16;
+    constexpr int SP = 2;         // p-slabs per pass
+    static_assert(NPS % SP == 0, "slab pairs");
     constexpr int BPL = N / 16;   // 16-byte pieces of a 32-row B block per lane
+    constexpr int XPL = 32 * 16 * SP / 8 / 64;   // ... of a 32-row x block (SP slabs)
     const Dims d = a.d;
     const int H = d.H, G = d.G, Q = d.Q;
     const int Qp = Q < 32 ? 32 : Q;
     const int g = h / (H / G);
-    const int lane = threadIdx.x & 63;
     const int64_t PN = (int64_t)P * N;
     const uint16_t *bx = static_cast<const uint16_t *>(a.buf_x);   // whole pools
     const uint16_t *bB = static_cast<const uint16_t *>(a.buf_B);
@@ -1497,12 +1499,15 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
     const float dec = fexp2(lam_last);
     const int nkk = Qp / 32;
 
-    auto load_block = [&](int ps, int kk, uint4 &xr, uint4 (&br)[BPL]) {
-        {
-            const int j = 32 * kk + (lane >> 1);
+    // x piece i of lane: row e / (2 SP), 8 columns from 16 p0 + 8 (e % (2 SP))
+    auto load_block = [&](int p0, int kk, uint4 (&xr)[XPL], uint4 (&br)[BPL]) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int e = lane + 64 * i, j = 32 * kk + e / (2 * SP);
             const int64_t rj = rows(j < k ? j : 0);
             const uint16_t *src = j < k ? bx + (rj * H + h) * P : xin;
-            xr = *reinterpret_cast<const uint4 *>(src + 16 * ps + 8 * (lane & 1));
+            xr[i] = *reinterpret_cast<const uint4 *>(src + 16 * p0 + 8 * (e % (2 * SP)));
         }
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
@@ -1512,11 +1517,13 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
             br[i] = *reinterpret_cast<const uint4 *>(src + 8 * (e % (N / 8)));
         }
     };
-    auto store_block = [&](int kk, const uint4 &xr, const uint4 (&br)[BPL]) {
-        {
-            const int r = lane >> 1;
-            *reinterpret_cast<uint4 *>(lds + L.cX + (r * L.cXS + 8 * (lane & 1)) * 2) =
-                keep_if(32 * kk + r <= k, xr);
+    auto store_block = [&](int kk, const uint4 (&xr)[XPL], const uint4 (&br)[BPL]) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+            const int e = lane + 64 * i, r = e / (2 * SP);
+            *reinterpret_cast<uint4 *>(lds + L.cX + (r * L.cXS + 8 * (e % (2 * SP))) * 2) =
+                keep_if(32 * kk + r <= k, xr[i]);
         }
 #pragma unroll
         for (int i = 0; i < BPL; ++i) {
@@ -1527,22 +1534,30 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
     };
 
 #pragma unroll 1
-    for (int ps = 0; ps < NPS; ++ps) {
-        uint4 xa, ba[BPL];
-        load_block(ps, 0, xa, ba);
-        // the slab's old tiles, decayed to the chunk end
-        f32x4 acc[NT];
-        slab_io<P, N, NT, true>(st, ps, 0, acc);
-        slab_scale<NT>(acc, dec);
+    for (int p0 = 0; p0 < NPS; p0 += SP) {
+        uint4 xa[XPL], ba[BPL];
+        load_block(p0, 0, xa, ba);
+        // the slabs' old tiles, decayed to the chunk end
+        f32x4 acc[SP][NT];
+#pragma unroll
+        for (int q = 0; q < SP; ++q) {
+            slab_io<P, N, NT, true>(st, p0 + q, 0, acc[q]);
+            slab_scale<NT>(acc[q], dec);
+        }
         for (int kk = 0; kk < nkk; ++kk) {
             store_block(kk, xa, ba);
             if (kk + 1 < nkk)
-                load_block(ps, kk + 1, xa, ba);
-            state_kstep<NT>(lds, L.cX, L.cXS, 0, L.cB, L.cBS, 0, 0, w + 32 * kk, acc);
+                load_block(p0, kk + 1, xa, ba);
+#pragma unroll
+            for (int q = 0; q < SP; ++q)
+                state_kstep<NT>(lds, L.cX, L.cXS, 16 * q, L.cB, L.cBS, 0, 0, w + 32 * kk, acc[q]);
         }
         // the new tiles of the fp32 state and of its bf16 copy
-        slab_io<P, N, NT, false>(st, ps, 0, acc);
-        slab_bf16<P, NT>(acc, ps, 0, lds, -1, 0, sbf);
+#pragma unroll
+        for (int q = 0; q < SP; ++q) {
+            slab_io<P, N, NT, false>(st, p0 + q, 0, acc[q]);
+            slab_bf16<P, NT>(acc[q], p0 + q, 0, lds, -1, 0, sbf);
+        }
     }
 }
 
