@@ -46,7 +46,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # packed fp32 instructions off, which halves the 157.3 TFLOP/s packed figure)
 FP32_VALU_PEAK_TFLOPS = 78.6
 KERNEL_SOURCES = ["ssd_device.hpp", "ssd_scalar.hip", "ssd_mfma.hip", "ssd_api.cpp",
-                  "ssd_internal.hpp", "ssd_conv.hip", "ssd_scratch.hip"]
+                  "ssd_internal.hpp", "ssd_conv.hip", "ssd_scratch.hip"]   # (not the probe)
 W1A_COPIES = 48              # input copies the 1 x 2048 latency leg rotates through
 CONV_W = 4                   # conv kernel width of the conv legs
 SPEC_BATCH, SPEC_T = 512, 4  # speculative verification: sequences, drafts each
@@ -499,6 +499,38 @@ def copy_gbs(torch, dev, reps=5):
     return gbs
 
 
+def read_gbs(torch, dev, reps=10):
+    """A plain streaming read of 1 GiB (the probe kernel of libssd_probe.so),
+    GB/s: the measured ceiling for read-dominated kernels on this GPU."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_replay_decode_amd", "libssd_probe.so"))
+    lib.ssd_probe_stream_read.restype = ctypes.c_int
+    lib.ssd_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    nbytes, blocks = 1 << 30, 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.ssd_probe_stream_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                       stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ssd_probe_stream_read failed ({rc})")
+    for _ in range(2):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, sink
+    return gbs
+
+
 def load_decode_ratio(sha):
     """Counted over algorithmic bytes of the B=256 chunk-256 decode kernel,
     from the committed counter summary, if taken on the current sources."""
@@ -806,6 +838,7 @@ def main():
         "recovery": spread([(8 + 2 * R, 9 + 2 * R)]),
     }
     ceiling = copy_gbs(torch, dev)
+    read_ceiling = read_gbs(torch, dev)
 
     others = other_workloads(erd, synth, torch, dev, args.warmup, args.steps)
 
@@ -875,6 +908,7 @@ def main():
             "algorithmic_flops_per_launch": pf,
             "measured_copy_gbs": ceiling,
             "frac_of_measured_copy": achieved / ceiling,
+            "measured_read_gbs": read_ceiling,
         },
         "decode": {
             "replay_q256_steps_per_s": dec_steps / t_dec256,
@@ -885,6 +919,9 @@ def main():
             "replay_q256_counter_frac": (dec256_gbs * dec_ratio / HBM_PEAK_GBS
                                          if dec_ratio else None),
             "replay_q256_us_per_step": 1e6 * t_dec256 / dec_steps,
+            # against the streaming-read ceiling measured in the same run
+            "replay_q256_frac_of_measured_read": dec256_gbs / read_ceiling,
+            "replay_q16_frac_of_measured_read": dec16_gbs / read_ceiling,
             "replay_q16_us_per_step": 1e6 * t_dec16 / dec_steps,
             "replay_q16_steps_per_s": dec_steps / t_dec16,
             "replay_q16_hbm_gbs": dec16_gbs,

@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd_replay.so")
+# the bench's bandwidth probe, a separate library (not part of the scan)
+PROBE_LIB = os.path.join(HERE, "libssd_probe.so")
+PROBE_SOURCE = "ssd_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -61,6 +64,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-shared", "-x", "hip",
+          os.path.join(CSRC, PROBE_SOURCE), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -529,6 +529,32 @@ __device__ __forceinline__ void stage_stream(const char *gbase, int gstride, int
     }
 }
 
+// The same with rows below nb from a contiguous slot buffer (row j at
+// gbuf + j * gstride) and the others from the input (row j at
+// gin + (j - nb) * gstride).
+template <int VB, int RB, int K, int NWV>
+__device__ __forceinline__ void stage_stream_split(const char *gbuf, const char *gin, int gstride,
+                                                   int nb, int r0, int n_valid, int k0,
+                                                   char *ldst) {
+    constexpr int DR = NWV * 1024 / RB, DC = NWV * 1024 % RB;
+    const int o = k0 * 1024 + 16 * lane_id();
+    int row = o / RB, cb = o - (o / RB) * RB;
+    for (int k = k0; k < K; k += NWV) {
+        const int j = r0 + row;
+        if (cb < VB && j < n_valid) {
+            const char *src = j < nb ? gbuf + (uint32_t)(j * gstride + cb)
+                                     : gin + (uint32_t)((j - nb) * gstride + cb);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(ldst + k * 1024), 16, 0, 0);
+        }
+        row += DR;
+        cb += DC;
+        if (cb >= RB) {
+            cb -= RB;
+            ++row;
+        }
+    }
+}
+
 template <int P, int N, int NWV, class DT, bool PG>
 __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h0, int wv,
                                            char *lds, const MLayout &L) {
@@ -545,6 +571,20 @@ __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h
                                           lds + L.X + h0 * XRB);
         stage_stream<N * 2, BRB, BK, NWV>(bb, v.G * N * 2, r0, v.n_valid,
                                           ((wv - XK) % NWV + NWV) % NWV, lds + L.B + h0 * BRB);
+    } else if constexpr (!PG) {
+        // buffered rows from the slot's contiguous buffer rows (row j at slot
+        // row rows(0) + j), the others from the input (row nb is token
+        // tok_base)
+        const int64_t b0 = v.rows(0);
+        const char *xbuf = reinterpret_cast<const char *>(v.bx + (b0 * v.H + v.h) * P);
+        const char *bbuf = reinterpret_cast<const char *>(v.bB + (b0 * v.G + v.g) * N);
+        const char *xin = reinterpret_cast<const char *>(v.x + (v.tok_base * v.H + v.h) * P);
+        const char *bin = reinterpret_cast<const char *>(v.B + (v.tok_base * v.G + v.g) * N);
+        stage_stream_split<P * 2, XRB, XK, NWV>(xbuf, xin, v.H * P * 2, v.nb, r0, v.n_valid, wv,
+                                                lds + L.X + h0 * XRB);
+        stage_stream_split<N * 2, BRB, BK, NWV>(bbuf, bin, v.G * N * 2, v.nb, r0, v.n_valid,
+                                                ((wv - XK) % NWV + NWV) % NWV,
+                                                lds + L.B + h0 * BRB);
     } else {
         for (int k = wv; k < XK + BK; k += NWV) {
             const bool isx = k < XK;
