@@ -400,6 +400,53 @@ def other_workloads(erd, synth, torch, dev, warmup, steps):
     return out
 
 
+def fused_conv_decode(erd, synth, torch, dev, shape, S, R, warmup, steps, pre, cw, cbias, prm,
+                      cd):
+    """The conv's decode form and the replay decode step at B=256, chunk 256
+    (the bench's decode workload): as one launch per step
+    (ssd_replay_decode_conv) and as the two calls it replaces (conv update,
+    then decode), each timed over steps x R steps after its own warm-up, on
+    separate caches and conv states of the same contents."""
+    A, D, bias = prm
+    n = (warmup + steps) * R
+    H, G, P, N = shape.H, shape.G, shape.P, shape.N
+    px, pdt, pB, pC = synth.make_tokens_torch(int(pre.sum()), H, G, P, N, 1, dev)
+    xbc = synth.make_xbc_torch(n * S, cd, 13, dev).view(n, S, cd)
+    dts = synth.make_tokens_torch(n * S, H, G, P, N, 14, dev)[1].view(n, S, H)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for form in ("one_launch", "two_launches"):
+        cache = erd.ReplayCache(shape, S, dev)
+        erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), px, pdt, pB, pC, A, D, bias)
+        cst = torch.zeros((S, cd, CONV_W - 1), dtype=torch.bfloat16, device=dev)
+        x = torch.empty((S, H, P), dtype=torch.bfloat16, device=dev)
+        Bt = torch.empty((S, G, N), dtype=torch.bfloat16, device=dev)
+        Ct = torch.empty_like(Bt)
+        y = torch.empty_like(x)
+        if form == "one_launch":
+            plan = erd.ConvDecodePlan(shape, S, A, cache, cw, cst, D, bias, bias=cbias)
+            call = lambda k: plan(xbc[k], dts[k], x, Bt, Ct, y)  # noqa: E731
+        else:
+            cplan = erd.ConvUpdatePlan(shape, S, cw, cst, cbias)
+            dplan = erd.DecodePlan(shape, S, A, D, bias, cache=cache)
+
+            def call(k):
+                cplan(xbc[k], x, Bt, Ct)
+                dplan(x, dts[k], Bt, Ct, y)
+        for k in range(warmup * R):
+            call(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(warmup * R, n):
+            call(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[form + "_us_per_step"] = 1e3 * e0.elapsed_time(e1) / (steps * R)
+    out["batch"], out["chunk_size"], out["conv_width"] = S, shape.chunk_size, CONV_W
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -841,6 +888,8 @@ def main():
     read_ceiling = read_gbs(torch, dev)
 
     others = other_workloads(erd, synth, torch, dev, args.warmup, args.steps)
+    fused = fused_conv_decode(erd, synth, torch, dev, shape, S, R, args.warmup, args.steps,
+                              pre, cw, cbias, (A, D, bias), cd)
 
     K = args.steps
     t_prefill = span(0, 1)
@@ -969,6 +1018,7 @@ def main():
             "alu_peak_tflops": FP32_VALU_PEAK_TFLOPS,
         },
         "other_workloads": others,
+        "conv_decode_fused": fused,
         "legs": legs,
         "commit_ms": 1e3 * t_commit / K,
         "wall_s": wall,

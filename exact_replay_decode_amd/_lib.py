@@ -25,7 +25,7 @@ EXPORTS = ("ssd_status_string", "ssd_replay_cache_bytes", "ssd_prefill_workspace
            "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
            "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
            "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen",
-           "ssd_prefill_chunk_count", "ssd_replay_decode_static")
+           "ssd_prefill_chunk_count", "ssd_replay_decode_static", "ssd_replay_decode_conv")
 
 
 class ssd_shape(ctypes.Structure):
@@ -91,6 +91,9 @@ def load() -> ctypes.CDLL:
     lib.ssd_replay_decode.argtypes = [shp, cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_replay_decode_static.restype = ctypes.c_int
     lib.ssd_replay_decode_static.argtypes = [shp, cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_replay_decode_conv.restype = ctypes.c_int
+    lib.ssd_replay_decode_conv.argtypes = [shp, cp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_conv1d_varlen.restype = ctypes.c_int
     lib.ssd_conv1d_varlen.argtypes = [shp, i32, i32, i32, i64, vp, vp, vp, i32, vp, vp, vp,
                                       vp, vp, vp, vp, vp]

@@ -396,6 +396,40 @@ def ssd_replay_decode(shape: Shape, cache: ReplayCache, x, dt, B, C, A, D=None, 
     return y
 
 
+def ssd_replay_decode_conv(shape: Shape, cache: ReplayCache, xBC, weight, conv_state, dt, A,
+                           D=None, dt_bias=None, bias=None, slot_idx=None, activation=True,
+                           out=None, y=None, stream=None):
+    """The causal conv's decode form and one exact-replay decode step in one
+    launch (ssd_conv1d_update, then ssd_replay_decode on its outputs, bit
+    for bit): xBC [batch, conv_dim] of the new tokens, conv_state
+    [num_slots, conv_dim, W-1] indexed by the cache's slots. Returns
+    (y, (x, B, C))."""
+    dev = cache.device
+    H, P = shape.H, shape.P
+    nb = int(xBC.shape[0])
+    cd = conv_dim(shape)
+    _need(xBC, "xBC", (nb, cd), shape.io, dev)
+    W = int(weight.shape[1]) if weight.dim() == 2 else -1
+    _need(weight, "weight", (cd, W), torch.float32, dev)
+    _opt(bias, "bias", (cd,), torch.float32, dev)
+    _need(conv_state, "conv_state", (cache.num_slots, cd, W - 1), shape.io, dev)
+    _need(dt, "dt", (nb, H), shape.dtt, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _opt(D, "D", (H,), torch.float32, dev)
+    _opt(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    sl = _slots(slot_idx, nb, dev)
+    x, B, C = _conv_outputs(shape, nb, dev, out)
+    y = torch.empty((nb, H, P), dtype=shape.io, device=dev) if y is None else \
+        _need(y, "y", (nb, H, P), shape.io, dev)
+    sh, cs = shape.c(), cache.struct()
+    rc = _lib.load().ssd_replay_decode_conv(
+        ctypes.byref(sh), ctypes.byref(cs), nb, _ptr(sl), W, int(bool(activation)), _ptr(xBC),
+        _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
+        _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y), _stream(stream))
+    _lib.check(rc, "ssd_replay_decode_conv")
+    return y, (x, B, C)
+
+
 def conv_dim(shape: Shape) -> int:
     """Channels of the conv before the scan: x | B | C."""
     return shape.H * shape.P + 2 * shape.G * shape.N
@@ -594,6 +628,44 @@ class DecodePlan:
                 self._b, y.data_ptr(), self._st)
         if rc != 0:
             _lib.check(rc, "DecodePlan")
+
+
+class ConvDecodePlan:
+    """Pre-marshalled ssd_replay_decode_conv calls (the conv's decode form and
+    the replay step in one launch) for a hot loop: each call passes the
+    step's xBC [batch, conv_dim], raw dt, the conv outputs x, B, C and y."""
+
+    def __init__(self, shape: Shape, batch: int, A, cache, weight, conv_state, D=None,
+                 dt_bias=None, bias=None, slot_idx=None, activation=True, stream=None):
+        dev = cache.device
+        cd = conv_dim(shape)
+        self.W = int(weight.shape[1])
+        _need(weight, "weight", (cd, self.W), torch.float32, dev)
+        _opt(bias, "bias", (cd,), torch.float32, dev)
+        _need(conv_state, "conv_state", (cache.num_slots, cd, self.W - 1), shape.io, dev)
+        _need(A, "A", (shape.H,), torch.float32, dev)
+        _opt(D, "D", (shape.H,), torch.float32, dev)
+        _opt(dt_bias, "dt_bias", (shape.H,), torch.float32, dev)
+        if slot_idx is None and batch > cache.num_slots:
+            raise ValueError("batch exceeds cache slots")
+        self.shape, self.batch, self.device = shape, batch, dev
+        self._keep = (A, D, dt_bias, cache, weight, conv_state, bias, slot_idx)
+        self._sh, self._cs = shape.c(), cache.struct()
+        self._lib = _lib.load()
+        self._st = _stream(stream)
+        self._sl = _ptr(_slots(slot_idx, batch, dev))
+        self._args = (self.W, int(bool(activation)))
+        self._w, self._b, self._cst = _ptr(weight), _ptr(bias), _ptr(conv_state)
+        self._A, self._D, self._db = _ptr(A), _ptr(D), _ptr(dt_bias)
+
+    def __call__(self, xBC, dt, x, B, C, y):
+        """Launch one step; tensors of the planned shapes, contiguous."""
+        rc = self._lib.ssd_replay_decode_conv(
+            ctypes.byref(self._sh), ctypes.byref(self._cs), self.batch, self._sl, *self._args,
+            xBC.data_ptr(), self._w, self._b, self._cst, x.data_ptr(), B.data_ptr(),
+            C.data_ptr(), dt.data_ptr(), self._A, self._D, self._db, y.data_ptr(), self._st)
+        if rc != 0:
+            _lib.check(rc, "ConvDecodePlan")
 
 
 class ConvUpdatePlan:

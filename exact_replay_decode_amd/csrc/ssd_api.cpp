@@ -414,12 +414,21 @@ int ssd_replay_accept(const ssd_shape *sh, const ssd_replay_cache *cache, int32_
 
 namespace {
 
+// The conv before the scan, for a decode step that takes it in the same
+// launch (conv.xBC non-null; the other fields as in ssd_conv1d_update).
+struct DecodeConv {
+    const void *xBC = nullptr;
+    const float *weight = nullptr, *bias = nullptr;
+    void *state = nullptr;
+    int32_t width = 0, act = 0;
+};
+
 // One decode step; own_work: the library's static bookkeeping array takes
 // the place of cache->work (which may then be NULL).
 int replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
                   const int32_t *slot_idx, const void *x, const void *dt, const void *B,
                   const void *C, const float *A, const float *D, const float *dt_bias, void *y,
-                  bool own_work, hipStream_t stream) {
+                  bool own_work, hipStream_t stream, const DecodeConv &conv = DecodeConv()) {
     Dims d;
     int st = check_shape(sh, &d);
     if (st != SSD_OK)
@@ -457,6 +466,34 @@ int replay_decode(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t ba
     if (own_work && ssd::static_work(&a.work, (hipStream_t)stream) != hipSuccess)
         return SSD_ERR_HIP;
     a.bm = buf_map(cache);
+    if (conv.xBC) {
+        // one launch when the matrix-core engine runs the step with each
+        // workgroup's heads in one B/C group (bf16 I/O); otherwise the conv
+        // update and the step as two launches (the same bits either way:
+        // one conv_point, the same inputs)
+        if (ssd::mfma_supported(d) && d.io_bf16 && (d.H / d.G) % 4 == 0) {
+            a.xBC = conv.xBC;
+            a.cw = conv.weight;
+            a.cb = conv.bias;
+            a.cstate = conv.state;
+            a.cW = conv.width;
+            a.cact = conv.act != 0;
+            return hip_status(ssd::launch_decode_mfma(a, (hipStream_t)stream));
+        }
+        ssd::ConvArgs c = {};
+        c.d = d;
+        c.W = conv.width;
+        c.act = conv.act != 0;
+        c.S = batch;
+        c.slot_idx = slot_idx;
+        c.num_slots = cache->num_slots;
+        c.xBC = conv.xBC; c.weight = conv.weight; c.bias = conv.bias;
+        c.state = conv.state;
+        c.x = const_cast<void *>(x); c.B = const_cast<void *>(B); c.C = const_cast<void *>(C);
+        const hipError_t e = ssd::launch_conv_update(c, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return hip_status(e);
+    }
     return hip_status(ssd::mfma_supported(d) ? ssd::launch_decode_mfma(a, (hipStream_t)stream)
                                              : ssd::launch_decode(a, (hipStream_t)stream));
 }
@@ -479,6 +516,35 @@ int ssd_replay_decode_static(const ssd_shape *sh, const ssd_replay_cache *cache,
                              const float *dt_bias, void *y, hipStream_t stream) {
     return replay_decode(sh, cache, batch, slot_idx, x, dt, B, C, A, D, dt_bias, y, true,
                          stream);
+}
+
+int ssd_replay_decode_conv(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t batch,
+                           const int32_t *slot_idx, int32_t width, int32_t activation,
+                           const void *xBC, const float *weight, const float *bias,
+                           void *conv_state, void *x, void *B, void *C, const void *dt,
+                           const float *A, const float *D, const float *dt_bias, void *y,
+                           hipStream_t stream) {
+    Dims d;
+    int st = check_shape(sh, &d);
+    if (st != SSD_OK)
+        return st;
+    if (width < 2 || width > 4)
+        return SSD_ERR_UNSUPPORTED;
+    if (batch > 65535)
+        return SSD_ERR_SHAPE;
+    if (batch > 0 && (!xBC || !weight || !conv_state))
+        return SSD_ERR_NULL;
+    if (!all_a16(xBC, conv_state) || !all_a16(weight, bias))
+        return SSD_ERR_ALIGN;
+    DecodeConv conv;
+    conv.xBC = xBC;
+    conv.weight = weight;
+    conv.bias = bias;
+    conv.state = conv_state;
+    conv.width = width;
+    conv.act = activation;
+    return replay_decode(sh, cache, batch, slot_idx, x, dt, B, C, A, D, dt_bias, y, false,
+                         stream, conv);
 }
 
 int ssd_conv1d_varlen(const ssd_shape *sh, int32_t W, int32_t act, int32_t S, int64_t T,

@@ -64,20 +64,6 @@ struct Lanes<IoF32> {
     }
 };
 
-// One output point: bias, then the W taps in order (fmaf), then SiLU
-// v / (1 + exp(-v)) with the hardware exp2 and reciprocal (a few ulps, far
-// below the bf16 storage rounding; the precise library forms cost a third
-// of the prefill's time). Both forms of the conv call only this.
-template <int W>
-__device__ __forceinline__ float conv_point(const float *w, const float (&v)[W], float bias,
-                                            bool act) {
-    float acc = bias;
-#pragma unroll
-    for (int i = 0; i < W; ++i)
-        acc = fmaf(w[i], v[i], acc);
-    return act ? __fdividef(acc, 1.0f + __expf(-acc)) : acc;
-}
-
 // The thread's CG channels starting at c0: taps and bias, read as 16-byte
 // pieces (the CG * W taps are contiguous and c0 * W * 4 bytes is a
 // multiple of 16 because CG * W * 4 is).

@@ -197,4 +197,19 @@ __device__ __forceinline__ void wave_scan_segments(float (&v)[4], int nseg) {
     }
 }
 
+// One output point of the causal conv before the scan: bias, then the W
+// taps in order (fmaf), then SiLU v / (1 + exp(-v)) with the hardware exp2
+// and reciprocal (a few ulps, far below the bf16 storage rounding). Every
+// form of the conv (prefill, decode, and the decode step with the conv in
+// the same launch) calls only this, so they produce the same bits.
+template <int W>
+__device__ __forceinline__ float conv_point(const float *w, const float (&v)[W], float bias,
+                                            bool act) {
+    float acc = bias;
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        acc = fmaf(w[i], v[i], acc);
+    return act ? __fdividef(acc, 1.0f + __expf(-acc)) : acc;
+}
+
 }  // namespace ssd

@@ -93,6 +93,15 @@ struct DecodeArgs {
                               // count and done counters [34], commit list [slots]
     BufMap bm;
     const int32_t *order;     // or null: batch positions by rank, heaviest first
+    // with the conv before the scan in the same launch (xBC non-null): the
+    // token's x | B | C are the causal conv of xBC [batch, conv_dim] (width
+    // cW, taps cw [conv_dim, cW], bias cb, SiLU if cact) over the slot's conv
+    // state cstate [slots, conv_dim, cW - 1], written to x, B, C, which the
+    // step then reads as its inputs
+    const void *xBC;
+    const float *cw, *cb;
+    void *cstate;
+    int32_t cW, cact;
 };
 
 // Causal depthwise conv1d before the scan: prefill (S sequences of a varlen

@@ -1601,6 +1601,93 @@ __device__ __forceinline__ void decode_commit(const DecodeArgs &a, const SlotRow
     }
 }
 
+// The conv before the scan, for one workgroup's part of a decode step with
+// the conv in the same launch (xBC non-null): the x channels of heads
+// h0 .. h0 + kDecodeWaves - 1 and the B | C channels of their group g, one
+// channel per thread, from the slot's conv state (the W - 1 previous
+// inputs) and the token's xBC row, with the conv's own conv_point; the
+// outputs go to the step's input rows x[b], B[b], C[b] (bf16, nearest
+// even), and the x channels' state, which this workgroup alone reads, is
+// shifted in place. The B | C channels are read by every workgroup of the
+// slot; the slot's last workgroup shifts them (conv_shift_bc).
+template <int P, int N, int W>
+__device__ __forceinline__ void conv_token(const DecodeArgs &a, int b, int slot, int h0, int g) {
+    const int H = a.d.H, G = a.d.G;
+    const int cd = H * P + 2 * G * N;
+    const int t = threadIdx.x;
+    const uint16_t *in = static_cast<const uint16_t *>(a.xBC) + (int64_t)b * cd;
+    uint16_t *st = static_cast<uint16_t *>(a.cstate) + (int64_t)slot * cd * (W - 1);
+    auto point = [&](int c, uint16_t (&raw)[W]) {
+        float v[W], w[W];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+            raw[i] = st[(int64_t)c * (W - 1) + i];
+        raw[W - 1] = in[c];
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            v[i] = IoBF16::val(raw[i]);
+            w[i] = a.cw[(int64_t)c * W + i];
+        }
+        return IoBF16::cvt(conv_point<W>(w, v, a.cb ? a.cb[c] : 0.0f, a.cact != 0));
+    };
+    if (t < kDecodeWaves * P && h0 + t / P < H) {
+        const int c = (h0 + t / P) * P + t % P;
+        uint16_t raw[W];
+        const uint16_t o = point(c, raw);
+        static_cast<uint16_t *>(const_cast<void *>(a.x))[(int64_t)b * H * P + c] = o;
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+            st[(int64_t)c * (W - 1) + i] = raw[i + 1];
+    }
+    if (t < 2 * N) {
+        const bool isB = t < N;
+        const int n = isB ? t : t - N;
+        const int c = H * P + (isB ? 0 : G * N) + g * N + n;
+        uint16_t raw[W];
+        const uint16_t o = point(c, raw);
+        uint16_t *dst = static_cast<uint16_t *>(const_cast<void *>(isB ? a.B : a.C));
+        dst[((int64_t)b * G + g) * N + n] = o;
+    }
+}
+
+// The slot's B | C conv state (every group's 2N channels) shifted by one
+// input, by one wave of the slot's last workgroup.
+template <int P, int N, int W>
+__device__ __forceinline__ void conv_shift_bc(const DecodeArgs &a, int b, int slot) {
+    const int H = a.d.H, G = a.d.G;
+    const int cd = H * P + 2 * G * N;
+    const uint16_t *in = static_cast<const uint16_t *>(a.xBC) + (int64_t)b * cd;
+    uint16_t *st = static_cast<uint16_t *>(a.cstate) + (int64_t)slot * cd * (W - 1);
+    for (int c = H * P + (threadIdx.x & 63); c < cd; c += 64) {
+        uint16_t raw[W];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+            raw[i] = st[(int64_t)c * (W - 1) + i];
+        raw[W - 1] = in[c];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+            st[(int64_t)c * (W - 1) + i] = raw[i + 1];
+    }
+}
+
+template <int P, int N>
+__device__ __forceinline__ void conv_token_w(const DecodeArgs &a, int b, int slot, int h0, int g) {
+    switch (a.cW) {
+    case 2: conv_token<P, N, 2>(a, b, slot, h0, g); break;
+    case 3: conv_token<P, N, 3>(a, b, slot, h0, g); break;
+    default: conv_token<P, N, 4>(a, b, slot, h0, g); break;
+    }
+}
+
+template <int P, int N>
+__device__ __forceinline__ void conv_shift_bc_w(const DecodeArgs &a, int b, int slot) {
+    switch (a.cW) {
+    case 2: conv_shift_bc<P, N, 2>(a, b, slot); break;
+    case 3: conv_shift_bc<P, N, 3>(a, b, slot); break;
+    default: conv_shift_bc<P, N, 4>(a, b, slot); break;
+    }
+}
+
 // Ranking of a large batch before its decode launch: batch positions whose
 // token fills the chunk first (their workgroups also run the chunk-state
 // update), then by the number of 32-row s-blocks the replay walks, most
@@ -1746,6 +1833,12 @@ void k_decode_mfma(DecodeArgs a) {
     }
     // the workgroup's heads share one B/C group: C.B^T is split between them
     const bool gshare = (H / G) % kDecodeWaves == 0;
+    if (a.xBC) {
+        // the token's x | B | C from the conv before the scan (the host
+        // takes this path only when the workgroup's heads share one group)
+        conv_token_w<P, N>(a, b, slot, hq * kDecodeWaves, (hq * kDecodeWaves) / (H / G));
+        __syncthreads();   // the conv outputs are the step's inputs
+    }
     DecodeCarry<P, DT> cy;
     if (h < H)
         decode_front<P, N, DT, PG, FUSED>(a, rows, b, slot, h, k, wave, gshare,
@@ -1784,6 +1877,10 @@ void k_decode_mfma(DecodeArgs a) {
             list[kListHead + at] = slot;
         }
     }
+    // the slot's last workgroup: every workgroup of the slot has read the
+    // B | C conv state (before counting itself in), so it can be shifted
+    if (a.xBC && wave == 0 && __shfl(prev, 0, 64) == HQ - 1)
+        conv_shift_bc_w<P, N>(a, b, slot);
     if (a.order)
         decode_order_done(a);
     (void)G;

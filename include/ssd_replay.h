@@ -283,6 +283,26 @@ int ssd_replay_decode_static(const ssd_shape *shape, const ssd_replay_cache *cac
                              const float *A, const float *D, const float *dt_bias,
                              void *y, hipStream_t stream);
 
+/* Decode step with the causal conv before the scan in the same launch
+ * ([RFC] section 2, item 6: the conv's decode form, before the SSM decode):
+ * ssd_conv1d_update(shape, width, activation, batch, slot_idx,
+ * cache->num_slots, xBC, weight, bias, conv_state, x, B, C) followed by
+ * ssd_replay_decode(shape, cache, batch, slot_idx, x, dt, B, C, A, D,
+ * dt_bias, y), bit for bit, as one launch (plus the ranking launch that
+ * ssd_replay_decode may put ahead) when the matrix-core engine runs the
+ * shape with bf16 I/O and (H / G) % 4 == 0, else as those two calls.
+ * x [batch,H,P] and B/C [batch,G,N] are outputs here (the conv's, which the
+ * step then reads); conv_state [num_slots, conv_dim, width - 1] is indexed
+ * by the cache's slots and updated in place. Arguments and errors as for
+ * the two calls; a position the step skips (slot out of range) gets no
+ * conv either. */
+int ssd_replay_decode_conv(const ssd_shape *shape, const ssd_replay_cache *cache,
+                           int32_t batch, const int32_t *slot_idx, int32_t width,
+                           int32_t activation, const void *xBC, const float *weight,
+                           const float *bias, void *conv_state, void *x, void *B, void *C,
+                           const void *dt, const float *A, const float *D,
+                           const float *dt_bias, void *y, hipStream_t stream);
+
 /* Speculative verification, output only ([RSSM] "Motivation and method":
  * drafts are verified with an output-only form instead of materialising a
  * state per draft; the acceptance length then advances only the committed

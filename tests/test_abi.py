@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
             "ssd_replay_decode", "ssm_state_update", "ssd_replay_cache_refresh",
             "ssd_replay_page_bytes", "ssd_conv1d_varlen", "ssd_conv1d_update",
             "ssd_replay_verify", "ssd_replay_accept", "ssm_state_update_varlen",
-            "ssd_prefill_chunk_count", "ssd_replay_decode_static"}
+            "ssd_prefill_chunk_count", "ssd_replay_decode_static", "ssd_replay_decode_conv"}
     assert set(declared_functions()) == want
     assert set(_lib.EXPORTS) == want
 
@@ -285,6 +285,28 @@ def test_conv_checks():
     assert upd(batch=5) == -2                                  # more rows than slots
     assert upd(batch=0) == 0
     assert upd(xBC=ctypes.c_void_p(0x1002)) == -9
+
+
+def test_fused_conv_decode_checks():
+    # the conv + decode step fails closed on the conv's arguments and on the
+    # decode's, before any launch
+    sh = shape()
+    lib = _lib.load()
+
+    def dec(c=None, W=4, batch=2, xBC=FAKE, weight=FAKE, state=FAKE):
+        c = cache(sh) if c is None else c
+        return lib.ssd_replay_decode_conv(ctypes.byref(sh), ctypes.byref(c), batch, None, W, 1,
+                                          xBC, weight, None, state, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, None, None, FAKE, None)
+    assert dec(W=1) == -7 and dec(W=5) == -7
+    assert dec(xBC=None) == -1 and dec(weight=None) == -1 and dec(state=None) == -1
+    assert dec(xBC=ctypes.c_void_p(0x1002)) == -9
+    assert dec(weight=ctypes.c_void_p(0x1004)) == -9
+    assert dec(c=cache(sh, state_dtype=1)) == -4                 # the decode's own checks
+    assert dec(c=cache(sh, chunk_size=32)) == -5
+    assert dec(c=cache(sh, work=None)) == -1
+    assert dec(batch=5) == -2                                    # more rows than slots
+    assert dec(batch=0) == 0
 
 
 def test_python_binding_checks_extents():

@@ -209,3 +209,57 @@ def test_conv_full_size_sampled_parity():
                                activation=False)
         check_parity(cat_out(x[a:a + T], B[a:a + T], C[a:a + T]), ref, mag, "bf16")
         assert np.array_equal(erd.to_f64(st[s]), fin[0])
+
+
+def _fused_setup(B, H, G, P, N, Q, W, seed):
+    shape = erd.Shape(H, G, P, N, Q, "bf16", "bf16")
+    cd = erd.conv_dim(shape)
+    cp = synth.make_conv_params(cd, W, seed)
+    hp = synth.make_head_params(H, seed)
+    prm = tuple(torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    pre = synth.replay_prefix_lengths(B, Q, seed)
+    px, pdt, pB, pC = synth.make_tokens_torch(int(pre.sum()), H, G, P, N, seed, DEV)
+    caches = []
+    for _ in range(2):
+        c = erd.ReplayCache(shape, B, DEV)
+        erd.ssd_replay_prefill(shape, c, synth.cu_seqlens(pre), px, pdt, pB, pC, *prm)
+        caches.append(c)
+    st = erd.to_device(synth.make_xbc(B * (W - 1), cd, seed + 1), "bf16", DEV)
+    cstate = st.view(W - 1, B, cd).permute(1, 2, 0).contiguous()
+    return shape, cd, cp, prm, caches, [cstate.clone(), cstate.clone()]
+
+
+@pytest.mark.parametrize("Q,G,W,Bn", [(256, 1, 4, 128), (16, 8, 3, 64), (256, 8, 2, 64)])
+def test_fused_conv_decode_equals_two_launches(Q, G, W, Bn):
+    """ssd_replay_decode_conv (the conv's decode form and the replay step in
+    one launch) against ssd_conv1d_update then ssd_replay_decode, over
+    enough steps to fill chunks (buffers holding 0..Q-1 tokens):
+    outputs, the conv's x | B | C, the conv state and every cache array
+    bit for bit; positions in permuted slot order with one skipped. B=128
+    at H=32 has more workgroups than run at once (the ranked launch)."""
+    H, P, N = 32, 64, 128
+    shape, cd, cp, prm, caches, cst = _fused_setup(Bn, H, G, P, N, Q, W, 31)
+    A, D, dtb = prm
+    weight, bias = torch.from_numpy(cp.weight).to(DEV), torch.from_numpy(cp.bias).to(DEV)
+    slots = torch.from_numpy(np.random.default_rng(5).permutation(Bn).astype(np.int32)).to(DEV)
+    slots[7] = -1                                   # skipped: no conv, no step
+    steps = 40 if Q == 256 else 20
+    xbc = erd.to_device(synth.make_xbc(steps * Bn, cd, 32), "bf16", DEV).view(steps, Bn, cd)
+    dts = erd.to_device(synth.make_tokens(steps * Bn, H, G, P, N, 33).dt, "bf16",
+                        DEV).view(steps, Bn, H)
+    for i in range(steps):
+        x, Bt, Ct = erd.ssd_conv1d_update(shape, xbc[i], weight, cst[0], bias, slot_idx=slots)
+        y0 = erd.ssd_replay_decode(shape, caches[0], x, dts[i], Bt, Ct, A, D, dtb,
+                                   slot_idx=slots)
+        y1, (x1, B1, C1) = erd.ssd_replay_decode_conv(shape, caches[1], xbc[i], weight, cst[1],
+                                                       dts[i], A, D, dtb, bias=bias,
+                                                       slot_idx=slots)
+        keep = torch.arange(Bn, device=DEV) != 7
+        assert same_bits(y1[keep], y0[keep]), i
+        assert same_bits(x1[keep], x[keep]) and same_bits(B1[keep], Bt[keep]) and \
+            same_bits(C1[keep], Ct[keep]), i
+        assert same_bits(cst[1], cst[0]), i
+    c0, c1 = caches
+    for name in ("state", "buf_x", "buf_dt", "buf_B", "buf_len", "boundary_pos", "work"):
+        assert same_bits(getattr(c1, name), getattr(c0, name)), name
+    assert same_bits(c1.state_bf_rowmajor(), c0.state_bf_rowmajor())
