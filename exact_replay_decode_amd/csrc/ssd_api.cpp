@@ -203,6 +203,9 @@ int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, i
     a.dry = mode == 1;
     a.no_y = mode == 2;
     a.take = mode == 2 ? take : nullptr;
+    // the sweeps of verification and acceptance list their sequences in the
+    // work array, which has room for num_slots of them
+    a.work = mode != 0 && S <= cache->num_slots ? cache->work : nullptr;
     if (mode == 1)   // verification writes only y
         return hip_status(ssd::mfma_supported(d) ? ssd::launch_verify_mfma(a, (hipStream_t)stream)
                                                  : ssd::launch_scan(a, (hipStream_t)stream));

@@ -54,6 +54,9 @@ struct ScanArgs {
     int32_t dry, no_y;
     const int32_t *take;
     int32_t only_cross;       // dry replay of the sequences whose drafts cross the chunk end
+    // the cache's work array (or null): the sweeps of verification and
+    // acceptance take their sequences from a list kept in it
+    int32_t *work;
 };
 
 // Write the trailing partial chunk of each sequence into the slot buffers

@@ -1100,6 +1100,69 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
     scan_one<P, N, DT, PG, RP>(a, wid / a.d.H, wid % a.d.H, lds);
 }
 
+// The work array after the per-slot arrival counters: [0] number of entries
+// on the list, [1] finished groups, [2, 2 + kDoneGroups) finished
+// workgroups per group, then the list itself (slots whose chunk-state update
+// is pending, a decode batch's ranking, or the sequences a sweep replays).
+// Every call leaves it zero.
+constexpr int kDoneGroups = 32;
+constexpr int kListHead = 2 + kDoneGroups;
+
+// End of a launch that read the list: every workgroup counts itself out (in
+// kDoneGroups groups by blockIdx, then once per group, so that no counter
+// takes many atomics); the last one zeroes entries [0, nclear) of the list,
+// and its count when `count` is set. Every workgroup has read what it needs
+// from the list before counting out.
+__device__ __forceinline__ void work_list_done(int32_t *list, int nclear, bool count) {
+    __shared__ int is_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int last = 0;
+        const int W = gridDim.x;
+        const int grp = blockIdx.x % kDoneGroups;
+        const int members = (W - grp + kDoneGroups - 1) / kDoneGroups;
+        int32_t *sub = list + 2 + grp;
+        if (__hip_atomic_fetch_add(sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            members - 1) {
+            __hip_atomic_store(sub, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int groups = W < kDoneGroups ? W : kDoneGroups;
+            if (__hip_atomic_fetch_add(list + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                groups - 1) {
+                __hip_atomic_store(list + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = 1;
+            }
+        }
+        is_last = last;
+    }
+    __syncthreads();
+    if (is_last) {
+        for (int i = threadIdx.x; i < nclear; i += blockDim.x)
+            list[kListHead + i] = 0;
+        if (count && threadIdx.x == 0)
+            list[0] = 0;
+    }
+}
+
+// Whether sequence s has work in a sweep: drafts that run past the chunk end
+// (verification), or accepted drafts that fill the chunk (acceptance).
+__device__ __forceinline__ bool sweep_has_work(const ScanArgs &a, int s) {
+    const int slot = a.slot_idx ? a.slot_idx[s] : s;
+    const int len = seq_len(a.cu, a.take, s);
+    if (len <= 0 || slot < 0 || slot >= a.num_slots)
+        return false;
+    const int k = a.buf_len[slot];
+    return k >= 0 && k < a.d.Q && (a.no_y ? k + len >= a.d.Q : k + len > a.d.Q);
+}
+
+// The acceptance sweep's list: the sequences whose accepted drafts fill the
+// chunk (one workgroup; list order does not matter).
+__global__ __launch_bounds__(1024) void k_sweep_list(ScanArgs a) {
+    int32_t *list = a.work + a.num_slots;
+    for (int s = threadIdx.x; s < a.S; s += blockDim.x)
+        if (sweep_has_work(a, s))
+            list[kListHead + atomicAdd(list, 1)] = s;
+}
+
 // Replay calls where few sequences have work: verification of drafts that
 // run past the chunk end (dry replay, only_cross), and acceptance (no_y),
 // where only the sequences whose accepted drafts fill a chunk have any.
@@ -1108,10 +1171,26 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a)
 // and replays them one after another. The pairs with nothing to do cost no
 // dispatch of a large-LDS workgroup, and a sequence's heads land on
 // different workgroups.
+// With the work array (a.work), the sequences come from the list that the
+// verification kernel or k_sweep_list put there: the pairs (listed
+// sequence, head) are dealt to the workgroups in turn, so no workgroup
+// replays two while another has none, and the last workgroup empties the
+// list.
 template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const int H = a.d.H, Q = a.d.Q;
+    const int H = a.d.H;
+    if (a.work) {
+        int32_t *wl = a.work + a.num_slots;
+        const int n = wl[0];
+        for (int j = blockIdx.x; j < n * H; j += gridDim.x) {
+            const int s = wl[kListHead + j / H];
+            __syncthreads();   // the previous pair's LDS use is over
+            scan_one<P, N, DT, PG, true>(a, s, j % H, lds);
+        }
+        work_list_done(wl, n, true);
+        return;
+    }
     const MLayout L(kMaxQ, P, N);   // scan_one's layout
     int *list = reinterpret_cast<int *>(lds + L.bytes);   // [1 + 64 * kPrefillWaves]
     const int total = a.S * H;
@@ -1123,14 +1202,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a
         const int i = base + threadIdx.x;
         const int e = blockIdx.x + gridDim.x * i;
         if (i < rounds && e < total) {
-            const int s = e / H;
-            const int slot = a.slot_idx ? a.slot_idx[s] : s;
-            const int len = seq_len(a.cu, a.take, s);
-            if (len > 0 && slot >= 0 && slot < a.num_slots) {
-                const int k = a.buf_len[slot];
-                if (k >= 0 && k < Q && (a.no_y ? k + len >= Q : k + len > Q))
-                    list[1 + atomicAdd(list, 1)] = e;
-            }
+            if (sweep_has_work(a, e / H))
+                list[1 + atomicAdd(list, 1)] = e;
         }
         __syncthreads();
         const int n = list[0];
@@ -1177,11 +1250,6 @@ constexpr int kDecodeWaves = 4;
 // of a full chunk at a time; when no chunk filled they return at once, in
 // one dispatch round.
 constexpr int kLdsBytesPerCu = 160 * 1024;
-// The work array after the per-slot arrival counters: [0] number of slots
-// on the commit list, [1] finished groups, [2, 2 + kDoneGroups) finished
-// workgroups per group, then the list itself.
-constexpr int kDoneGroups = 32;
-constexpr int kListHead = 2 + kDoneGroups;
 
 // Per-wave LDS of the decode kernel, in bytes.
 struct DLayout {
@@ -1746,36 +1814,9 @@ __global__ __launch_bounds__(kOrderThreads) void k_decode_order(DecodeArgs a) {
         order[atomicAdd(&count[bin_of(b)], 1)] = b;
 }
 
-// End of a ranked decode launch: every workgroup counts itself out (in
-// kDoneGroups groups by blockIdx, then once per group, so that no counter
-// takes many atomics); the last one zeroes the ranking and the counters. All
-// other workgroups read their rank's entry before counting out.
+// End of a ranked decode launch: the last workgroup zeroes the ranking.
 __device__ __forceinline__ void decode_order_done(const DecodeArgs &a) {
-    __shared__ int is_last;
-    int32_t *list = a.work + a.num_slots;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int last = 0;
-        const int W = gridDim.x;
-        const int grp = blockIdx.x % kDoneGroups;
-        const int members = (W - grp + kDoneGroups - 1) / kDoneGroups;
-        int32_t *sub = list + 2 + grp;
-        if (__hip_atomic_fetch_add(sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            members - 1) {
-            __hip_atomic_store(sub, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int groups = W < kDoneGroups ? W : kDoneGroups;
-            if (__hip_atomic_fetch_add(list + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                groups - 1) {
-                __hip_atomic_store(list + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last = 1;
-            }
-        }
-        is_last = last;
-    }
-    __syncthreads();
-    if (is_last)
-        for (int i = threadIdx.x; i < a.batch; i += blockDim.x)
-            list[kListHead + i] = 0;
+    work_list_done(a.work + a.num_slots, a.batch, false);
 }
 
 template <int P, int N, class DT, bool PG, bool FUSED>
@@ -2034,6 +2075,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
     if (T <= 0 || h >= H || slot < 0 || slot >= a.num_slots)
         return;
     const int k = a.buf_len[slot];
+    // drafts that run past the chunk end are the sweep's: the sequence's
+    // first workgroup puts it on the sweep's list
+    if (a.work && k >= 0 && k < Q && k + T > Q && wid % HQ == 0 && threadIdx.x == 0) {
+        int32_t *wl = a.work + a.num_slots;
+        wl[kListHead + atomicAdd(wl, 1)] = sq;
+    }
     if (k < 0 || k >= Q || k + T > Q)
         return;
     const SlotRows<PG> rows(a.bm, slot, Q);
@@ -2289,6 +2336,11 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
                 hipSuccess)
             return e;
         const int grid = std::max(1, std::min(a.d.H * a.S, cus));
+        if (a.work && a.no_y) {
+            k_sweep_list<<<dim3(1), dim3(1024), 0, stream>>>(a);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
         k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), bytes, stream>>>(a);
         return hipGetLastError();
     }

@@ -98,16 +98,21 @@ typedef struct {
  *   buf_len       [num_slots] int32        tokens buffered, in [0, Q)
  *   boundary_pos  [num_slots] int64        sequence position of the boundary,
  *                                          a multiple of Q
- *   work          [2*num_slots+34] int32   decode bookkeeping: per-slot
- *                                          arrival counters (the last
- *                                          workgroup of a slot advances
- *                                          buf_len), done counters, and a
- *                                          list area: a large batch's
- *                                          ranking (positions, heaviest
- *                                          first) or the slots whose chunk
- *                                          filled in this step; zero before
- *                                          first use, and every call leaves
- *                                          it zero
+ *   work          [2*num_slots+34] int32   bookkeeping: per-slot arrival
+ *                                          counters (the last workgroup of
+ *                                          a slot advances buf_len), done
+ *                                          counters, and a list area: a
+ *                                          large decode batch's ranking
+ *                                          (positions, heaviest first), the
+ *                                          slots whose chunk filled in this
+ *                                          step, or the sequences the
+ *                                          verification / acceptance sweep
+ *                                          replays; zero before first use,
+ *                                          and every call leaves it zero.
+ *                                          Required by the decode calls;
+ *                                          verification and acceptance also
+ *                                          run with NULL (their sweep then
+ *                                          tests every sequence)
  * A fresh slot is all zeros. The struct itself is a host object; the
  * pointers in it are device pointers.
  *
