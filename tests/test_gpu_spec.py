@@ -157,6 +157,40 @@ def test_verify_equals_decode_steps():
             assert same_bits(a[s, :n[s]], b[s, :n[s]])
 
 
+@pytest.mark.parametrize("S", [200, 256])
+def test_large_verify_equals_decode_steps(S):
+    """A batch with more workgroups than run at once (H=32: 8 per sequence,
+    S x 8 > 768), buffers at every offset, so that drafts cross the chunk
+    end for the last offsets and the crossing sweep takes several listed
+    sequences. Outputs equal T decode steps on a copy of the cache; the
+    cache, work array included, is unchanged."""
+    H, P, N, Q, T = 32, 64, 128, 64, 4
+    shape = erd.Shape(H, 1, P, N, Q, "bf16", "bf16")
+    hp = synth.make_head_params(H, 5)
+    pre = Q + (np.arange(S) * 7) % Q               # every buffer fill, shuffled
+    lengths = pre + T
+    cu = synth.cu_seqlens(lengths)
+    x, dt, B, C = synth.make_tokens_torch(int(cu[-1]), H, 1, P, N, 5, DEV)
+    A, D, bias = (torch.from_numpy(v).to(DEV) for v in (hp.A, hp.D, hp.dt_bias))
+    cache = erd.ReplayCache(shape, S, DEV)
+    ip = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + pre[s])
+                                          for s in range(S)])).to(DEV)
+    erd.ssd_replay_prefill(shape, cache, synth.cu_seqlens(pre), x[ip], dt[ip], B[ip], C[ip],
+                           A, D, bias)
+    idr = torch.from_numpy(np.concatenate([np.arange(cu[s] + pre[s], cu[s + 1])
+                                           for s in range(S)])).to(DEV)
+    dcu = synth.cu_seqlens([T] * S)
+    before = cache_bits(cache)
+    yv = erd.ssd_replay_verify(shape, cache, dcu, x[idr], dt[idr], B[idr], C[idr], A, D, bias)
+    assert unchanged(cache, before), "verification wrote to the cache"
+    dec = cache.clone()
+    yd = []
+    for k in range(T):
+        it = torch.from_numpy((cu[:-1] + pre + k).astype(np.int64)).to(DEV)
+        yd.append(erd.ssd_replay_decode(shape, dec, x[it], dt[it], B[it], C[it], A, D, bias))
+    assert same_bits(yv.view(S, T, H, P), torch.stack(yd, 1))
+
+
 def test_accept_clamps_and_zero():
     """accepted < 0 commits nothing, accepted > drafts commits all drafts."""
     pr = make_problem([100, 100], H=4, G=1, P=64, N=128, Q=32, seed=6)
