@@ -54,6 +54,10 @@ struct ScanArgs {
     int32_t dry, no_y;
     const int32_t *take;
     int32_t only_cross;       // dry replay of the sequences whose drafts cross the chunk end
+    // plain prefill with each head's P columns in two halves, one workgroup
+    // each (launched with the half width; d.P stays the full width); 0 or 1:
+    // one workgroup per head
+    int32_t psplit;
     // the cache's work array (or null): the sweeps of verification and
     // acceptance take their sequences from a list kept in it
     int32_t *work;

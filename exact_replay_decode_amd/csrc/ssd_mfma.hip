@@ -484,6 +484,10 @@ struct MView {
     int64_t tok_base;
     int nb, n_valid;
     int h, g, H, G;
+    // input x and output y rows: elements per token (H times the full head
+    // width) and the first column of this workgroup's part of the head
+    int64_t xrow;
+    int xoff;
     __device__ int64_t token(int j) const { return tok_base + (j - nb); }
 };
 
@@ -565,9 +569,9 @@ __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h
     if (v.nb == 0) {
         // every row is an input token: row j at base + j * stride; the
         // pieces are dealt to the waves as one sequence, x then B
-        const char *xb = reinterpret_cast<const char *>(v.x + (v.token(0) * v.H + v.h) * P);
+        const char *xb = reinterpret_cast<const char *>(v.x + v.token(0) * v.xrow + v.xoff);
         const char *bb = reinterpret_cast<const char *>(v.B + (v.token(0) * v.G + v.g) * N);
-        stage_stream<P * 2, XRB, XK, NWV>(xb, v.H * P * 2, r0, v.n_valid, wv,
+        stage_stream<P * 2, XRB, XK, NWV>(xb, (int)v.xrow * 2, r0, v.n_valid, wv,
                                           lds + L.X + h0 * XRB);
         stage_stream<N * 2, BRB, BK, NWV>(bb, v.G * N * 2, r0, v.n_valid,
                                           ((wv - XK) % NWV + NWV) % NWV, lds + L.B + h0 * BRB);
@@ -794,7 +798,7 @@ __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int
     const int t = 32 * tau + c;
     if (t < row_lo || t >= row_hi)
         return;
-    uint16_t *yrow = y + (v.token(t) * v.H + v.h) * P;
+    uint16_t *yrow = y + v.token(t) * v.xrow + v.xoff;
     const char *xrow = lds + L.X + t * L.XS * 2;
     // four outputs at a time (bf16 pairs rounded to nearest even, as one
     // conversion each), so that few of them are live at once
@@ -852,7 +856,8 @@ __device__ __forceinline__ int wave_tblock(int nT, int wave) {
 }
 
 template <int P, int N, class DT, bool PG, bool RP>
-__device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *lds) {
+__device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *lds,
+                                         int part = 0) {
     using TD = typename DT::T;
     using SL = Slab<P, N>;
     const Dims d = a.d;
@@ -861,7 +866,10 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     const int g = h / (H / G);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool swave = wave < kStateWaves;
-    constexpr int PN = P * N;
+    // this workgroup's columns of the head: P of the head's d.P (all of them,
+    // or half with psplit), from column p0; a head's state is [d.P][N]
+    const int p0 = part * P;
+    const int64_t HS = (int64_t)d.P * N, p0N = (int64_t)p0 * N;
     const MLayout L(kMaxQ, P, N);
     // replay calls (RP) read the slot cache and buffer; plain prefill does not
     constexpr bool replay = RP;
@@ -883,9 +891,9 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     if (!rows.ok(a.bm, (RP && a.dry) ? nbuf : replay_npos(nbuf, len, Q)))
         return;
 
-    float *init = replay ? a.cache_state + ((int64_t)slot * H + h) * PN
+    float *init = replay ? a.cache_state + ((int64_t)slot * H + h) * HS
                            : (a.init_state ? const_cast<float *>(a.init_state) +
-                                                 ((int64_t)s * H + h) * PN
+                                                 ((int64_t)s * H + h) * HS + p0N
                                            : nullptr);
     // the state waves' tiles of the state, and its bf16 read-out copy in LDS
     int ps, nt0;
@@ -904,6 +912,8 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     v.bdt = replay ? static_cast<const TD *>(a.buf_dt) : nullptr;
     v.rows = rows;
     v.h = h; v.g = g; v.H = H; v.G = G;
+    v.xrow = (int64_t)H * d.P;
+    v.xoff = h * d.P + p0;
 
     const float A2_h = a.A[h] * kLog2e;
     const float D_h = a.D ? a.D[h] : 0.0f;
@@ -912,11 +922,11 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     const int nfull = total / Q;
     // without outputs only the chunks that fill are processed
     const int nchunks = (RP && a.no_y) ? nfull : (total + Q - 1) / Q;
-    float *bnd = replay ? a.cache_state + ((int64_t)slot * H + h) * PN
-                          : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * PN
+    float *bnd = replay ? a.cache_state + ((int64_t)slot * H + h) * HS
+                          : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * HS + p0N
                                               : nullptr);
     uint16_t *bnd_bf = replay ? static_cast<uint16_t *>(a.cache_state_bf) +
-                                      ((int64_t)slot * H + h) * PN
+                                      ((int64_t)slot * H + h) * HS
                                 : nullptr;
     const bool write_bnd = bnd && (!replay || nfull > 0) && !(RP && a.dry);
     uint16_t *y = static_cast<uint16_t *>(a.y);
@@ -926,7 +936,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     if (!replay && a.chunk_states)
         cst = a.chunk_states +
               ((int64_t)full_chunks_before(a.cu, s, Q, reinterpret_cast<int *>(lds + L.tot)) * H +
-               h) * PN;
+               h) * HS + p0N;
     const int tau = wave_tblock(Qp / 32, wave);
     auto set_chunk = [&](int c) {
         v.nb = (c == 0) ? nbuf : 0;
@@ -978,7 +988,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
                     slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
             }
             if (cst && c >= 1 && c <= nfull)
-                slab_io<P, N, SL::NT, false>(cst + (int64_t)(c - 1) * H * PN, ps, nt0, S);
+                slab_io<P, N, SL::NT, false>(cst + (int64_t)(c - 1) * H * HS, ps, nt0, S);
             set_chunk(c);
             const int n_valid = v.n_valid;
             const bool upd = n_valid == Q || (!replay && a.final_state);
@@ -1027,14 +1037,15 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             __syncthreads();   // end of chunk c
         }
         if (cst && nfull == nchunks && nfull > 0)
-            slab_io<P, N, SL::NT, false>(cst + (int64_t)(nfull - 1) * H * PN, ps, nt0, S);
+            slab_io<P, N, SL::NT, false>(cst + (int64_t)(nfull - 1) * H * HS, ps, nt0, S);
         if (nfull == nchunks && write_bnd) {
             slab_io<P, N, SL::NT, false>(bnd, ps, nt0, S);
             if (bnd_bf)
                 slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
         }
         if (!replay && a.final_state)
-            slab_io<P, N, SL::NT, false>(a.final_state + ((int64_t)s * H + h) * PN, ps, nt0, S);
+            slab_io<P, N, SL::NT, false>(a.final_state + ((int64_t)s * H + h) * HS + p0N, ps, nt0,
+                                         S);
     } else {
         // t-block waves. The C rows of the t-block's next chunk go out right
         // after its outputs; a t-block without output rows loads, and
@@ -1097,7 +1108,13 @@ template <int P, int N, class DT, bool PG, bool RP>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int wid = xcd_local_index(blockIdx.x, gridDim.x);
-    scan_one<P, N, DT, PG, RP>(a, wid / a.d.H, wid % a.d.H, lds);
+    if (a.psplit == 2) {
+        // both halves of a head's columns next to each other
+        const int hp = wid % (2 * a.d.H);
+        scan_one<P, N, DT, PG, RP>(a, wid / (2 * a.d.H), hp >> 1, lds, hp & 1);
+    } else {
+        scan_one<P, N, DT, PG, RP>(a, wid / a.d.H, wid % a.d.H, lds);
+    }
 }
 
 // The work array after the per-slot arrival counters: [0] number of entries
@@ -2353,6 +2370,28 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     }
     if (PG)
         return hipErrorInvalidValue;   // paged buffers belong to replay calls
+    if constexpr (P == 64) {
+        // Few (sequence, head) pairs (a batch-1 prompt): each head's columns
+        // in two halves, one workgroup each. The halves share nothing but
+        // the per-row quantities and C.B^T, which each computes identically,
+        // so every output and state element has the bits of the one-workgroup
+        // form, on twice as many compute units.
+        int dev = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess ||
+            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+                hipSuccess)
+            return e;
+        if ((int64_t)a.d.H * a.S * 2 <= cus) {
+            const MLayout Lh(kMaxQ, P / 2, N);
+            if ((e = set_lds(k_scan_mfma<P / 2, N, DT, false, false>, Lh.bytes)) != hipSuccess)
+                return e;
+            ScanArgs h = a;
+            h.psplit = 2;
+            k_scan_mfma<P / 2, N, DT, false, false>
+                <<<dim3(2 * a.d.H * a.S), dim3(64 * kPrefillWaves), Lh.bytes, stream>>>(h);
+            return hipGetLastError();
+        }
+    }
     if ((e = set_lds(k_scan_mfma<P, N, DT, false, false>, L.bytes)) != hipSuccess)
         return e;
     k_scan_mfma<P, N, DT, false, false>
