@@ -408,11 +408,12 @@ __device__ __forceinline__ void slab_io(float *g, int ps, int nt0, f32x4 (&S)[NT
 }
 
 // bf16 (nearest even) of the tiles: into the row-major S_bf tile in LDS
-// (byte base sb, row stride ss; sb < 0: not stored) and into a [N/16][P][16]
-// bf16 copy in global memory (gbf, or null).
+// (byte base sb, row stride ss; sb < 0: not stored) and into a [N/16][gP][16]
+// bf16 copy in global memory (gbf, or null), the tiles' rows from row gp0 of
+// it (a workgroup holding columns gp0 .. gp0 + P - 1 of a head of width gP).
 template <int P, int NT>
 __device__ __forceinline__ void slab_bf16(const f32x4 (&S)[NT], int ps, int nt0, char *lds, int sb,
-                                          int ss, uint16_t *gbf) {
+                                          int ss, uint16_t *gbf, int gP = P, int gp0 = 0) {
     const int lane = lane_id();
     const int p = 16 * ps + (lane & 15), q = lane >> 4;
 #pragma unroll
@@ -422,7 +423,7 @@ __device__ __forceinline__ void slab_bf16(const f32x4 (&S)[NT], int ps, int nt0,
         if (sb >= 0)
             *reinterpret_cast<uint2 *>(lds + sb + (p * ss + n) * 2) = v;
         if (gbf)
-            *reinterpret_cast<uint2 *>(gbf + state_bf_index(p, n, P)) = v;
+            *reinterpret_cast<uint2 *>(gbf + state_bf_index(gp0 + p, n, gP)) = v;
     }
 }
 
@@ -580,12 +581,12 @@ __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h
         // row rows(0) + j), the others from the input (row nb is token
         // tok_base)
         const int64_t b0 = v.rows(0);
-        const char *xbuf = reinterpret_cast<const char *>(v.bx + (b0 * v.H + v.h) * P);
+        const char *xbuf = reinterpret_cast<const char *>(v.bx + b0 * v.xrow + v.xoff);
         const char *bbuf = reinterpret_cast<const char *>(v.bB + (b0 * v.G + v.g) * N);
-        const char *xin = reinterpret_cast<const char *>(v.x + (v.tok_base * v.H + v.h) * P);
+        const char *xin = reinterpret_cast<const char *>(v.x + v.tok_base * v.xrow + v.xoff);
         const char *bin = reinterpret_cast<const char *>(v.B + (v.tok_base * v.G + v.g) * N);
-        stage_stream_split<P * 2, XRB, XK, NWV>(xbuf, xin, v.H * P * 2, v.nb, r0, v.n_valid, wv,
-                                                lds + L.X + h0 * XRB);
+        stage_stream_split<P * 2, XRB, XK, NWV>(xbuf, xin, (int)v.xrow * 2, v.nb, r0, v.n_valid,
+                                                wv, lds + L.X + h0 * XRB);
         stage_stream_split<N * 2, BRB, BK, NWV>(bbuf, bin, v.G * N * 2, v.nb, r0, v.n_valid,
                                                 ((wv - XK) % NWV + NWV) % NWV,
                                                 lds + L.B + h0 * BRB);
@@ -601,7 +602,7 @@ __device__ __forceinline__ void stage_slab(const MView<DT, PG> &v, int r0, int h
             const int64_t br = v.rows(jj);   // (paged: every lane takes part)
             const bool buf = jj < v.nb;
             const uint16_t *src =
-                isx ? (buf ? v.bx + (br * v.H + v.h) * P : v.x + (v.token(jj) * v.H + v.h) * P)
+                isx ? (buf ? v.bx + br * v.xrow + v.xoff : v.x + v.token(jj) * v.xrow + v.xoff)
                     : (buf ? v.bB + (br * v.G + v.g) * N : v.B + (v.token(jj) * v.G + v.g) * N);
             char *dst = lds + (isx ? L.X + h0 * XRB : L.B + h0 * BRB) + kk * 1024;
             if (ok)
@@ -891,7 +892,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     if (!rows.ok(a.bm, (RP && a.dry) ? nbuf : replay_npos(nbuf, len, Q)))
         return;
 
-    float *init = replay ? a.cache_state + ((int64_t)slot * H + h) * HS
+    float *init = replay ? a.cache_state + ((int64_t)slot * H + h) * HS + p0N
                            : (a.init_state ? const_cast<float *>(a.init_state) +
                                                  ((int64_t)s * H + h) * HS + p0N
                                            : nullptr);
@@ -922,7 +923,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
     const int nfull = total / Q;
     // without outputs only the chunks that fill are processed
     const int nchunks = (RP && a.no_y) ? nfull : (total + Q - 1) / Q;
-    float *bnd = replay ? a.cache_state + ((int64_t)slot * H + h) * HS
+    float *bnd = replay ? a.cache_state + ((int64_t)slot * H + h) * HS + p0N
                           : (a.boundary_state ? a.boundary_state + ((int64_t)s * H + h) * HS + p0N
                                               : nullptr);
     uint16_t *bnd_bf = replay ? static_cast<uint16_t *>(a.cache_state_bf) +
@@ -985,7 +986,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             if (c == nfull && write_bnd) {
                 slab_io<P, N, SL::NT, false>(bnd, ps, nt0, S);
                 if (bnd_bf)
-                    slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
+                    slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf, d.P, p0);
             }
             if (cst && c >= 1 && c <= nfull)
                 slab_io<P, N, SL::NT, false>(cst + (int64_t)(c - 1) * H * HS, ps, nt0, S);
@@ -1041,7 +1042,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
         if (nfull == nchunks && write_bnd) {
             slab_io<P, N, SL::NT, false>(bnd, ps, nt0, S);
             if (bnd_bf)
-                slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf);
+                slab_bf16<P, SL::NT>(S, ps, nt0, lds, -1, 0, bnd_bf, d.P, p0);
         }
         if (!replay && a.final_state)
             slab_io<P, N, SL::NT, false>(a.final_state + ((int64_t)s * H + h) * HS + p0N, ps, nt0,
@@ -2361,6 +2362,35 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
         k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), bytes, stream>>>(a);
         return hipGetLastError();
     }
+    if constexpr (P == 64) {
+        // Few (sequence, head) pairs (a batch-1 prompt or prompt chunk): each
+        // head's columns in two halves, one workgroup each. The halves share
+        // nothing but the per-row quantities and C.B^T, which each computes
+        // identically, so every output and state element has the bits of the
+        // one-workgroup form, on twice as many compute units.
+        int dev = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess ||
+            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+                hipSuccess)
+            return e;
+        if ((int64_t)a.d.H * a.S * 2 <= cus) {
+            const MLayout Lh(kMaxQ, P / 2, N);
+            if (PG && !a.replay)
+                return hipErrorInvalidValue;   // paged buffers belong to replay calls
+            void (*kern)(ScanArgs);
+            if constexpr (PG)
+                kern = k_scan_mfma<P / 2, N, DT, true, true>;
+            else
+                kern = a.replay ? k_scan_mfma<P / 2, N, DT, false, true>
+                                : k_scan_mfma<P / 2, N, DT, false, false>;
+            if ((e = set_lds(kern, Lh.bytes)) != hipSuccess)
+                return e;
+            ScanArgs h = a;
+            h.psplit = 2;
+            kern<<<dim3(2 * a.d.H * a.S), dim3(64 * kPrefillWaves), Lh.bytes, stream>>>(h);
+            return hipGetLastError();
+        }
+    }
     if (a.replay) {
         if ((e = set_lds(k_scan_mfma<P, N, DT, PG, true>, L.bytes)) != hipSuccess)
             return e;
@@ -2370,28 +2400,6 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     }
     if (PG)
         return hipErrorInvalidValue;   // paged buffers belong to replay calls
-    if constexpr (P == 64) {
-        // Few (sequence, head) pairs (a batch-1 prompt): each head's columns
-        // in two halves, one workgroup each. The halves share nothing but
-        // the per-row quantities and C.B^T, which each computes identically,
-        // so every output and state element has the bits of the one-workgroup
-        // form, on twice as many compute units.
-        int dev = 0, cus = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess ||
-            (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
-                hipSuccess)
-            return e;
-        if ((int64_t)a.d.H * a.S * 2 <= cus) {
-            const MLayout Lh(kMaxQ, P / 2, N);
-            if ((e = set_lds(k_scan_mfma<P / 2, N, DT, false, false>, Lh.bytes)) != hipSuccess)
-                return e;
-            ScanArgs h = a;
-            h.psplit = 2;
-            k_scan_mfma<P / 2, N, DT, false, false>
-                <<<dim3(2 * a.d.H * a.S), dim3(64 * kPrefillWaves), Lh.bytes, stream>>>(h);
-            return hipGetLastError();
-        }
-    }
     if ((e = set_lds(k_scan_mfma<P, N, DT, false, false>, L.bytes)) != hipSuccess)
         return e;
     k_scan_mfma<P, N, DT, false, false>
