@@ -270,3 +270,63 @@ def test_full_batch_prefill_sampled_parity():
         ys, fs, _ = erd.ssd_prefill_varlen(shape, [0, T], x[sl], dt[sl], A, B[sl], C[sl], D,
                                            bias)
         assert same_bits(ys, y[sl]) and same_bits(fs[0], fin[s])
+
+
+# ---- whole heads and split columns ----------------------------------------
+
+def test_split_columns_equal_whole_heads():
+    """With few (sequence, head) pairs the prefill runs each head as two
+    workgroups on its column halves, with many as one workgroup per head.
+    Each sequence of an 8-sequence pack (H=32: 256 pairs, whole heads) run
+    alone (32 pairs, split columns) gives the same outputs, final, boundary
+    and chunk states bit for bit, from seeded initial states; and continuing
+    a replay cache sequence by sequence (split) or as one pack (whole) leaves
+    the same outputs and cache."""
+    H, G, P, N, Q = 32, 1, 64, 128, 256
+    lengths = [700, 300, 900, 256, 130, 512, 1000, 77]
+    S = len(lengths)
+    pr = make_problem(lengths, H=H, G=G, P=P, N=N, Q=Q, seed=11)
+    x, dt, B, C = pr.dev(None)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    init = (torch.randn((S, H, P, N), generator=g) * 0.1).to(DEV)
+    y, fin, bnd, cst = erd.ssd_prefill_varlen(pr.shape, pr.cu, x, dt, pr.A, B, C, pr.D, pr.bias,
+                                              init_state=init, want_chunk_states=True)
+    cu = pr.cu
+    f0 = 0
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        ys, fs, bs, cs = erd.ssd_prefill_varlen(pr.shape, [0, b - a], x[a:b], dt[a:b], pr.A,
+                                                B[a:b], C[a:b], pr.D, pr.bias,
+                                                init_state=init[s:s + 1].contiguous(),
+                                                want_chunk_states=True)
+        nf = (b - a) // Q
+        assert same_bits(ys, y[a:b]), s
+        assert same_bits(fs, fin[s:s + 1]) and same_bits(bs, bnd[s:s + 1]), s
+        assert same_bits(cs, cst[f0:f0 + nf]), s
+        f0 += nf
+    # replay: the first 60 % of every sequence as one pack, then the rest as
+    # one pack (cache A) or sequence by sequence (cache B)
+    first = [int(L * 0.6) for L in lengths]
+    rest = [L - f for L, f in zip(lengths, first)]
+    i1 = torch.from_numpy(np.concatenate([np.arange(cu[s], cu[s] + first[s])
+                                          for s in range(S)])).to(DEV)
+    i2 = [torch.arange(int(cu[s]) + first[s], int(cu[s + 1]), device=DEV) for s in range(S)]
+    caches = []
+    for mode in ("pack", "each"):
+        cache = erd.ReplayCache(pr.shape, S, DEV, with_C=True)
+        erd.ssd_replay_prefill(pr.shape, cache, np.cumsum([0] + first), x[i1], dt[i1], B[i1],
+                               C[i1], pr.A, pr.D, pr.bias)
+        if mode == "pack":
+            i = torch.cat(i2)
+            y2 = erd.ssd_replay_prefill(pr.shape, cache, np.cumsum([0] + rest), x[i], dt[i],
+                                        B[i], C[i], pr.A, pr.D, pr.bias)
+        else:
+            y2 = torch.cat([erd.ssd_replay_prefill(
+                pr.shape, cache, [0, rest[s]], x[i2[s]], dt[i2[s]], B[i2[s]], C[i2[s]], pr.A,
+                pr.D, pr.bias, slot_idx=torch.tensor([s], dtype=torch.int32, device=DEV))
+                for s in range(S)])
+        caches.append((y2, cache))
+    (ya, ca), (yb, cb) = caches
+    assert same_bits(ya, yb)
+    for name in ("state", "state_bf", "buf_len", "boundary_pos", "work"):
+        assert same_bits(getattr(ca, name), getattr(cb, name)), name
