@@ -206,6 +206,8 @@ int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, i
     // the sweeps of verification and acceptance list their sequences in the
     // work array, which has room for num_slots of them
     a.work = mode != 0 && S <= cache->num_slots ? cache->work : nullptr;
+    for (int32_t s = 0; s < S; ++s)
+        a.max_len = std::max(a.max_len, cu_host[s + 1] - cu_host[s]);
     if (mode == 1)   // verification writes only y
         return hip_status(ssd::mfma_supported(d) ? ssd::launch_verify_mfma(a, (hipStream_t)stream)
                                                  : ssd::launch_scan(a, (hipStream_t)stream));

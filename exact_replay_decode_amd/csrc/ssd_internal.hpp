@@ -58,6 +58,8 @@ struct ScanArgs {
     // each (launched with the half width; d.P stays the full width); 0 or 1:
     // one workgroup per head
     int32_t psplit;
+    // verification: the most drafts any sequence has (host-side count)
+    int32_t max_len;
     // the cache's work array (or null): the sweeps of verification and
     // acceptance take their sequences from a list kept in it
     int32_t *work;

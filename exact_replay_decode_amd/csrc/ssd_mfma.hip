@@ -2068,7 +2068,8 @@ struct VLayout {
 };
 
 template <int P, int N, class DT, bool PG, bool GSHARE>
-__global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(GSHARE ? 3 : 1)))
+void k_verify_mfma(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds_all[];
     using TD = typename DT::T;
     constexpr int NPT = P / 32, NK = N / 16;
@@ -2180,18 +2181,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
         }
         const float lam_t = lam[t];
         // read-out from the bf16 state copy (operand (pt, kk) is 1 KiB
-        // contiguous)
+        // contiguous); it starts the accumulators, before any s-block
         f32x16 acc[NPT];
+        auto readout = [&]() {
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt)
-            acc[pt] = readout_scale(
-                readout_raw<N>(
-                    [&](int kk) {
-                        return *reinterpret_cast<const bf16x8 *>(
-                            sbf + ((int64_t)kk * P + 32 * pt + c) * 16 + 8 * gl);
-                    },
-                    cf),
-                fexp2(lam_t));
+            for (int pt = 0; pt < NPT; ++pt)
+                acc[pt] = readout_scale(
+                    readout_raw<N>(
+                        [&](int kk) {
+                            return *reinterpret_cast<const bf16x8 *>(
+                                sbf + ((int64_t)kk * P + 32 * pt + c) * 16 + 8 * gl);
+                        },
+                        cf),
+                    fexp2(lam_t));
+        };
         // B rows and x rows of s-block sg (committed rows from the buffer,
         // drafts from the inputs)
         constexpr int XPL = P / 16;
@@ -2240,32 +2243,34 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
             mx_accumulate<0, NPT>(mb, lds, L.X, L.XS, 0, acc, lane);
         };
         if constexpr (gshare) {
-            // the C.B^T blocks of this t-block, split between the waves
-            // (s-blocks wave, wave + 4, ...) and handed over in LDS, where
-            // element r of lane l sits at float (r / 4) * 256 + 4 l + r % 4
+            // The C.B^T blocks of this t-block, split between the waves
+            // (s-blocks wave, wave + 4, ...) and handed over in LDS: only the
+            // columns of the t-block's drafts (chunk rows c_lo .. c_lo + gcols
+            // - 1 of it; the others' weights are zeroed anyway), column t at
+            // floats (t - c_lo) * 32 + s. The read-out follows the hand-over
+            // and each block's B rows are loaded just before its MFMAs, so
+            // that the wave holds no more than three waves per SIMD allow.
+            const int gcols = min(a.max_len, 32);
+            const int c_lo = max(k, 32 * tau) - 32 * tau;
+            const bool gcol = c >= c_lo && c < c_lo + gcols;
             uint4 nx_[XPL];
             load_x(0, nx_);
             if (tau > tau0)
                 __syncthreads();   // the previous t-block's blocks are read
-            if (wave <= tau) {
-                uint4 nb_[NK];
-                load_b(wave, nb_);
-                for (int sg = wave; sg <= tau; sg += kDecodeWaves) {
-                    uint4 braw[NK];
-#pragma unroll
-                    for (int kk = 0; kk < NK; ++kk)
-                        braw[kk] = nb_[kk];
-                    if (sg + kDecodeWaves <= tau)
-                        load_b(sg + kDecodeWaves, nb_);
-                    const f32x16 gt = gram_of(sg, braw);
-                    float *dst = gsh + sg * 1024 + 4 * lane;
+            for (int sg = wave; sg <= tau; sg += kDecodeWaves) {
+                uint4 braw[NK];
+                load_b(sg, braw);
+                const f32x16 gt = gram_of(sg, braw);
+                if (gcol) {
+                    float *dst = gsh + (sg * gcols + c - c_lo) * 32 + 4 * gl;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<float4 *>(dst + 256 * q) =
+                        *reinterpret_cast<float4 *>(dst + 8 * q) =
                             make_float4(gt[4 * q], gt[4 * q + 1], gt[4 * q + 2], gt[4 * q + 3]);
                 }
             }
             __syncthreads();
+            readout();
             for (int sg = 0; sg <= tau; ++sg) {
                 uint4 xr[XPL];
 #pragma unroll
@@ -2273,19 +2278,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_verify_mfma(ScanArgs a) {
                     xr[i] = nx_[i];
                 if (sg < tau)
                     load_x(sg + 1, nx_);
-                const float *src = gsh + sg * 1024 + 4 * lane;
-                f32x16 gt;
+                f32x16 gt = {};
+                if (gcol) {
+                    const float *src = gsh + (sg * gcols + c - c_lo) * 32 + 4 * gl;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4 *>(src + 256 * q);
-                    gt[4 * q] = v.x;
-                    gt[4 * q + 1] = v.y;
-                    gt[4 * q + 2] = v.z;
-                    gt[4 * q + 3] = v.w;
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = *reinterpret_cast<const float4 *>(src + 8 * q);
+                        gt[4 * q] = v.x;
+                        gt[4 * q + 1] = v.y;
+                        gt[4 * q + 2] = v.z;
+                        gt[4 * q + 3] = v.w;
+                    }
                 }
                 accumulate(sg, gt, xr);
             }
         } else {
+            readout();
             // one block ahead of their use
             uint4 nb_[NK], nx_[XPL];
             load_b(0, nb_);
@@ -2481,8 +2489,9 @@ hipError_t verify_mfma(const ScanArgs &a, hipStream_t stream) {
     const int Qp = a.d.Q < 32 ? 32 : a.d.Q;
     // per-wave areas, then the shared C.B^T blocks (32 x 32 fp32 each)
     const bool gshare = (a.d.H / a.d.G) % kDecodeWaves == 0;
+    // (the shared blocks keep only the drafts' columns: at most 32 of each)
     const size_t bytes = (size_t)VLayout(Qp, P).bytes * kDecodeWaves +
-                         (gshare ? (size_t)(Qp / 32) * 4096 : 0);
+                         (gshare ? (size_t)(Qp / 32) * 32 * std::min(a.max_len, 32) * 4 : 0);
     const auto kern = gshare ? k_verify_mfma<P, N, DT, PG, true> : k_verify_mfma<P, N, DT, PG, false>;
     hipError_t e = set_lds(kern, bytes);
     if (e != hipSuccess)
