@@ -1191,8 +1191,8 @@ __global__ __launch_bounds__(1024) void k_sweep_list(ScanArgs a) {
 // different workgroups.
 // With the work array (a.work), the sequences come from the list that the
 // verification kernel or k_sweep_list put there: the pairs (listed
-// sequence, head) are dealt to the workgroups in turn, so no workgroup
-// replays two while another has none, and the last workgroup empties the
+// sequence, head) are dealt to the workgroups in turn, so no workgroup has
+// more than one pair more than another, and the last workgroup empties the
 // list.
 template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
