@@ -204,8 +204,8 @@ int replay_scan(const ssd_shape *sh, const ssd_replay_cache *cache, int32_t S, i
     a.no_y = mode == 2;
     a.take = mode == 2 ? take : nullptr;
     // the sweeps of verification and acceptance list their sequences in the
-    // work array, which has room for num_slots of them
-    a.work = mode != 0 && S <= cache->num_slots ? cache->work : nullptr;
+    // work array (distinct slots: S <= num_slots, the list's room)
+    a.work = mode != 0 ? cache->work : nullptr;
     for (int32_t s = 0; s < S; ++s)
         a.max_len = std::max(a.max_len, cu_host[s + 1] - cu_host[s]);
     if (mode == 1)   // verification writes only y

@@ -1184,54 +1184,24 @@ __global__ __launch_bounds__(1024) void k_sweep_list(ScanArgs a) {
 // Replay calls where few sequences have work: verification of drafts that
 // run past the chunk end (dry replay, only_cross), and acceptance (no_y),
 // where only the sequences whose accepted drafts fill a chunk have any.
-// One round of workgroups; each tests the (sequence, head) pairs
-// e = blockIdx.x + gridDim.x i in parallel, lists those with work in LDS
-// and replays them one after another. The pairs with nothing to do cost no
-// dispatch of a large-LDS workgroup, and a sequence's heads land on
-// different workgroups.
-// With the work array (a.work), the sequences come from the list that the
-// verification kernel or k_sweep_list put there: the pairs (listed
-// sequence, head) are dealt to the workgroups in turn, so no workgroup has
-// more than one pair more than another, and the last workgroup empties the
-// list.
+// One round of workgroups (at most one per compute unit), so the pairs with
+// nothing to do cost no dispatch of a large-LDS workgroup.
+// The sequences come from the list that the verification kernel or
+// k_sweep_list put in the work array: the pairs (listed sequence, head) are
+// dealt to the workgroups in turn, so no workgroup has more than one pair
+// more than another, and the last workgroup empties the list.
 template <int P, int N, class DT, bool PG>
 __global__ __launch_bounds__(64 * kPrefillWaves, 1) void k_scan_cross(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int H = a.d.H;
-    if (a.work) {
-        int32_t *wl = a.work + a.num_slots;
-        const int n = wl[0];
-        for (int j = blockIdx.x; j < n * H; j += gridDim.x) {
-            const int s = wl[kListHead + j / H];
-            __syncthreads();   // the previous pair's LDS use is over
-            scan_one<P, N, DT, PG, true>(a, s, j % H, lds);
-        }
-        work_list_done(wl, n, true);
-        return;
+    int32_t *wl = a.work + a.num_slots;
+    const int n = wl[0];
+    for (int j = blockIdx.x; j < n * H; j += gridDim.x) {
+        const int s = wl[kListHead + j / H];
+        __syncthreads();   // the previous pair's LDS use is over
+        scan_one<P, N, DT, PG, true>(a, s, j % H, lds);
     }
-    const MLayout L(kMaxQ, P, N);   // scan_one's layout
-    int *list = reinterpret_cast<int *>(lds + L.bytes);   // [1 + 64 * kPrefillWaves]
-    const int total = a.S * H;
-    const int rounds = (total + gridDim.x - 1) / gridDim.x;   // candidates per workgroup
-    for (int base = 0; base < rounds; base += 64 * kPrefillWaves) {
-        if (threadIdx.x == 0)
-            list[0] = 0;
-        __syncthreads();
-        const int i = base + threadIdx.x;
-        const int e = blockIdx.x + gridDim.x * i;
-        if (i < rounds && e < total) {
-            if (sweep_has_work(a, e / H))
-                list[1 + atomicAdd(list, 1)] = e;
-        }
-        __syncthreads();
-        const int n = list[0];
-        for (int j = 0; j < n; ++j) {
-            const int ej = list[1 + j];
-            __syncthreads();   // the previous pair's LDS use is over
-            scan_one<P, N, DT, PG, true>(a, ej / H, ej % H, lds);
-        }
-        __syncthreads();   // list reads are done before the next round resets it
-    }
+    work_list_done(wl, n, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -2096,7 +2066,7 @@ void k_verify_mfma(ScanArgs a) {
     const int k = a.buf_len[slot];
     // drafts that run past the chunk end are the sweep's: the sequence's
     // first workgroup puts it on the sweep's list
-    if (a.work && k >= 0 && k < Q && k + T > Q && wid % HQ == 0 && threadIdx.x == 0) {
+    if (k >= 0 && k < Q && k + T > Q && wid % HQ == 0 && threadIdx.x == 0) {
         int32_t *wl = a.work + a.num_slots;
         wl[kListHead + atomicAdd(wl, 1)] = sq;
     }
@@ -2352,9 +2322,9 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
     const MLayout L(kMaxQ, P, N);   // scan_one's layout: full-height tiles for every chunk size
     hipError_t e;
     if (a.only_cross || a.no_y) {
-        // the crossing-draft sweep adds its pair list after the layout
-        const size_t bytes = L.bytes + 4 * (1 + 64 * kPrefillWaves);
-        if ((e = set_lds(k_scan_cross<P, N, DT, PG>, bytes)) != hipSuccess)
+        if (!a.work)
+            return hipErrorInvalidValue;   // the sweeps take their sequences from it
+        if ((e = set_lds(k_scan_cross<P, N, DT, PG>, L.bytes)) != hipSuccess)
             return e;
         int dev = 0, cus = 0;
         if ((e = hipGetDevice(&dev)) != hipSuccess ||
@@ -2362,12 +2332,12 @@ hipError_t scan_mfma(const ScanArgs &a, hipStream_t stream) {
                 hipSuccess)
             return e;
         const int grid = std::max(1, std::min(a.d.H * a.S, cus));
-        if (a.work && a.no_y) {
+        if (a.no_y) {
             k_sweep_list<<<dim3(1), dim3(1024), 0, stream>>>(a);
             if ((e = hipGetLastError()) != hipSuccess)
                 return e;
         }
-        k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), bytes, stream>>>(a);
+        k_scan_cross<P, N, DT, PG><<<dim3(grid), dim3(64 * kPrefillWaves), L.bytes, stream>>>(a);
         return hipGetLastError();
     }
     if constexpr (P == 64) {

@@ -108,11 +108,7 @@ typedef struct {
  *                                          step, or the sequences the
  *                                          verification / acceptance sweep
  *                                          replays; zero before first use,
- *                                          and every call leaves it zero.
- *                                          Required by the decode calls;
- *                                          verification and acceptance also
- *                                          run with NULL (their sweep then
- *                                          tests every sequence)
+ *                                          and every call leaves it zero
  * A fresh slot is all zeros. The struct itself is a host object; the
  * pointers in it are device pointers.
  *
