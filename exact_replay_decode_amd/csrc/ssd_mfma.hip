@@ -224,30 +224,49 @@ __device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float
 // Y^T[p][t] += sum_s X^T[p][s] M^T[s][t] over one s-block, K = 16 rows per
 // MFMA: rows r0 = 16 half + 4g .. +3 and r0 + 8 .. +11 of the block, read
 // transposed from the row-major LDS tile (xbase, row stride xs, block row 0
-// at xrow0); mb[4 half .. 4 half + 3] holds the matching M^T rows.
+// at xrow0); mb[4 half .. 4 half + 3] holds the matching M^T rows. mx_load
+// fetches the X^T operands (xo[half][pt - PT0]) so that a caller can issue
+// them ahead of the weights; mx_apply runs the MFMAs, half by half.
 template <int PT0, int PT1>
-__device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const char *lds, int xbase,
-                                              int xs, int xrow0, f32x16 *acc, int lane) {
+__device__ __forceinline__ void mx_load(const char *lds, int xbase, int xs, int xrow0,
+                                        bf16x8 (&xo)[2][PT1 - PT0], int lane) {
     const int g = lane >> 5;
     // lane terms: the k-group's rows 4g.., the 16-column half of the p-tile
     const int la = tr_lane(lane, xs) + (4 * g * xs + 16 * ((lane >> 4) & 1)) * 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int pt = PT0; pt < PT1; ++pt) {
+            const int a = xbase + ((xrow0 + 16 * half) * xs + 32 * pt) * 2;
+            xo[half][pt - PT0] = as_bf16x8(lds_tr8(lds, la, a, 8 * xs * 2));
+        }
+}
+
+template <int PT0, int PT1>
+__device__ __forceinline__ void mx_apply(const uint32_t (&mb)[8], const bf16x8 (&xo)[2][PT1 - PT0],
+                                         f32x16 *acc) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 bv = {mb[4 * half], mb[4 * half + 1], mb[4 * half + 2], mb[4 * half + 3]};
         const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
 #pragma unroll
-        for (int pt = PT0; pt < PT1; ++pt) {
-            const int a = xbase + ((xrow0 + 16 * half) * xs + 32 * pt) * 2;
-            const bf16x8 aop = as_bf16x8(lds_tr8(lds, la, a, 8 * xs * 2));
-            acc[pt] = mfma(aop, bop, acc[pt]);
-        }
+        for (int pt = PT0; pt < PT1; ++pt)
+            acc[pt] = mfma(xo[half][pt - PT0], bop, acc[pt]);
     }
+}
+
+template <int PT0, int PT1>
+__device__ __forceinline__ void mx_accumulate(const uint32_t (&mb)[8], const char *lds, int xbase,
+                                              int xs, int xrow0, f32x16 *acc, int lane) {
+    bf16x8 xo[2][PT1 - PT0];
+    mx_load<PT0, PT1>(lds, xbase, xs, xrow0, xo, lane);
+    mx_apply<PT0, PT1>(mb, xo, acc);
 }
 
 // Output of one 32-row t-block in prefill: p-tiles [PT0, PT1) of Y^T for
 // chunk rows t = 32 tau + (lane % 32). cf[k] holds C[t][16k + 8g .. +7]
-// (g = lane/32), zero for rows that are not outputs. acc[pt] receives
+// (g = lane/32) for output rows (other rows' columns are not used). acc[pt] receives
 // Y^T[p][t] (without the D x term) for p = 32 pt + 8 (r/4) + 4 g + r % 4.
 // tblock_part takes the s-blocks [sg0, sg1] (sg1 <= tau) after the read-out
 // when sg0 == 0 (which initialises acc): the prefill runs a t-block's
@@ -284,19 +303,24 @@ __device__ __forceinline__ void tblock_part(int tau, int sg0, int sg1, const bf1
     }
 
     const float lam_t = lam[t];
-    auto gram = [&](int sg) {
-        return gram_block<N>(
-            [&](int k) { return lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2); },
-            cf);
-    };
+    // per s-block: all eight B operands of C.B^T are fetched before its
+    // first MFMA (one LDS round trip instead of eight), and the X^T operands
+    // of M.X while the weights are computed
     for (int sg = sg0; sg <= sg1; ++sg) {
-        const f32x16 gt = gram(sg);
+        bf16x8 bo[N / 16];
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k)
+            bo[k] = lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x16 gt = gram_block<N>([&](int k) { return bo[k]; }, cf);
+        bf16x8 xo[2][PT1 - PT0];
+        mx_load<PT0, PT1>(lds, L.X, L.XS, 32 * sg, xo, lane);
         uint32_t mb[8];
         if (sg == tau)
             m_diag(gt, lam_t, uu, 32 * sg, t, mb, lane);
         else
             m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb, lane);
-        mx_accumulate<PT0, PT1>(mb, lds, L.X, L.XS, 32 * sg, acc, lane);
+        mx_apply<PT0, PT1>(mb, xo, acc);
     }
 }
 
@@ -362,6 +386,21 @@ __device__ __forceinline__ void split_wx(const i16x8 &xv, const float (&ws)[8], 
 // the slab's first column xc) and of the B tile (bb, bs); wk points at the
 // state weights of those rows. Lane group q = (lane % 64) / 16 supplies rows
 // 8q .. 8q + 7 of the step: k index j of both operands is row 8q + j.
+// The step's arithmetic from its operands: xv (the lane's 8 raw x values),
+// ws (their state weights) and bop(i), the B^T operand of n-tile nt0 + i.
+template <int NT, class F>
+__device__ __forceinline__ void state_kstep_ops(const i16x8 &xv, const float (&ws)[8], F bop,
+                                                f32x4 (&acc)[NT]) {
+    bf16x8 bhi, blo;
+    split_wx(xv, ws, bhi, blo);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const bf16x8 a = bop(i);
+        acc[i] = mfma16(a, bhi, acc[i]);
+        acc[i] = mfma16(a, blo, acc[i]);
+    }
+}
+
 template <int NT>
 __device__ __forceinline__ void state_kstep(const char *lds, int xb, int xs, int xc, int bb,
                                             int bs, int row0, int nt0, const float *wk,
@@ -373,16 +412,58 @@ __device__ __forceinline__ void state_kstep(const char *lds, int xb, int xs, int
     const float4 w0 = *reinterpret_cast<const float4 *>(wk + 8 * q);
     const float4 w1 = *reinterpret_cast<const float4 *>(wk + 8 * q + 4);
     const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    bf16x8 bhi, blo;
-    split_wx(xv, ws, bhi, blo);
     const int lab = tr_lane(lane, bs) + 8 * q * bs * 2;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const bf16x8 a = as_bf16x8(lds_tr8(lds, lab, bb + (row0 * bs + 16 * (nt0 + i)) * 2,
-                                           4 * bs * 2));
-        acc[i] = mfma16(a, bhi, acc[i]);
-        acc[i] = mfma16(a, blo, acc[i]);
-    }
+    state_kstep_ops<NT>(
+        xv, ws,
+        [&](int i) {
+            return as_bf16x8(lds_tr8(lds, lab, bb + (row0 * bs + 16 * (nt0 + i)) * 2, 4 * bs * 2));
+        },
+        acc);
+}
+
+// The prefill's form of the step, for waves that have direct global-to-LDS
+// loads in flight into other rows of the same tiles. The compiler cannot
+// tell those rows apart and would wait for every load before each LDS read;
+// here each fetch is an asm statement that waits for its own reads
+// (lgkmcnt) only. XS and BS are the x and B row strides in elements.
+__device__ __forceinline__ uint32_t lds_off(const void *p) {
+    return (uint32_t)(uintptr_t)(const lds_char *)p;
+}
+
+template <int D>
+__device__ __forceinline__ i16x8 lds_tr8_own(uint32_t a) {
+    i16x4 x, y;
+    asm volatile("ds_read_b64_tr_b16 %0, %2\n\t"
+                 "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(x), "=&v"(y)
+                 : "v"(a), "i"(D));
+    const i16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return v;
+}
+
+__device__ __forceinline__ void lds_f32x8_own(uint32_t a, f32x4 &w0, f32x4 &w1) {
+    asm volatile("ds_read_b128 %0, %2\n\t"
+                 "ds_read_b128 %1, %2 offset:16\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(w0), "=&v"(w1)
+                 : "v"(a));
+}
+
+template <int NT, int XS, int BS>
+__device__ __forceinline__ void state_kstep_own(const char *lds, int xb, int xc, int bb, int row0,
+                                                int nt0, const float *wk, f32x4 (&acc)[NT]) {
+    const int lane = lane_id();
+    const int q = lane >> 4;
+    const uint32_t l0 = lds_off(lds);
+    const i16x8 xv = lds_tr8_own<4 * XS * 2>(l0 + tr_lane(lane, XS) + 8 * q * XS * 2 + xb +
+                                             (row0 * XS + xc) * 2);
+    f32x4 w0, w1;
+    lds_f32x8_own(lds_off(wk + 8 * q), w0, w1);
+    const float ws[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    const uint32_t lab = l0 + tr_lane(lane, BS) + 8 * q * BS * 2 + bb + (row0 * BS + 16 * nt0) * 2;
+    state_kstep_ops<NT>(
+        xv, ws, [&](int i) { return as_bf16x8(lds_tr8_own<4 * BS * 2>(lab + 32 * i)); }, acc);
 }
 
 // Tiles nt0 .. nt0 + NT - 1 of p-slab ps <-> a [P][N] fp32 state in global
@@ -789,6 +870,24 @@ __device__ __forceinline__ void load_cfrag(const MView<DT, PG> &v, int tau, int 
     }
 }
 
+// The prefill's form: rows that produce no output keep the row they loaded
+// (row row_lo, an input token) instead of zeros. Column t of the read-out,
+// C.B^T and M.X tiles depends on lane column t of cf alone, and columns of
+// rows that are not outputs are never stored, so every stored element is
+// the same; leaving out the select lets the fragments be loaded straight
+// into the registers the MFMAs read.
+template <int N, class DT, bool PG>
+__device__ __forceinline__ void load_cfrag_raw(const MView<DT, PG> &v, int tau, int row_lo,
+                                               bf16x8 (&cf)[N / 16]) {
+    const int lane = lane_id();
+    const int g = lane >> 5, t = 32 * tau + (lane & 31);
+    const bool ok = t >= row_lo && t < v.n_valid && t >= v.nb;
+    const uint16_t *src = v.C + (v.token(ok ? t : row_lo) * v.G + v.g) * N;
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k)
+        cf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 16 * k + 8 * g));
+}
+
 // y rows [row_lo, row_hi) of t-block tau: y = fmaf(D, x, acc), -0 -> +0.
 template <int P, int PT0, int PT1, class V>
 __device__ __forceinline__ void emit_tblock(const V &v, int tau, int row_lo, int row_hi,
@@ -1002,8 +1101,8 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             auto ksteps = [&](char *t, int k0, int k1) {
                 const float *w = reinterpret_cast<const float *>(t + Lc.w);
                 for (int kk = k0; kk < k1; ++kk)
-                    state_kstep<SL::NT>(t, Lc.X, Lc.XS, 16 * ps, Lc.B, Lc.BS, 32 * kk, nt0,
-                                        w + 32 * kk, S);
+                    state_kstep_own<SL::NT, P + kPad, N + kPad>(t, Lc.X, 16 * ps, Lc.B, 32 * kk,
+                                                                nt0, w + 32 * kk, S);
             };
             // Phase 1 (or the only phase): staging this chunk's slab B (two
             // slabs) or the next chunk into the other half, then the K steps
@@ -1049,12 +1148,12 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
                                          S);
     } else {
         // t-block waves. The C rows of the t-block's next chunk go out right
-        // after its outputs; a t-block without output rows loads, and
-        // zeroes, the chunk's last row (n_valid - 1 >= nb is an input token).
+        // after its outputs; a t-block without output rows loads the chunk's
+        // last row (n_valid - 1 >= nb is an input token).
         bf16x8 cf[N / 16];
         auto load_c = [&](const MView<DT, PG> &vv) {
             const int lo = max(32 * tau, vv.nb), hi = min(32 * tau + 32, vv.n_valid);
-            load_cfrag<N, DT>(vv, tau, lo < hi ? lo : vv.n_valid - 1, cf);
+            load_cfrag_raw<N, DT>(vv, tau, lo < hi ? lo : vv.n_valid - 1, cf);
         };
         if (nchunks > 0 && tau >= 0) {
             set_chunk(0);
