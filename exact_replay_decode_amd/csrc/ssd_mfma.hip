@@ -185,17 +185,25 @@ __device__ __forceinline__ f32x16 gram_block(F ba, const bf16x8 *cf) {
     return gt;
 }
 
+// A lane's per-row values of one s-block: v[q] = a[s_base + 8q + 4g .. +3]
+// (g = lane / 32), the rows s of its accumulator elements gt[4q .. 4q + 3].
+__device__ __forceinline__ void srows(const float *a, int s_base, float4 (&v)[4], int lane) {
+    const int g = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        v[q] = *reinterpret_cast<const float4 *>(a + s_base + 8 * q + 4 * g);
+}
+
 // Weights of the diagonal s-block, packed to bf16 pairs: gt[4q + e] =
 // G[t][s] for s = s_base + 8q + 4g + e; m = G 2^(l_t - u_s) for s <= t and +0
-// otherwise (selected, never multiplied).
-__device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const float *uu, int s_base,
-                                       int t, uint32_t (&mb)[8], int lane) {
+// otherwise (selected, never multiplied). u4: the rows' u (srows).
+__device__ __forceinline__ void m_diag_rows(const f32x16 &gt, float lam_t, const float4 (&u4)[4],
+                                            int s_base, int t, uint32_t (&mb)[8], int lane) {
     const int g = lane >> 5;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int s0 = s_base + 8 * q + 4 * g;
-        const float4 u4 = *reinterpret_cast<const float4 *>(uu + s0);
-        const float us[4] = {u4.x, u4.y, u4.z, u4.w};
+        const float us[4] = {u4[q].x, u4[q].y, u4[q].z, u4[q].w};
         float m[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -207,18 +215,31 @@ __device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const floa
     }
 }
 
+__device__ __forceinline__ void m_diag(const f32x16 &gt, float lam_t, const float *uu, int s_base,
+                                       int t, uint32_t (&mb)[8], int lane) {
+    float4 u4[4];
+    srows(uu, s_base, u4, lane);
+    m_diag_rows(gt, lam_t, u4, s_base, t, mb, lane);
+}
+
 // Weights of an earlier s-block: (G alpha) beta_s with alpha = 2^(l_t - c)
-// and beta_s = 2^(c - u_s), c = l at the end of the s-block.
-__device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float *bt, int s_base,
-                                      uint32_t (&mb)[8], int lane) {
-    const int g = lane >> 5;
+// and beta_s = 2^(c - u_s), c = l at the end of the s-block. b4: the rows'
+// beta (srows).
+__device__ __forceinline__ void m_off_rows(const f32x16 &gt, float alpha, const float4 (&b4)[4],
+                                           uint32_t (&mb)[8]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int s0 = s_base + 8 * q + 4 * g;
-        const float4 b4 = *reinterpret_cast<const float4 *>(bt + s0);
-        mb[2 * q] = bf16_pack((gt[4 * q] * alpha) * b4.x, (gt[4 * q + 1] * alpha) * b4.y);
-        mb[2 * q + 1] = bf16_pack((gt[4 * q + 2] * alpha) * b4.z, (gt[4 * q + 3] * alpha) * b4.w);
+        mb[2 * q] = bf16_pack((gt[4 * q] * alpha) * b4[q].x, (gt[4 * q + 1] * alpha) * b4[q].y);
+        mb[2 * q + 1] =
+            bf16_pack((gt[4 * q + 2] * alpha) * b4[q].z, (gt[4 * q + 3] * alpha) * b4[q].w);
     }
+}
+
+__device__ __forceinline__ void m_off(const f32x16 &gt, float alpha, const float *bt, int s_base,
+                                      uint32_t (&mb)[8], int lane) {
+    float4 b4[4];
+    srows(bt, s_base, b4, lane);
+    m_off_rows(gt, alpha, b4, mb);
 }
 
 // Y^T[p][t] += sum_s X^T[p][s] M^T[s][t] over one s-block, K = 16 rows per
@@ -304,8 +325,8 @@ __device__ __forceinline__ void tblock_part(int tau, int sg0, int sg1, const bf1
 
     const float lam_t = lam[t];
     // per s-block: all eight B operands of C.B^T are fetched before its
-    // first MFMA (one LDS round trip instead of eight), and the X^T operands
-    // of M.X while the weights are computed
+    // first MFMA (one LDS round trip instead of eight), and the per-row
+    // values of the weights and the X^T operands of M.X while its MFMAs run
     for (int sg = sg0; sg <= sg1; ++sg) {
         bf16x8 bo[N / 16];
 #pragma unroll
@@ -313,13 +334,16 @@ __device__ __forceinline__ void tblock_part(int tau, int sg0, int sg1, const bf1
             bo[k] = lds_b128(lds, L.B + ((32 * sg + c) * L.BS + 16 * k + 8 * g) * 2);
         __builtin_amdgcn_sched_barrier(0);
         const f32x16 gt = gram_block<N>([&](int k) { return bo[k]; }, cf);
+        float4 rv[4];
+        srows(sg == tau ? uu : bt, 32 * sg, rv, lane);
+        const float c_end = lam[32 * sg + 31];
         bf16x8 xo[2][PT1 - PT0];
         mx_load<PT0, PT1>(lds, L.X, L.XS, 32 * sg, xo, lane);
         uint32_t mb[8];
         if (sg == tau)
-            m_diag(gt, lam_t, uu, 32 * sg, t, mb, lane);
+            m_diag_rows(gt, lam_t, rv, 32 * sg, t, mb, lane);
         else
-            m_off(gt, fexp2(lam_t - lam[32 * sg + 31]), bt, 32 * sg, mb, lane);
+            m_off_rows(gt, fexp2(lam_t - c_end), rv, mb);
         mx_apply<PT0, PT1>(mb, xo, acc);
     }
 }
