@@ -1088,8 +1088,6 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
         if (swave) {
             slab_bf16<P, SL::NT>(S, ps, nt0, lds, L.S, L.SS, nullptr);
             stage_slab<P, N, kStateWaves>(v, 0, 0, wave, lds, L);
-            if (two)
-                stage_slab<P, N, kStateWaves>(v, kSlab, kSlab, wave, lds, L);
             if (wave == 0) {
                 TD rawdt[4];
                 load_dt<DT>(v, rawdt);
@@ -1132,8 +1130,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             // slabs) or the next chunk into the other half, then the K steps
             // over the rows that are in
             if (two) {
-                if (c > 0)
-                    stage_slab<P, N, kStateWaves>(vc, kSlab, kSlab, wave, lds, L);
+                stage_slab<P, N, kStateWaves>(vc, kSlab, kSlab, wave, lds, L);
             } else if (more) {
                 stage_slab<P, N, kStateWaves>(v, 0, kSlab * ((c + 1) & 1), wave, lds, L);
             }
