@@ -961,21 +961,22 @@ __device__ __forceinline__ int xcd_local_index(int bid, int nblocks) {
 // w % 4). Waves 0..3 are the state waves: each owns a quarter of the fp32
 // state in registers and updates it over the chunk, and they stage the
 // chunk rows into LDS. Waves 4..11 each compute the outputs of one 32-row
-// t-block: with 8 t-blocks wave 4 + k takes 7 - k and wave 8 + k takes k, so
-// every SIMD has the same causal work and the heavy t-block on its older
-// wave. Wave 8 also computes the next chunk's per-row quantities (into the
-// other set of per-row arrays) once its own t-block is done.
+// t-block: with 8 t-blocks wave 4 + k takes k and wave 8 + k takes 7 - k, so
+// every SIMD has the same causal work. t-blocks 0..3 finish (and store their
+// outputs) in the first half of the chunk, on the older waves, which a SIMD
+// issues first; in the second half they are idle and t-blocks 4..7 have the
+// SIMDs to themselves. One t-block wave also computes the next chunk's
+// per-row quantities (into the other set of per-row arrays) once its own
+// t-block is done: with two slabs t-block 3's (idle in the second half, next
+// to t-block 4, the lightest there), with one slab an idle wave.
 constexpr int kPrefillWaves = 12;
-// the t-block wave that also computes the next chunk's per-row arrays:
-// t-block 0 with eight t-blocks (no work in phase 2), idle with four or fewer
-constexpr int kScalarWave = kStateWaves + 4;
 
 __device__ __forceinline__ int wave_tblock(int nT, int wave) {
     const int i = wave - kStateWaves;
     if (i < 0)
         return -1;
     if (nT == 8)
-        return i < 4 ? 7 - i : i - 4;
+        return i < 4 ? i : 11 - i;
     return i < nT ? i : -1;
 }
 
@@ -1213,7 +1214,7 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             }
             // the next chunk's per-row arrays (the scalar wave has no phase-2
             // t-block work, so the dt load's latency is not in its way)
-            if (wave == kScalarWave && more) {
+            if (wave == (two ? kStateWaves + 3 : kStateWaves + 7) && more) {
                 TD rawdt[4];
                 load_dt<DT>(v, rawdt);
                 chunk_scalars_wave<DT>(rawdt, v.n_valid, A2_h, bias, d.softplus, lds,
