@@ -474,6 +474,32 @@ __device__ __forceinline__ void lds_f32x8_own(uint32_t a, f32x4 &w0, f32x4 &w1) 
                  : "v"(a));
 }
 
+// Four n-tiles' B^T operands in one asm statement (one LDS round trip):
+// tiles at byte addresses a, a + 32, a + 64, a + 96, each two transposed
+// fetches D bytes apart.
+template <int D>
+__device__ __forceinline__ void lds_tr8x4_own(uint32_t a, bf16x8 (&o)[4]) {
+    i16x4 r[8];
+    asm volatile("ds_read_b64_tr_b16 %0, %8\n\t"
+                 "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
+                 "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+                 "ds_read_b64_tr_b16 %3, %8 offset:%10\n\t"
+                 "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+                 "ds_read_b64_tr_b16 %5, %8 offset:%11\n\t"
+                 "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+                 "ds_read_b64_tr_b16 %7, %8 offset:%12\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                   "=&v"(r[6]), "=&v"(r[7])
+                 : "v"(a), "i"(D), "i"(32 + D), "i"(64 + D), "i"(96 + D));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const i16x8 v = {r[2 * i][0],     r[2 * i][1],     r[2 * i][2],     r[2 * i][3],
+                         r[2 * i + 1][0], r[2 * i + 1][1], r[2 * i + 1][2], r[2 * i + 1][3]};
+        o[i] = as_bf16x8(v);
+    }
+}
+
 template <int NT, int XS, int BS>
 __device__ __forceinline__ void state_kstep_own(const char *lds, int xb, int xc, int bb, int row0,
                                                 int nt0, const float *wk, f32x4 (&acc)[NT]) {
@@ -486,8 +512,17 @@ __device__ __forceinline__ void state_kstep_own(const char *lds, int xb, int xc,
     lds_f32x8_own(lds_off(wk + 8 * q), w0, w1);
     const float ws[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
     const uint32_t lab = l0 + tr_lane(lane, BS) + 8 * q * BS * 2 + bb + (row0 * BS + 16 * nt0) * 2;
-    state_kstep_ops<NT>(
-        xv, ws, [&](int i) { return as_bf16x8(lds_tr8_own<4 * BS * 2>(lab + 32 * i)); }, acc);
+    if constexpr (NT % 4 == 0) {
+        // the B^T operands four tiles per LDS round trip
+        bf16x8 bo[NT];
+#pragma unroll
+        for (int i = 0; i < NT; i += 4)
+            lds_tr8x4_own<4 * BS * 2>(lab + 32 * i, *reinterpret_cast<bf16x8(*)[4]>(bo + i));
+        state_kstep_ops<NT>(xv, ws, [&](int i) { return bo[i]; }, acc);
+    } else {
+        state_kstep_ops<NT>(
+            xv, ws, [&](int i) { return as_bf16x8(lds_tr8_own<4 * BS * 2>(lab + 32 * i)); }, acc);
+    }
 }
 
 // Tiles nt0 .. nt0 + NT - 1 of p-slab ps <-> a [P][N] fp32 state in global
