@@ -405,12 +405,7 @@ __device__ __forceinline__ void split_wx(const i16x8 &xv, const float (&ws)[8], 
     blo = __builtin_bit_cast(bf16x8, lv);
 }
 
-// One K = 32 step for NT n-tiles (from nt0) of a p-slab: rows row0 ..
-// row0 + 31 of the row-major x tile (byte base xb, row stride xs elements,
-// the slab's first column xc) and of the B tile (bb, bs); wk points at the
-// state weights of those rows. Lane group q = (lane % 64) / 16 supplies rows
-// 8q .. 8q + 7 of the step: k index j of both operands is row 8q + j.
-// The step's arithmetic from its operands: xv (the lane's 8 raw x values),
+// A state K step's arithmetic from its operands: xv (the lane's 8 raw x values),
 // ws (their state weights) and bop(i), the B^T operand of n-tile nt0 + i.
 template <int NT, class F>
 __device__ __forceinline__ void state_kstep_ops(const i16x8 &xv, const float (&ws)[8], F bop,
@@ -425,6 +420,11 @@ __device__ __forceinline__ void state_kstep_ops(const i16x8 &xv, const float (&w
     }
 }
 
+// One K = 32 step for NT n-tiles (from nt0) of a p-slab: rows row0 ..
+// row0 + 31 of the row-major x tile (byte base xb, row stride xs elements,
+// the slab's first column xc) and of the B tile (bb, bs); wk points at the
+// state weights of those rows. Lane group q = (lane % 64) / 16 supplies rows
+// 8q .. 8q + 7 of the step: k index j of both operands is row 8q + j.
 template <int NT>
 __device__ __forceinline__ void state_kstep(const char *lds, int xb, int xs, int xc, int bb,
                                             int bs, int row0, int nt0, const float *wk,
