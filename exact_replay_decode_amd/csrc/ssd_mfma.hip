@@ -1227,6 +1227,11 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
             const int lo = max(32 * tau, vc.nb), hi = min(32 * tau + 32, vc.n_valid);
             const bool out = tau >= 0 && lo < hi && !(RP && a.no_y);
             f32x16 acc[P / 32];
+            // t-block 3 (four s-blocks, outputs and C loads, all in phase 1) is
+            // the longest path of phase 1: its wave goes first on its SIMD
+            // until the phase barrier
+            if (two && tau == sgA)
+                __builtin_amdgcn_s_setprio(1);
             // s-blocks of slab A (all of them with one slab)
             if (out)
                 tblock_part<P, N, 0, P / 32>(tau, 0, two ? min(tau, sgA) : tau, cf, lds, Lc, acc);
@@ -1237,6 +1242,8 @@ __device__ __forceinline__ void scan_one(const ScanArgs &a, int s, int h, char *
                     load_c(v);
             }
             if (two) {
+                if (tau == sgA)
+                    __builtin_amdgcn_s_setprio(0);
                 __syncthreads();   // phase 2: slab B is in
                 if (tau > sgA) {
                     if (out) {
